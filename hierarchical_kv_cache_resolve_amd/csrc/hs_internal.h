@@ -1,0 +1,92 @@
+// hs_internal.h -- shared types of the gfx950 RESOLVE kernels and their host launchers.
+//
+// Device state of one handle (all arrays layer-major so that one layer's state
+// is contiguous; `rl` below is layer * num_req + request):
+//   cache      uint8  [layer][req][B][row_bytes]   the GPU hot cache (blog section 2, item 2)
+//   slot_pos   int32  [layer][req][B]    logical position held by each slot, -1 = empty
+//   ts         uint32 [layer][req][B]    recency stamp, 0 = never used; a miss fetched at
+//                                        step t gets 2t+1, a hit 2t+2, so hits rank above
+//                                        newly fetched misses (pith "What carries the argument")
+//   page_table int32  [layer][req][L_ctx] slot of each logical position, -1 = host only
+//                                        (blog section 2, item 3)
+//   clock      uint32 [layer][req]       resolves done on this (request, layer)
+//   plan       int4   [layer][req][B]    last step's misses {j, slot, evicted pos, new pos}
+//   miss_count int32  [layer][req]
+//   hit_mask   uint8  [layer][req][B]
+//   status     int32  [layer][req]       0, or the device error code of the last step
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hisparse.h"
+
+namespace hs {
+
+constexpr int kPlanThreads = 1024;           // one workgroup per (request, layer)
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kFetchThreads = 256;
+constexpr int kMaxBatch = 32;                // layers per batched launch
+constexpr int kHistBins = 1024;              // radix-select digit of 10 bits
+
+struct StateBase {
+    uint8_t* cache;
+    int32_t* slot_pos;
+    uint32_t* ts;
+    int32_t* page_table;
+    uint32_t* clock;
+    int4* plan;
+    int32_t* miss_count;
+    uint8_t* hit_mask;
+    int32_t* status;
+    int32_t* err;                   // sticky {code, layer, req, detail}
+    unsigned long long* stats;      // [layer][4]: hits, misses, miss bytes, resolves
+    const uint8_t* pool;            // device-visible pointer to the host pool
+    const int64_t* region_row;      // [req * num_layers + layer]
+    int64_t L_ctx;
+    int64_t row_bytes;
+    int R, NL, B;
+};
+
+struct LayerBatch {
+    const int32_t* sel[kMaxBatch];  // [R][k] per entry
+    int32_t* out[kMaxBatch];        // [R][k] per entry
+    int layer[kMaxBatch];
+    int n;
+    int k;
+    int hash_bits;
+};
+
+struct FetchBatch {
+    int layer[kMaxBatch];
+    int n;
+};
+
+struct ReplayBatch {
+    int anchor;
+    int k;
+    int shared[kMaxBatch];
+    int n;
+};
+
+// Host launchers (defined in the .hip files).
+size_t plan_lds_bytes(int k, int hash_bits);
+hipError_t launch_plan(const StateBase& s, const LayerBatch& lb, hipStream_t st);
+hipError_t launch_publish(const StateBase& s, const LayerBatch& lb, hipStream_t st);
+hipError_t launch_fetch(const StateBase& s, const FetchBatch& fb, int blocks, int unroll, bool nt, hipStream_t st);
+hipError_t launch_replay_meta(const StateBase& s, const ReplayBatch& rb, hipStream_t st);
+hipError_t launch_gather_checksum(const StateBase& s, int layer, const int32_t* slot_idx, int k, uint64_t* out,
+                                  hipStream_t st);
+hipError_t launch_link_read(const void* src, void* dst, size_t bytes, hipStream_t st);
+hipError_t launch_hbm_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
+
+// Record the first device-side data error in the sticky word.
+__device__ inline void record_error(int32_t* err, int code, int layer, int req, int detail) {
+    if (atomicCAS(err, 0, code) == 0) {
+        err[1] = layer;
+        err[2] = req;
+        err[3] = detail;
+    }
+}
+
+}  // namespace hs

@@ -1,0 +1,40 @@
+"""The C-ABI library loads on a machine without a GPU and exports every declared symbol."""
+import ctypes
+import os
+import re
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "hisparse.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hisparse_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(os.path.join(ROOT, "hierarchical_kv_cache_resolve_amd", "libhisparse.so"))
+    names = declared_functions()
+    assert len(names) >= 20
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_footprint_identity_pure_function():
+    import hierarchical_kv_cache_resolve_amd as hs
+    # HBM = N_l * B * W_KV * s per request, no L_ctx term
+    assert hs.hisparse_kv_bytes(16, 8, 4096, 576, hs.BF16) == 16 * 8 * 4096 * 576 * 2
+    assert hs.hisparse_kv_bytes(64, 16, 4096, 2048, hs.BF16) == 64 * 16 * 4096 * 4096
+    assert hs.hisparse_kv_bytes(1, 1, 512, 576, hs.FP8) == 512 * 576
+    assert hs.hisparse_kv_bytes(1, 1, 512, 576, hs.FP32) == 512 * 576 * 4
+    assert hs.hisparse_kv_bytes(0, 1, 512, 576, hs.BF16) == 0
+    assert hs.hisparse_kv_bytes(1, 1, 512, 576, 9) == 0
+
+
+def test_no_oracle_on_product_path():
+    pkg = os.path.join(ROOT, "hierarchical_kv_cache_resolve_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp", ".c")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f

@@ -1,0 +1,231 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by element.
+
+Shapes span several workgroup tiles (B up to 16384 slots, i.e. 16 slots per
+lane) and ragged tails (B and k not multiples of the lane count, B not a
+multiple of 4, records of 16 B to 4 KB).  Everything integer is compared
+bit-exactly: slot_idx, hit mask, miss count, the plan (victim slot, evicted
+and new position), slot map, stamps, page table, clocks, and the cached bytes.
+"""
+import numpy as np
+import pytest
+
+import tracegen as tg
+from gpu_helpers import checksum_ref, compare_step, executor, make_pool, make_resolver, oracle_step
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module")
+def hs():
+    import hierarchical_kv_cache_resolve_amd as m
+    return m
+
+
+def run_parity(hs, w, steps=None, full_state_every=1, bytes_every=1, options=None):
+    from oracle import Oracle
+    steps = w.steps if steps is None else steps
+    print(f"[parity] {w.name} R={w.num_req} L={w.num_layers} B={w.B} k={w.k} L_ctx={w.L_ctx} "
+          f"row={w.row_bytes} steps={steps}", flush=True)
+    tr = tg.trace(w, steps=steps)
+    pool = make_pool(hs, w)
+    pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
+    res = make_resolver(hs, w, pool)
+    for key, val in (options or {}).items():
+        res.set_option(key, val)
+    o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes, model_bytes=True)
+    dev = torch.device("cuda:0")
+    sel_d = torch.from_numpy(tr).to(dev)
+    out = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
+    with executor() as ex:
+        for t in range(steps):
+            for l in range(w.num_layers):
+                res.resolve(l, sel_d[t, l], out[l])
+            refs = oracle_step(o, w, tr[t], pool_np, pool_exec=ex)
+            got = out.cpu().numpy()
+            for l in range(w.num_layers):
+                st = res.state(l, page_table=(t % full_state_every == 0))
+                compare_step(got[l], refs[l], st, w, l, t)
+                if t % full_state_every == 0:
+                    assert np.array_equal(st["slot_pos"], o.slot_pos[l]), f"slot_pos step {t} layer {l}"
+                    assert np.array_equal(st["ts"], o.ts[l]), f"ts step {t} layer {l}"
+                    assert np.array_equal(st["clock"], o.clock[l]), f"clock step {t} layer {l}"
+                    assert np.array_equal(st["page_table"], o.page_table[l]), f"page_table step {t} layer {l}"
+                if t % bytes_every == 0:
+                    # bytes of occupied slots only: an empty slot holds nothing
+                    occ = o.slot_pos[l] >= 0
+                    assert np.array_equal(res.cache_layer(l)[occ], o.cache[l][occ]), f"cache bytes step {t} layer {l}"
+    code, _, _ = res.error()
+    assert code == 0
+    s = res.stats()
+    assert s.hits + s.misses == steps * w.num_layers * w.num_req * w.k
+    res.close()
+    pool.free()
+    o.close()
+
+
+def test_tiny_workload_full(hs):
+    run_parity(hs, tg.TINY)
+
+
+def wl(name, **kw):
+    base = dict(name=name, num_req=3, num_layers=2, L_ctx=6000, W_KV=72, elem_bytes=2, k=700, B=1500, steps=12,
+                p_keep=0.8, seed_index=31)
+    base.update(kw)
+    return tg.Workload(**base)
+
+
+RAGGED = [
+    wl("ragged_b_not_mult4", B=1499, k=701),
+    wl("per1_small", B=300, k=257, W_KV=8),
+    wl("per2", B=2047, k=1023),
+    wl("per4_mla", B=4096, k=2048, L_ctx=40000, W_KV=576, num_req=2, num_layers=2, steps=10),
+    wl("per8", B=8000, k=3000, L_ctx=60000, W_KV=24, num_req=2, steps=8),
+    wl("per16_maxb", B=16384, k=4096, L_ctx=90000, W_KV=8, num_req=1, num_layers=1, steps=6),
+    wl("b_equals_k", B=900, k=900, p_keep=0.6),
+    wl("uniform_small_ctx", mode=tg.UNIFORM, L_ctx=2000, B=1200, k=500),
+    wl("k1_b1", k=1, B=1, L_ctx=5, steps=20, W_KV=8),
+    wl("k1_b3", k=1, B=3, L_ctx=7, steps=30, W_KV=8),
+    wl("gqa_row", W_KV=2048, B=600, k=300, L_ctx=3000, steps=8),
+    wl("many_requests", num_req=64, num_layers=1, B=256, k=128, L_ctx=4000, W_KV=8, steps=10),
+    wl("hit_only", mode=tg.HITONLY, p_keep=1.0, steps=6),
+]
+
+
+@pytest.mark.parametrize("w", RAGGED, ids=[w.name for w in RAGGED])
+def test_ragged_shapes(hs, w):
+    run_parity(hs, w)
+
+
+@pytest.mark.parametrize("unroll,blocks,nt", [(1, 7, 0), (2, 64, 1), (8, 4096, 0)])
+def test_fetch_launch_shapes(hs, unroll, blocks, nt):
+    w = wl("fetch_shape", B=1000, k=600, W_KV=200, steps=6)
+    run_parity(hs, w, options={hs.HS_OPT_FETCH_UNROLL: unroll, hs.HS_OPT_FETCH_BLOCKS: blocks,
+                               hs.HS_OPT_NT_LOADS: nt})
+
+
+def test_gather_checksum_matches_pool_rows(hs):
+    w = wl("checksum", W_KV=576, B=800, k=512, L_ctx=5000, steps=5)
+    tr = tg.trace(w)
+    pool = make_pool(hs, w)
+    pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
+    res = make_resolver(hs, w, pool)
+    dev = torch.device("cuda:0")
+    out = torch.empty((w.num_req, w.k), dtype=torch.int32, device=dev)
+    cs = torch.empty(w.num_req, dtype=torch.int64, device=dev)
+    rr = w.region_rows()
+    for t in range(w.steps):
+        for l in range(w.num_layers):
+            res.resolve(l, torch.from_numpy(tr[t, l]).to(dev), out)
+            res.gather_checksum(l, out, cs)
+            got = cs.cpu().numpy().view(np.uint64)
+            for r in range(w.num_req):
+                rows = pool_np[rr[r * w.num_layers + l] + tr[t, l, r]]
+                assert int(got[r]) == checksum_ref(rows)
+    res.close()
+    pool.free()
+
+
+def test_rejected_requests_and_sticky_error(hs):
+    from oracle import Oracle
+    w = wl("errors", num_req=4, num_layers=1, B=64, k=16, L_ctx=200, W_KV=8, steps=3)
+    tr = tg.trace(w)
+    pool = make_pool(hs, w)
+    pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
+    res = make_resolver(hs, w, pool)
+    o = Oracle(w.num_req, 1, w.B, w.L_ctx, w.row_bytes)
+    dev = torch.device("cuda:0")
+    out = torch.empty((w.num_req, w.k), dtype=torch.int32, device=dev)
+    for t in range(2):
+        res.resolve(0, torch.from_numpy(tr[t, 0]).to(dev), out)
+        o.resolve(0, tr[t, 0], pool_np, w.region_rows())
+    before = res.state(0)
+    bad = tr[2, 0].copy()
+    bad[1, 5] = bad[1, 9]          # repeated position in request 1
+    bad[3, 0] = w.L_ctx            # out of range in request 3
+    res.resolve(0, torch.from_numpy(bad).to(dev), out)
+    ref = o.resolve(0, bad, pool_np, w.region_rows())
+    got = out.cpu().numpy()
+    assert np.array_equal(got, ref["slot_idx"])
+    assert np.all(got[1] == -1) and np.all(got[3] == -1)
+    assert ref["err"].tolist()[1] != 0 and ref["err"].tolist()[3] != 0
+    after = res.state(0)
+    for r in (1, 3):
+        assert np.array_equal(after["slot_pos"][r], before["slot_pos"][r])
+        assert np.array_equal(after["ts"][r], before["ts"][r])
+        assert np.array_equal(after["page_table"][r], before["page_table"][r])
+        assert after["clock"][r] == before["clock"][r]
+    assert np.array_equal(after["slot_pos"], o.slot_pos[0])
+    code, layer, req = res.error()
+    assert code in (hs.HS_DEV_DUP, hs.HS_DEV_RANGE) and layer == 0 and req in (1, 3)
+    res.clear_error()
+    assert res.error()[0] == 0
+    res.close()
+    pool.free()
+
+
+def test_synchronous_argument_errors(hs):
+    w = wl("args", num_req=2, num_layers=2, B=32, k=8, L_ctx=100, W_KV=8)
+    pool = make_pool(hs, w)
+    res = make_resolver(hs, w, pool)
+    dev = torch.device("cuda:0")
+    sel = torch.zeros((2, 40), dtype=torch.int32, device=dev)
+    out = torch.empty((2, 40), dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream().cuda_stream
+    assert hs.hisparse_resolve(res.h, 0, sel.data_ptr(), 33, out.data_ptr(), s) == hs.HS_E_K   # k > B
+    assert hs.hisparse_resolve(res.h, 0, sel.data_ptr(), 0, out.data_ptr(), s) == hs.HS_E_K    # empty
+    assert hs.hisparse_resolve(res.h, 2, sel.data_ptr(), 8, out.data_ptr(), s) == hs.HS_E_LAYER
+    assert hs.hisparse_resolve(res.h, -1, sel.data_ptr(), 8, out.data_ptr(), s) == hs.HS_E_LAYER
+    assert hs.hisparse_resolve(res.h, 0, 0, 8, out.data_ptr(), s) == hs.HS_E_INVAL
+    assert hs.hisparse_prefetch(res.h, 0, [1], s) == hs.HS_E_ORDER   # anchor not resolved yet
+    # record bytes not a multiple of 16
+    desc = hs.hs_host_pool(pool.ptr, w.pool_rows, w.L_ctx, None)
+    with pytest.raises(hs.HisparseError) as e:
+        hs.hisparse_create(2, 2, 32, 7, hs.BF16, desc)
+    assert e.value.rc == hs.HS_E_ALIGN
+    # a history region outside the pool
+    bad_rr = np.array([0, 0, 0, w.pool_rows], dtype=np.int64)
+    desc = hs.hs_host_pool(pool.ptr, w.pool_rows, w.L_ctx, bad_rr.ctypes.data)
+    with pytest.raises(hs.HisparseError) as e:
+        hs.hisparse_create(2, 2, 32, 8, hs.BF16, desc)
+    assert e.value.rc == hs.HS_E_POOL
+    # pageable memory is not a pool
+    pageable = np.zeros(w.pool_rows * w.row_bytes, np.uint8)
+    desc = hs.hs_host_pool(pageable.ctypes.data, w.pool_rows, w.L_ctx, None)
+    with pytest.raises(hs.HisparseError) as e:
+        hs.hisparse_create(2, 2, 32, 8, hs.BF16, desc)
+    assert e.value.rc == hs.HS_E_POOL
+    with pytest.raises(hs.HisparseError):
+        hs.hisparse_create(2, 2, 0, 8, hs.BF16, hs.hs_host_pool(pool.ptr, w.pool_rows, w.L_ctx, None))
+    assert res.hbm_bytes() == hs.hisparse_kv_bytes(2, 2, 32, 8, hs.BF16) == 2 * 2 * 32 * 16
+    res.close()
+    pool.free()
+
+
+def test_reset_refills_exactly(hs):
+    from oracle import Oracle
+    w = wl("reset", steps=6)
+    tr = tg.trace(w)
+    pool = make_pool(hs, w)
+    pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
+    res = make_resolver(hs, w, pool)
+    dev = torch.device("cuda:0")
+    out = torch.empty((w.num_req, w.k), dtype=torch.int32, device=dev)
+    for t in range(3):
+        for l in range(w.num_layers):
+            res.resolve(l, torch.from_numpy(tr[t, l]).to(dev), out)
+    res.reset()
+    assert res.stats().resolves == 0
+    o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes)
+    for t in range(3, 6):
+        for l in range(w.num_layers):
+            res.resolve(l, torch.from_numpy(tr[t, l]).to(dev), out)
+            ref = o.resolve(l, tr[t, l], pool_np, w.region_rows())
+            assert np.array_equal(out.cpu().numpy(), ref["slot_idx"])
+            if t == 3:
+                assert np.all(ref["miss_count"] == w.k)
+            occ = o.slot_pos[l] >= 0
+            assert np.array_equal(res.cache_layer(l)[occ], o.cache[l][occ])
+    res.close()
+    pool.free()
