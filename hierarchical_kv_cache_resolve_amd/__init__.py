@@ -23,7 +23,7 @@ HS_DEV_RANGE, HS_DEV_DUP, HS_DEV_NOT_RESIDENT, HS_DEV_DIVERGED = 1, 2, 3, 4
 HS_MAX_B, HS_MAX_K, HS_MAX_REQ = 16384, 4096, 1024
 BF16, FP16, FP8, FP32 = 0, 1, 2, 3
 ELEM_BYTES = {BF16: 2, FP16: 2, FP8: 1, FP32: 4}
-HS_OPT_FETCH_BLOCKS, HS_OPT_FETCH_UNROLL, HS_OPT_TIMING, HS_OPT_NT_LOADS = 1, 2, 3, 4
+HS_OPT_FETCH_BLOCKS, HS_OPT_FETCH_UNROLL, HS_OPT_TIMING, HS_OPT_NT_LOADS, HS_OPT_PHASE_TRACE = 1, 2, 3, 4, 5
 
 _ERR_NAMES = {v: k for k, v in dict(HS_E_INVAL=-1, HS_E_HANDLE=-2, HS_E_LAYER=-3, HS_E_K=-4, HS_E_ALIGN=-5,
                                      HS_E_POOL=-6, HS_E_NOMEM=-7, HS_E_HIP=-8, HS_E_DEVICE=-9,
@@ -81,6 +81,7 @@ _sig("hisparse_reset", _i32, _vp)
 _sig("hisparse_set_option", _i32, _vp, _i32, _i64)
 _sig("hisparse_timing", _i32, _vp, ctypes.POINTER(hs_timing), _i32)
 _sig("hisparse_memcpy_d2h", _i32, _vp, _vp, _sz)
+_sig("hisparse_phase_trace", _i32, _vp, _i32, _vp, ctypes.POINTER(ctypes.c_double))
 _sig("hisparse_host_alloc", _i32, _sz, _i32, ctypes.POINTER(_vp))
 _sig("hisparse_host_free", _i32, _vp)
 _sig("hisparse_gather_checksum", _i32, _vp, _i32, _vp, _i32, _vp, _vp)
@@ -196,6 +197,14 @@ def hisparse_timing(h, clear=False) -> hs_timing:
     t = hs_timing()
     _check("hisparse_timing", _lib.hisparse_timing(h, ctypes.byref(t), 1 if clear else 0))
     return t
+
+
+def hisparse_phase_trace(h, layer, num_req):
+    """Raw phase stamps [num_req][16] of the last metadata launch and the tick period in ns."""
+    out = np.zeros((num_req, 16), dtype=np.uint64)
+    ns = ctypes.c_double()
+    _check("hisparse_phase_trace", _lib.hisparse_phase_trace(h, layer, out.ctypes.data, ctypes.byref(ns)))
+    return out, ns.value
 
 
 def hisparse_memcpy_d2h(dst, d_src, nbytes) -> int:

@@ -74,7 +74,7 @@ int hash_bits_for(int k) {
 void free_all(hisparse_ctx* h) {
     hs::StateBase& s = h->s;
     void* ptrs[] = {s.cache, s.slot_pos, s.ts, s.page_table, s.clock, s.plan, s.miss_count,
-                    s.hit_mask, s.status, s.err, s.stats, h->d_region_row};
+                    s.hit_mask, s.status, s.err, s.stats, s.phase, h->d_region_row};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     for (hipEvent_t e : h->ev_plan)
@@ -478,6 +478,21 @@ int hisparse_set_option(hisparse_t h, int key, int64_t value) {
         case HS_OPT_NT_LOADS:
             h->nt = value != 0;
             return HS_OK;
+        case HS_OPT_PHASE_TRACE:
+            if (value && !h->s.phase) {
+                const size_t n = static_cast<size_t>(h->R) * h->NL * hs::kPhaseSlots;
+                void* p = nullptr;
+                HS_TRY(hipDeviceSynchronize());
+                if (alloc_dev(&p, n * sizeof(unsigned long long)) != HS_OK) return HS_E_NOMEM;
+                HS_TRY(hipMemset(p, 0, n * sizeof(unsigned long long)));
+                HS_TRY(hipDeviceSynchronize());
+                h->s.phase = static_cast<unsigned long long*>(p);
+            } else if (!value && h->s.phase) {
+                HS_TRY(hipDeviceSynchronize());
+                (void)hipFree(h->s.phase);
+                h->s.phase = nullptr;
+            }
+            return HS_OK;
         case HS_OPT_TIMING:
             if (value && h->ring.empty()) {
                 h->ring.resize(kRingPairs);
@@ -531,6 +546,19 @@ int hisparse_host_alloc(size_t bytes, int coherent, void** out) {
         *out = nullptr;
         return HS_E_NOMEM;
     }
+    return HS_OK;
+}
+
+int hisparse_phase_trace(hisparse_t h, int layer, uint64_t* out, double* ns_per_tick) {
+    if (!valid(h)) return HS_E_HANDLE;
+    if (layer < 0 || layer >= h->NL) return HS_E_LAYER;
+    if (!out || !ns_per_tick || !h->s.phase) return HS_E_INVAL;
+    int khz = 0;
+    HS_TRY(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, h->device));
+    *ns_per_tick = khz > 0 ? 1e6 / khz : 0.0;
+    HS_TRY(hipDeviceSynchronize());
+    const size_t n = static_cast<size_t>(h->R) * hs::kPhaseSlots;
+    HS_TRY(hipMemcpy(out, h->s.phase + static_cast<size_t>(layer) * n, n * sizeof(uint64_t), hipMemcpyDeviceToHost));
     return HS_OK;
 }
 

@@ -28,6 +28,7 @@ constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kFetchThreads = 256;
 constexpr int kMaxBatch = 32;                // layers per batched launch
 constexpr int kHistBins = 1024;              // radix-select digit of 10 bits
+constexpr int kPhaseSlots = 16;              // phase stamps per (request, layer)
 
 struct StateBase {
     uint8_t* cache;
@@ -41,6 +42,7 @@ struct StateBase {
     int32_t* status;
     int32_t* err;                   // sticky {code, layer, req, detail}
     unsigned long long* stats;      // [layer][4]: hits, misses, miss bytes, resolves
+    unsigned long long* phase;      // [layer][req][kPhaseSlots] wall-clock stamps, or null (off)
     const uint8_t* pool;            // device-visible pointer to the host pool
     const int64_t* region_row;      // [req * num_layers + layer]
     int64_t L_ctx;
@@ -70,7 +72,7 @@ struct ReplayBatch {
 };
 
 // Host launchers (defined in the .hip files).
-size_t plan_lds_bytes(int k, int hash_bits);
+size_t plan_lds_bytes(int k, int hash_bits, int B);
 hipError_t launch_plan(const StateBase& s, const LayerBatch& lb, hipStream_t st);
 hipError_t launch_publish(const StateBase& s, const LayerBatch& lb, hipStream_t st);
 hipError_t launch_fetch(const StateBase& s, const FetchBatch& fb, int blocks, int unroll, bool nt, hipStream_t st);

@@ -25,39 +25,95 @@ namespace hs {
 namespace {
 
 constexpr int kEmpty = -1;
+constexpr int kMisc = 128;  // LDS words for flags, per-wave partial counts and broadcasts
 
-__device__ inline unsigned hash_pos(int p, int bits) {
+// Offsets inside the misc block (each scan owns its own words, so no barrier
+// is needed before one scan's partials are overwritten by the next).
+enum : int {
+    M_FLAGS = 0,     // bit 0: a position out of range, bit 1: a repeated position
+    M_BADAT = 1,     // largest offending selection index + 1
+    M_MISS = 2,      // [16] misses per wave
+    M_MIN = 18,      // [16] per-wave minimum candidate stamp
+    M_MAX = 34,      // [16] per-wave maximum candidate stamp
+    M_STRICT = 50,   // [16] strictly-older candidates per wave
+    M_TIE = 66,      // [16] tied candidates per wave
+    M_HIST = 82,     // [16] histogram-scan wave totals
+    M_BIN = 98,      // crossing bin of the current radix pass
+    M_BELOW = 99,    // candidates below the crossing bin
+};
+
+__device__ inline unsigned hash_bucket(int p, int bucket_bits) {
     // multiplicative hashing with the golden-ratio constant (Knuth, TAOCP 6.4)
-    return (static_cast<unsigned>(p) * 0x9E3779B1u) >> (32 - bits);
+    return bucket_bits > 0 ? (static_cast<unsigned>(p) * 0x9E3779B1u) >> (32 - bucket_bits) : 0u;
 }
 
-// Block-wide exclusive scan of one int per lane (1024 lanes).  `scratch`
-// holds kPlanWaves + 1 ints of LDS.  Ends with a barrier, so the scratch may
-// be reused by the next call.
-__device__ inline int block_excl_scan(int v, int* total, int* scratch) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
+__device__ inline unsigned long long lanemask_lt() {
+    const int lane = threadIdx.x & 63;
+    return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
+// LDS carve-up of the metadata kernel (ints): miss-hash keys [H], miss-hash
+// values [H], slot per selection [k], miss list [k], selection copy [k],
+// hit bitmap over slots [B/32 rounded up to 4], histogram [kHistBins], misc
+// [kMisc].  Keys come first so 16-byte bucket reads are aligned.
+struct PlanLds {
+    int* bkey;
+    int* bval;
+    int* sidx;
+    int* mlist;
+    int* sel;
+    unsigned* hitmap;
+    int* hist;
+    int* misc;
+};
+
+__device__ inline int hitmap_words(int B) { return ((B + 127) >> 7) << 2; }
+
+__device__ inline PlanLds carve(int* base, int H, int k, int B) {
+    PlanLds l;
+    l.bkey = base;
+    l.bval = l.bkey + H;
+    l.sidx = l.bval + H;
+    l.mlist = l.sidx + k;
+    l.sel = l.mlist + k;
+    l.hitmap = reinterpret_cast<unsigned*>(l.sel + k);
+    l.hist = reinterpret_cast<int*>(l.hitmap) + hitmap_words(B);
+    l.misc = l.hist + kHistBins;
+    return l;
+}
+
+// Bucketed open addressing: 4 entries per bucket, filled in order, buckets
+// probed linearly.  One 16-byte LDS read checks a whole bucket, which keeps
+// the 64 lanes of a wave close together.  Returns false if p is already
+// present.
+__device__ inline bool bucket_insert(const PlanLds& l, unsigned nbm, int bucket_bits, int p, int j) {
+    unsigned b = hash_bucket(p, bucket_bits);
+    for (;;) {
+        const int4 kk = *reinterpret_cast<const int4*>(l.bkey + 4 * b);
+        if (kk.x == p || kk.y == p || kk.z == p || kk.w == p) return false;
+        const int snap[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (snap[i] != kEmpty) continue;
+            const int prev = atomicCAS(&l.bkey[4 * b + i], kEmpty, p);
+            if (prev == kEmpty) {
+                l.bval[4 * b + i] = j;
+                return true;
+            }
+            if (prev == p) return false;
+        }
+        b = (b + 1) & nbm;
+    }
+}
+
+__device__ inline int wave_incl_scan(int x) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const int y = __shfl_up(x, off, 64);
         if (lane >= off) x += y;
     }
-    if (lane == 63) scratch[wave] = x;
-    __syncthreads();
-    if (wave == 0) {
-        int w = lane < kPlanWaves ? scratch[lane] : 0;
-#pragma unroll
-        for (int off = 1; off < kPlanWaves; off <<= 1) {
-            const int y = __shfl_up(w, off, 64);
-            if (lane >= off) w += y;
-        }
-        if (lane < kPlanWaves) scratch[lane] = w;
-    }
-    __syncthreads();
-    const int base = wave ? scratch[wave - 1] : 0;
-    *total = scratch[kPlanWaves - 1];
-    __syncthreads();
-    return base + x - v;
+    return x;
 }
 
 __device__ inline unsigned wave_min(unsigned v) {
@@ -72,63 +128,26 @@ __device__ inline unsigned wave_max(unsigned v) {
     return v;
 }
 
-// LDS carve-up of the plan kernel (ints): hash keys [H], hash values [H],
-// slot per selection [k], miss list [k], selection copy [k], histogram
-// [kHistBins], scan scratch [32].
-struct PlanLds {
-    int* hkey;
-    int* hval;
-    int* sidx;
-    int* mlist;
-    int* sel;
-    int* hist;
-    int* scratch;
-};
-
-__device__ inline PlanLds carve(int* base, int H, int k) {
-    PlanLds l;
-    l.hkey = base;
-    l.hval = l.hkey + H;
-    l.sidx = l.hval + H;
-    l.mlist = l.sidx + k;
-    l.sel = l.mlist + k;
-    l.hist = l.sel + k;
-    l.scratch = l.hist + kHistBins;
-    return l;
-}
-
-// Insert (p -> j) with linear probing.  Returns false if p is already present.
-__device__ inline bool hash_insert(const PlanLds& l, int H, int bits, int p, int j) {
-    unsigned h = hash_pos(p, bits);
-    for (;;) {
-        const int prev = atomicCAS(&l.hkey[h], kEmpty, p);
-        if (prev == kEmpty) {
-            l.hval[h] = j;
-            return true;
-        }
-        if (prev == p) return false;
-        h = (h + 1) & static_cast<unsigned>(H - 1);
-    }
-}
-
-__device__ inline int hash_find(const PlanLds& l, int H, int bits, int p) {
-    unsigned h = hash_pos(p, bits);
-    for (;;) {
-        const int key = l.hkey[h];
-        if (key == p) return l.hval[h];
-        if (key == kEmpty) return -1;
-        h = (h + 1) & static_cast<unsigned>(H - 1);
-    }
+// Block-wide OR of a small flag word: lanes holding a non-zero value OR it
+// into one LDS word (the word must be zero before; read it after a barrier).
+__device__ inline void block_or_into(int* word, int v) {
+    if (__ballot(v != 0) != 0ull && v != 0) atomicOr(word, v);
 }
 
 // Per-lane contiguous slot range [tid*PER, tid*PER + PER), moved as 16-byte
 // vectors when the whole range is in bounds and 16-byte aligned (B % 4 == 0).
-template <int PER, typename T>
+// Per-lane contiguous slot run [tid*PER, tid*PER + PER).  VEC (B % 4 == 0)
+// moves it as 16-byte pieces, each of which lies wholly inside or wholly
+// outside [0, B); the scalar form handles any B.  The two forms are separate
+// instantiations so that no load result has to be merged across a branch.
+template <int PER, bool VEC, typename T>
 __device__ inline void load_run(const T* g, int s0, int B, T (&v)[PER], T fill) {
-    if (s0 + PER <= B && (PER % 4) == 0 && (B & 3) == 0) {
+    if constexpr (VEC && (PER % 4) == 0) {
 #pragma unroll
         for (int q = 0; q < PER; q += 4) {
-            const int4 w = *reinterpret_cast<const int4*>(g + s0 + q);
+            int4 w = make_int4(static_cast<int>(fill), static_cast<int>(fill), static_cast<int>(fill),
+                               static_cast<int>(fill));
+            if (s0 + q < B) w = *reinterpret_cast<const int4*>(g + s0 + q);
             v[q] = static_cast<T>(w.x);
             v[q + 1] = static_cast<T>(w.y);
             v[q + 2] = static_cast<T>(w.z);
@@ -140,17 +159,19 @@ __device__ inline void load_run(const T* g, int s0, int B, T (&v)[PER], T fill) 
     }
 }
 
-template <int PER, typename T>
+template <int PER, bool VEC, typename T>
 __device__ inline void store_run(T* g, int s0, int B, const T (&v)[PER]) {
-    if (s0 + PER <= B && (PER % 4) == 0 && (B & 3) == 0) {
+    if constexpr (VEC && (PER % 4) == 0) {
 #pragma unroll
         for (int q = 0; q < PER; q += 4) {
-            int4 w;
-            w.x = static_cast<int>(v[q]);
-            w.y = static_cast<int>(v[q + 1]);
-            w.z = static_cast<int>(v[q + 2]);
-            w.w = static_cast<int>(v[q + 3]);
-            *reinterpret_cast<int4*>(g + s0 + q) = w;
+            if (s0 + q < B) {
+                int4 w;
+                w.x = static_cast<int>(v[q]);
+                w.y = static_cast<int>(v[q + 1]);
+                w.z = static_cast<int>(v[q + 2]);
+                w.w = static_cast<int>(v[q + 3]);
+                *reinterpret_cast<int4*>(g + s0 + q) = w;
+            }
         }
     } else {
 #pragma unroll
@@ -173,95 +194,181 @@ __device__ inline void reject(const StateBase& s, int32_t* out, int k, int64_t r
     }
 }
 
-template <int PER>
+// Optional per-phase wall-clock stamps (constant-rate clock).  Lane 0 keeps
+// them in registers and writes them once at the end, so tracing adds no
+// global store that a later barrier would have to wait for.
+#define HS_PHASE(i)                                                      \
+    do {                                                                 \
+        if (s.phase != nullptr && tid == 0) stamp[(i)] = wall_clock64(); \
+    } while (0)
+#define HS_PHASE_FLUSH()                                                                \
+    do {                                                                                \
+        if (s.phase != nullptr && tid == 0)                                             \
+            for (int i_ = 0; i_ < 11; ++i_) s.phase[rl * kPhaseSlots + i_] = stamp[i_]; \
+    } while (0)
+
+constexpr int kMaxSelPerLane = HS_MAX_K / kPlanThreads;  // 4
+
+// The metadata half of RESOLVE for one (request, layer).
+//   1. every global read is issued up front: clock, selection, slot map and
+//      stamps of this lane's slot run, then the page-table entry of each
+//      selected position (which says where the position is cached, if at all);
+//   2. hits are marked in an LDS bitmap over the slots (a slot claimed twice
+//      means a repeated position); the positions that missed go into an LDS
+//      hash table, which catches repeats among them;
+//   3. misses are compacted in ascending j with wave ballots;
+//   4. the m victims are the non-hit slots with the smallest (stamp, slot)
+//      keys (radix select on the stamps, then one ballot-counted pass);
+//   5. the i-th miss takes the i-th victim in slot order; slot map, stamps
+//      (2t+1 for misses, 2t+2 for hits), page table and plan are written and
+//      every selection's slot is published.
+template <int PER, bool VEC>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBatch lb) {
     extern __shared__ int lds_raw[];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = blockIdx.x;
     const int layer = lb.layer[blockIdx.y];
-    const int k = lb.k, B = s.B, bits = lb.hash_bits, H = 1 << bits;
+    const int k = lb.k, B = s.B, H = 1 << lb.hash_bits;
+    const int bucket_bits = lb.hash_bits - 2;
+    const unsigned nbm = static_cast<unsigned>((H >> 2) - 1);
     const int64_t rl = static_cast<int64_t>(layer) * s.R + r;
     const int32_t* sel = lb.sel[blockIdx.y] + static_cast<int64_t>(r) * k;
     int32_t* out = lb.out[blockIdx.y] + static_cast<int64_t>(r) * k;
     int32_t* spos_g = s.slot_pos + rl * B;
     uint32_t* ts_g = s.ts + rl * B;
     int32_t* pt = s.page_table + rl * s.L_ctx;
-    const PlanLds l = carve(lds_raw, H, k);
+    const PlanLds l = carve(lds_raw, H, k, B);
+    const unsigned long long lt = lanemask_lt();
+    unsigned long long stamp[11] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    HS_PHASE(0);
 
-    // Independent global loads first: step clock and this lane's slot run.
+    // 1. global reads
     const uint32_t t = s.clock[rl];
+    int selv[kMaxSelPerLane];
+#pragma unroll
+    for (int q = 0; q < kMaxSelPerLane; ++q) {
+        const int j = tid + q * kPlanThreads;
+        selv[q] = j < k ? sel[j] : 0;
+    }
     const int s0 = tid * PER;
     int spos[PER];
-    load_run<PER, int>(spos_g, s0, B, spos, kEmpty);
-
-    for (int i = tid; i < H; i += kPlanThreads) l.hkey[i] = kEmpty;
-    for (int j = tid; j < k; j += kPlanThreads) l.sidx[j] = -1;
-    __syncthreads();
-
-    // Stage 1: hash table over the selected positions.
-    int bad_range = 0, bad_dup = 0, bad_at = -1;
-    for (int j = tid; j < k; j += kPlanThreads) {
-        const int p = sel[j];
-        l.sel[j] = p;
-        if (p < 0 || static_cast<int64_t>(p) >= s.L_ctx) {
-            bad_range = 1;
-            bad_at = j;
-        } else if (!hash_insert(l, H, bits, p, j)) {
-            bad_dup = 1;
-            bad_at = j;
-        }
-    }
-    const int any_range = __syncthreads_or(bad_range);
-    const int any_dup = __syncthreads_or(bad_dup);
-    if (any_range || any_dup) {
-        const int code = any_range ? HS_DEV_RANGE : HS_DEV_DUP;
-        reject(s, out, k, rl, layer, r, code, bad_at);
-        return;
-    }
-
-    // Stage 2: probe every cached position against the hash to mark hits.
-    unsigned hitbits = 0;
+    uint32_t tsv[PER];
+    load_run<PER, VEC, int>(spos_g, s0, B, spos, kEmpty);
+    load_run<PER, VEC, uint32_t>(ts_g, s0, B, tsv, 0xFFFFFFFFu);
+    int bad = 0, bad_at = 0;
+    int ptv[kMaxSelPerLane];
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        if (s0 + q < B && spos[q] >= 0) {
-            const int j = hash_find(l, H, bits, spos[q]);
-            if (j >= 0) {
-                l.sidx[j] = s0 + q;
-                hitbits |= 1u << q;
+    for (int q = 0; q < kMaxSelPerLane; ++q) {
+        const int j = tid + q * kPlanThreads;
+        ptv[q] = -1;
+        if (j < k) {
+            const int p = selv[q];
+            if (p < 0 || static_cast<int64_t>(p) >= s.L_ctx) {
+                bad |= 1;
+                bad_at = j + 1;
+            } else {
+                ptv[q] = pt[p];
             }
         }
     }
-    __syncthreads();
 
-    // Miss list in ascending j: each lane owns a contiguous run of j.
+    for (int i = tid; i < H; i += kPlanThreads) l.bkey[i] = kEmpty;
+    for (int i = tid; i < hitmap_words(B); i += kPlanThreads) l.hitmap[i] = 0u;
+    l.hist[tid] = 0;
+    if (tid < kMisc) l.misc[tid] = 0;
+    __syncthreads();
+    HS_PHASE(1);
+
+    // 2. hits into the slot bitmap, misses into the hash
+#pragma unroll
+    for (int q = 0; q < kMaxSelPerLane; ++q) {
+        const int j = tid + q * kPlanThreads;
+        if (j < k && !(bad & 1)) {
+            const int p = selv[q];
+            const int slot = ptv[q];
+            l.sel[j] = p;
+            if (slot >= 0) {
+                l.sidx[j] = slot;
+                if (slot >= B) {
+                    bad |= 1;  // a page-table entry outside the cache: treat like a bad position
+                    bad_at = j + 1;
+                } else {
+                    const unsigned bit = 1u << (slot & 31);
+                    if (atomicOr(&l.hitmap[slot >> 5], bit) & bit) {
+                        bad |= 2;
+                        bad_at = j + 1;
+                    }
+                }
+            } else {
+                l.sidx[j] = -1;
+                if (!bucket_insert(l, nbm, bucket_bits, p, j)) {
+                    bad |= 2;
+                    bad_at = j + 1;
+                }
+            }
+        }
+    }
+    block_or_into(&l.misc[M_FLAGS], bad);
+    if (bad) atomicMax(&l.misc[M_BADAT], bad_at);
+    __syncthreads();
+    HS_PHASE(2);
+    const int flags = l.misc[M_FLAGS];
+    if (flags) {
+        reject(s, out, k, rl, layer, r, (flags & 1) ? HS_DEV_RANGE : HS_DEV_DUP, l.misc[M_BADAT] - 1);
+        return;
+    }
+    // this lane's slots that hold a selected position (PER divides 32)
+    const unsigned hitbits =
+        s0 < B ? (l.hitmap[s0 >> 5] >> (s0 & 31)) & ((PER == 32) ? 0xFFFFFFFFu : ((1u << PER) - 1u)) : 0u;
+    HS_PHASE(3);
+
+    // 3. miss list in ascending j: each lane owns the contiguous run
+    // [tid*kper, tid*kper + kper); prefix counts come from wave ballots.
     const int kper = (k + kPlanThreads - 1) / kPlanThreads;
     const int j0 = tid * kper;
-    int cnt = 0;
-    for (int q = 0; q < kper; ++q) {
-        const int j = j0 + q;
-        if (j < k && l.sidx[j] < 0) ++cnt;
+    unsigned mflags = 0;
+    int mpre = 0, mtot = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxSelPerLane; ++q) {
+        if (q < kper) {
+            const int j = j0 + q;
+            const bool f = j < k && l.sidx[j] < 0;
+            mflags |= static_cast<unsigned>(f) << q;
+            const unsigned long long bm = __ballot(f);
+            mpre += __popcll(bm & lt);
+            mtot += __popcll(bm);
+        }
     }
-    int m;
-    int base = block_excl_scan(cnt, &m, l.scratch);
-    for (int q = 0; q < kper; ++q) {
-        const int j = j0 + q;
-        if (j < k && l.sidx[j] < 0) l.mlist[base++] = j;
+    if (lane == 0) l.misc[M_MISS + wave] = mtot;
+    __syncthreads();
+    int m = 0, base = mpre;
+#pragma unroll
+    for (int w = 0; w < kPlanWaves; ++w) {
+        const int c = l.misc[M_MISS + w];
+        m += c;
+        if (w < wave) base += c;
     }
+#pragma unroll
+    for (int q = 0; q < kMaxSelPerLane; ++q)
+        if ((mflags >> q) & 1u) l.mlist[base++] = j0 + q;
+    HS_PHASE(4);
     const int h = k - m;
     const uint32_t ts_miss = 2u * t + 1u, ts_hit = 2u * t + 2u;
 
     if (m == 0) {
         // Every selection hit: only the hit stamps change.
+        if (hitbits) {
 #pragma unroll
-        for (int q = 0; q < PER; ++q)
-            if ((hitbits >> q) & 1u) ts_g[s0 + q] = ts_hit;
+            for (int q = 0; q < PER; ++q)
+                if ((hitbits >> q) & 1u) tsv[q] = ts_hit;
+            store_run<PER, VEC, uint32_t>(ts_g, s0, B, tsv);
+        }
     } else {
         __syncthreads();  // miss list complete
-        uint32_t tsv[PER];
-        load_run<PER, uint32_t>(ts_g, s0, B, tsv, 0xFFFFFFFFu);
+        HS_PHASE(5);
         const int ncand = B - h;
-        // Stage 3: threshold stamp T and the number of slots stamped exactly T
-        // that must go (lowest slots first).
+        // 4. threshold stamp T and how many candidates stamped exactly T must
+        // go (lowest slots first); the rest of the victims are older than T.
         uint32_t T;
         int need_eq;
         if (m == ncand) {
@@ -278,31 +385,30 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBa
             }
             mn = wave_min(mn);
             mx = wave_max(mx);
-            const int lane = tid & 63, wave = tid >> 6;
             if (lane == 0) {
-                l.hist[wave] = static_cast<int>(mn);
-                l.hist[kPlanWaves + wave] = static_cast<int>(mx);
+                l.misc[M_MIN + wave] = static_cast<int>(mn);
+                l.misc[M_MAX + wave] = static_cast<int>(mx);
             }
             __syncthreads();
             mn = 0xFFFFFFFFu;
             mx = 0u;
+#pragma unroll
             for (int w = 0; w < kPlanWaves; ++w) {
-                mn = min(mn, static_cast<unsigned>(l.hist[w]));
-                mx = max(mx, static_cast<unsigned>(l.hist[kPlanWaves + w]));
+                mn = min(mn, static_cast<unsigned>(l.misc[M_MIN + w]));
+                mx = max(mx, static_cast<unsigned>(l.misc[M_MAX + w]));
             }
-            __syncthreads();
             if (mn == mx) {
                 T = mn;
                 need_eq = m;
             } else {
+                // Radix select over stamps relative to the minimum, 10-bit
+                // digits from the top; usually one pass.
                 const int nbits = 32 - __clz(static_cast<int>(mx - mn));
                 uint64_t prefix = 0;
                 int remaining = m, pos = nbits;
                 while (pos > 0) {
                     const int d = pos < 10 ? pos : 10;
                     pos -= d;
-                    l.hist[tid] = 0;
-                    __syncthreads();
 #pragma unroll
                     for (int q = 0; q < PER; ++q) {
                         if (s0 + q < B && !((hitbits >> q) & 1u)) {
@@ -313,35 +419,60 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBa
                     }
                     __syncthreads();
                     const int hb = l.hist[tid];
-                    int tot;
-                    const int below = block_excl_scan(hb, &tot, l.scratch);
+                    l.hist[tid] = 0;  // ready for the next pass
+                    const int incl = wave_incl_scan(hb);
+                    if (lane == 63) l.misc[M_HIST + wave] = incl;
+                    __syncthreads();
+                    int below = incl - hb;
+#pragma unroll
+                    for (int w = 0; w < kPlanWaves; ++w)
+                        if (w < wave) below += l.misc[M_HIST + w];
                     if (below < remaining && remaining <= below + hb) {
-                        l.scratch[kPlanWaves + 1] = tid;
-                        l.scratch[kPlanWaves + 2] = below;
+                        l.misc[M_BIN] = tid;
+                        l.misc[M_BELOW] = below;
                     }
                     __syncthreads();
-                    prefix = (prefix << d) | static_cast<uint64_t>(l.scratch[kPlanWaves + 1]);
-                    remaining -= l.scratch[kPlanWaves + 2];
-                    __syncthreads();
+                    prefix = (prefix << d) | static_cast<uint64_t>(l.misc[M_BIN]);
+                    remaining -= l.misc[M_BELOW];
                 }
                 T = mn + static_cast<uint32_t>(prefix);
                 need_eq = remaining;
             }
         }
+        HS_PHASE(6);
 
-        // Victim ranks in slot order: one scan counts strictly older
-        // candidates (high 16 bits) and tied candidates (low 16 bits).
-        int strict = 0, tie = 0;
+        // Victim ranks in slot order: strictly older candidates and tied
+        // candidates are counted together with two ballots per slot column.
+        unsigned strict_bits = 0, tie_bits = 0;
+        int spre = 0, tpre = 0, stot = 0, ttot = 0;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            if (s0 + q < B && !((hitbits >> q) & 1u)) {
-                if (tsv[q] < T) ++strict;
-                else if (tsv[q] == T) ++tie;
+            const bool cand = s0 + q < B && !((hitbits >> q) & 1u);
+            const bool st = cand && tsv[q] < T;
+            const bool ti = cand && tsv[q] == T;
+            strict_bits |= static_cast<unsigned>(st) << q;
+            tie_bits |= static_cast<unsigned>(ti) << q;
+            const unsigned long long bs = __ballot(st), bt = __ballot(ti);
+            spre += __popcll(bs & lt);
+            tpre += __popcll(bt & lt);
+            stot += __popcll(bs);
+            ttot += __popcll(bt);
+        }
+        if (lane == 0) {
+            l.misc[M_STRICT + wave] = stot;
+            l.misc[M_TIE + wave] = ttot;
+        }
+        __syncthreads();
+        int sb = spre, tb = tpre;
+#pragma unroll
+        for (int w = 0; w < kPlanWaves; ++w) {
+            if (w < wave) {
+                sb += l.misc[M_STRICT + w];
+                tb += l.misc[M_TIE + w];
             }
         }
-        int tot;
-        const int ex = block_excl_scan((strict << 16) | tie, &tot, l.scratch);
-        int sb = ex >> 16, tb = ex & 0xFFFF;
+        HS_PHASE(7);
+        // 5. assignment and metadata update
         bool any_victim = false;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
@@ -352,17 +483,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBa
                 continue;
             }
             int rank = -1;
-            if (tsv[q] < T) {
+            if ((strict_bits >> q) & 1u) {
                 rank = sb + min(tb, need_eq);
                 ++sb;
-            } else if (tsv[q] == T) {
+            } else if ((tie_bits >> q) & 1u) {
                 if (tb < need_eq) rank = sb + tb;
                 ++tb;
             }
             if (rank >= 0 && rank < m) {
-                // Stage 4 bookkeeping and metadata update: the rank-th miss (in
-                // ascending j) takes this slot; the evicted position goes back to
-                // host-only (no write-back: the host copy is authoritative).
+                // the rank-th miss (ascending j) takes this slot; the evicted
+                // position goes back to host-only (no write-back: the host copy
+                // is authoritative)
                 const int j = l.mlist[rank];
                 const int newp = l.sel[j];
                 const int old = spos[q];
@@ -375,12 +506,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBa
                 any_victim = true;
             }
         }
-        if (any_victim) store_run<PER, int>(spos_g, s0, B, spos);
-        if (any_victim || hitbits) store_run<PER, uint32_t>(ts_g, s0, B, tsv);
+        if (any_victim) store_run<PER, VEC, int>(spos_g, s0, B, spos);
+        if (any_victim || hitbits) store_run<PER, VEC, uint32_t>(ts_g, s0, B, tsv);
+        HS_PHASE(8);
     }
     __syncthreads();
+    HS_PHASE(9);
 
-    // Stage 5: publish the slot of every selection.
+    // publication of every selection's slot
     for (int j = tid; j < k; j += kPlanThreads) {
         const int v = l.sidx[j];
         out[j] = v >= 0 ? v : -2 - v;
@@ -396,6 +529,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBa
         atomicAdd(st + 2, static_cast<unsigned long long>(m) * static_cast<unsigned long long>(s.row_bytes));
         atomicAdd(st + 3, 1ull);
     }
+    HS_PHASE(10);
+    HS_PHASE_FLUSH();
 }
 
 // Publish-only resolve of a shared layer whose plan was replayed from its
@@ -411,7 +546,9 @@ __global__ __launch_bounds__(kPlanThreads) void publish_kernel(StateBase s, Laye
     int32_t* out = lb.out[blockIdx.y] + static_cast<int64_t>(r) * k;
     const int32_t* pt = s.page_table + rl * s.L_ctx;
     const int32_t* spos = s.slot_pos + rl * B;
+    __shared__ int pub_flags;
     for (int i = tid; i < (B + 31) / 32; i += kPlanThreads) pub_bits[i] = 0u;
+    if (tid == 0) pub_flags = 0;
     __syncthreads();
     int bad_range = 0, bad_dup = 0, bad_res = 0, bad_at = -1;
     for (int j = tid; j < k; j += kPlanThreads) {
@@ -433,11 +570,11 @@ __global__ __launch_bounds__(kPlanThreads) void publish_kernel(StateBase s, Laye
             bad_at = j;
         }
     }
-    const int any_range = __syncthreads_or(bad_range);
-    const int any_dup = __syncthreads_or(bad_dup);
-    const int any_res = __syncthreads_or(bad_res);
-    if (any_range || any_dup || any_res) {
-        const int code = any_range ? HS_DEV_RANGE : (any_dup ? HS_DEV_DUP : HS_DEV_NOT_RESIDENT);
+    block_or_into(&pub_flags, bad_range | (bad_dup << 1) | (bad_res << 2));
+    __syncthreads();
+    const int fl = pub_flags;
+    if (fl) {
+        const int code = (fl & 1) ? HS_DEV_RANGE : ((fl & 2) ? HS_DEV_DUP : HS_DEV_NOT_RESIDENT);
         for (int j = tid; j < k; j += kPlanThreads) out[j] = -1;
         if (tid == 0) record_error(s.err, code, layer, r, bad_at);
         return;
@@ -466,7 +603,9 @@ __global__ __launch_bounds__(kPlanThreads) void replay_meta_kernel(StateBase s, 
     }
     const int m = s.miss_count[ra];
     const int4* pa = s.plan + ra * B;
+    __shared__ int div_flag;
     for (int i = tid; i < B; i += kPlanThreads) prev_pos[i] = INT_MIN;
+    if (tid == 0) div_flag = 0;
     __syncthreads();
     for (int i = tid; i < m; i += kPlanThreads) {
         const int4 e = pa[i];
@@ -481,7 +620,9 @@ __global__ __launch_bounds__(kPlanThreads) void replay_meta_kernel(StateBase s, 
         if (sps[i] != expect) diverged = 1;
     }
     if (tid == 0 && s.clock[rs] + 1u != s.clock[ra]) diverged = 1;
-    if (__syncthreads_or(diverged)) {
+    block_or_into(&div_flag, diverged);
+    __syncthreads();
+    if (div_flag) {
         if (tid == 0) {
             s.miss_count[rs] = 0;
             record_error(s.err, HS_DEV_DIVERGED, L2, r, A);
@@ -517,35 +658,37 @@ __global__ __launch_bounds__(kPlanThreads) void replay_meta_kernel(StateBase s, 
 
 }  // namespace
 
-size_t plan_lds_bytes(int k, int hash_bits) {
-    return sizeof(int) * (2 * (static_cast<size_t>(1) << hash_bits) + 3 * static_cast<size_t>(k) + kHistBins + 32);
+size_t plan_lds_bytes(int k, int hash_bits, int B) {
+    const size_t hit_words = static_cast<size_t>(((B + 127) >> 7) << 2);
+    return sizeof(int) * (2 * (static_cast<size_t>(1) << hash_bits) + 3 * static_cast<size_t>(k) + hit_words +
+                          kHistBins + kMisc);
+}
+
+template <int PER, bool VEC>
+static hipError_t launch_plan_t(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&plan_kernel<PER, VEC>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((plan_kernel<PER, VEC>), dim3(s.R, lb.n), dim3(kPlanThreads), lds, st, s, lb);
+    return hipGetLastError();
+}
+
+template <int PER>
+static hipError_t launch_plan_p(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
+    return (s.B & 3) == 0 ? launch_plan_t<PER, true>(s, lb, lds, st) : launch_plan_t<PER, false>(s, lb, lds, st);
 }
 
 hipError_t launch_plan(const StateBase& s, const LayerBatch& lb, hipStream_t st) {
-    const dim3 grid(s.R, lb.n), block(kPlanThreads);
-    const size_t lds = plan_lds_bytes(lb.k, lb.hash_bits);
+    const size_t lds = plan_lds_bytes(lb.k, lb.hash_bits, s.B);
     const int per = (s.B + kPlanThreads - 1) / kPlanThreads;
-#define HS_PLAN_CASE(P)                                                                          \
-    case P:                                                                                      \
-        if (lds > 65536) {                                                                       \
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&plan_kernel<P>),   \
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,       \
-                                               static_cast<int>(lds));                           \
-            if (e != hipSuccess) return e;                                                       \
-        }                                                                                        \
-        hipLaunchKernelGGL(plan_kernel<P>, grid, block, lds, st, s, lb);                         \
-        break;
-    switch (per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16) {
-        HS_PLAN_CASE(1)
-        HS_PLAN_CASE(2)
-        HS_PLAN_CASE(4)
-        HS_PLAN_CASE(8)
-        HS_PLAN_CASE(16)
-        default:
-            return hipErrorInvalidValue;
-    }
-#undef HS_PLAN_CASE
-    return hipGetLastError();
+    if (per <= 1) return launch_plan_p<1>(s, lb, lds, st);
+    if (per <= 2) return launch_plan_p<2>(s, lb, lds, st);
+    if (per <= 4) return launch_plan_p<4>(s, lb, lds, st);
+    if (per <= 8) return launch_plan_p<8>(s, lb, lds, st);
+    if (per <= 16) return launch_plan_p<16>(s, lb, lds, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_publish(const StateBase& s, const LayerBatch& lb, hipStream_t st) {

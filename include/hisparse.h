@@ -178,6 +178,7 @@ int hisparse_reset(hisparse_t h);
 #define HS_OPT_FETCH_UNROLL 2   /* 16-byte loads in flight per lane: 1, 2, 4 or 8 (default 4) */
 #define HS_OPT_TIMING 3         /* 1: time every plan/fetch launch with HIP events */
 #define HS_OPT_NT_LOADS 4       /* 1: non-temporal host loads and cache stores (default 1) */
+#define HS_OPT_PHASE_TRACE 5    /* 1: the metadata kernel stamps the end of each of its phases */
 int hisparse_set_option(hisparse_t h, int key, int64_t value);
 
 /* Per-kernel times of launches issued while HS_OPT_TIMING was on, measured
@@ -189,6 +190,11 @@ typedef struct {
     int64_t dropped;  /* launches not timed because the event ring was full */
 } hs_timing;
 int hisparse_timing(hisparse_t h, hs_timing* out, int clear);
+
+/* Phase stamps of the last metadata launch of `layer` while HS_OPT_PHASE_TRACE
+ * was on: out [num_req][16] raw ticks of the device's constant wall clock
+ * (0 = phase not reached), ns_per_tick its period.  Synchronises the device. */
+int hisparse_phase_trace(hisparse_t h, int layer, uint64_t* out, double* ns_per_tick);
 
 /* Synchronous device-to-host copy (synchronises the device first), for
  * inspecting the state returned by hisparse_layer_state. */
