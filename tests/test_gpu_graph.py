@@ -1,0 +1,73 @@
+"""RESOLVE inside a HIP graph: a captured decode step replayed over many steps
+equals the same steps run eagerly, bit-exactly (the step clock lives on the
+device, the grid is fixed and no call allocates, synchronises or records a
+memset).  Eager work and synchronisations run between the replays."""
+import numpy as np
+import pytest
+
+import tracegen as tg
+from gpu_helpers import make_pool, make_resolver
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module")
+def hs():
+    import hierarchical_kv_cache_resolve_amd as m
+    return m
+
+
+@pytest.mark.parametrize("prefetch", [False, True], ids=["plain", "prefetch"])
+def test_graph_replay_equals_eager(hs, prefetch):
+    w = tg.PREFETCH.replace(name="graph", num_req=4, num_layers=8, group=4 if prefetch else 1, L_ctx=30000,
+                            k=512, B=1024, steps=10, W_KV=64)
+    tr = tg.trace(w)
+    pool = make_pool(hs, w)
+    eager = make_resolver(hs, w, pool)
+    graphed = make_resolver(hs, w, pool)
+    dev = torch.device("cuda:0")
+    sel = torch.from_numpy(tr).to(dev)
+    sel_buf = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
+    out_buf = torch.empty_like(sel_buf)
+    out_eager = torch.empty_like(sel_buf)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        cur = torch.cuda.current_stream()
+        for g0 in range(0, w.num_layers, w.group):
+            graphed.resolve(g0, sel_buf[g0], out_buf[g0], cur)
+            shared = list(range(g0 + 1, g0 + w.group))
+            if shared:
+                side.wait_stream(cur)
+                graphed.prefetch(g0, shared, side)
+            for l in shared:
+                graphed.resolve(l, sel_buf[l], out_buf[l], cur)
+    main = torch.cuda.current_stream()
+    for t in range(w.steps):
+        sel_buf.copy_(sel[t])
+        g.replay()
+        junk = torch.randn(1 << 20, device=dev).sum()  # unrelated eager work between replays
+        for g0 in range(0, w.num_layers, w.group):
+            eager.resolve(g0, sel[t, g0], out_eager[g0], main)
+            shared = list(range(g0 + 1, g0 + w.group))
+            if shared:
+                eager.prefetch(g0, shared, side)
+            for l in shared:
+                eager.resolve(l, sel[t, l], out_eager[l], main)
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+        assert np.array_equal(out_buf.cpu().numpy(), out_eager.cpu().numpy()), f"replay {t}"
+        for l in range(w.num_layers):
+            a, b = graphed.state(l), eager.state(l)
+            for key in ("slot_pos", "ts", "clock", "page_table", "miss_count"):
+                assert np.array_equal(a[key], b[key]), f"{key} replay {t} layer {l}"
+            occ = b["slot_pos"] >= 0
+            assert np.array_equal(graphed.cache_layer(l)[occ], eager.cache_layer(l)[occ])
+    assert graphed.error()[0] == 0 and eager.error()[0] == 0
+    del g
+    graphed.close()
+    eager.close()
+    pool.free()
