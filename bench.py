@@ -70,6 +70,11 @@ def parse():
     ap.add_argument("--coherent", action="store_true")
     ap.add_argument("--timing", type=int, default=1, help="replay the timed steps with HIP events on every launch")
     ap.add_argument("--graph", type=int, default=1, help="run the timed steps as one captured HIP graph")
+    ap.add_argument("--prefetch", type=int, default=1, help="shared-selection workloads: replay anchor plans")
+    ap.add_argument("--consumer", type=int, default=-1,
+                    help="run the gather-checksum consumer after every layer (default: on for shared workloads)")
+    ap.add_argument("--hit-only-workload", default="gqa_record",
+                    help="shapes of the hit-only leg (its pool aliases every history onto one region)")
     return ap.parse_args()
 
 
@@ -85,6 +90,8 @@ def main():
     import tracegen as tg
 
     w = tg.WORKLOADS[args.workload]
+    if args.consumer < 0:
+        args.consumer = 1 if w.group > 1 else 0
     W, K = args.warmup, args.steps
     nthreads = max(1, min(16, os.cpu_count() or 1))
     dev = torch.device("cuda:0")
@@ -111,39 +118,65 @@ def main():
     out = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
-    def step(t):
-        for l in range(w.num_layers):
-            res.resolve(l, sel[t, l], out[l], sptr)
+    use_prefetch = w.group > 1 and args.prefetch
+    side = torch.cuda.Stream() if use_prefetch else None
+    cs = torch.empty((w.num_layers, w.num_req), dtype=torch.int64, device=dev) if args.consumer else None
+
+    def step(t, sp, capturing=False, prefetch=use_prefetch):
+        if not prefetch:
+            for l in range(w.num_layers):
+                res.resolve(l, sel[t, l], out[l], sp)
+                if cs is not None:
+                    res.gather_checksum(l, out[l], cs[l], sp)
+            return
+        # shared-selection groups: anchor, replay of its plan on the side
+        # stream, then the shared layers only publish
+        for g0 in range(0, w.num_layers, w.group):
+            res.resolve(g0, sel[t, g0], out[g0], sp)
+            shared = list(range(g0 + 1, min(g0 + w.group, w.num_layers)))
+            if capturing:
+                side.wait_stream(torch.cuda.current_stream())
+            res.prefetch(g0, shared, side)
+            if cs is not None:
+                res.gather_checksum(g0, out[g0], cs[g0], sp)
+            for l in shared:
+                res.resolve(l, sel[t, l], out[l], sp)
+                if cs is not None:
+                    res.gather_checksum(l, out[l], cs[l], sp)
+
+    def timed_run(prefetch):
+        """Run steps W..W+K-1 (as one captured graph unless --graph 0); returns seconds."""
+        graph = None
+        if args.graph:
+            # the timed steps as one HIP graph: every input already resident,
+            # every pointer fixed, the step clock on the device
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                cap = torch.cuda.current_stream().cuda_stream
+                for t in range(W, W + K):
+                    step(t, cap, capturing=True, prefetch=prefetch)
+            torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        if graph is not None:
+            graph.replay()
+        else:
+            for t in range(W, W + K):
+                step(t, sptr, prefetch=prefetch)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        del graph
+        return dt
 
     for t in range(W):
-        step(t)
+        step(t, sptr)
     torch.cuda.synchronize()
-    graph = None
-    if args.graph:
-        # the timed steps as one HIP graph: every input already resident, every
-        # pointer fixed, the step clock on the device
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            cap = torch.cuda.current_stream().cuda_stream
-            for t in range(W, W + K):
-                for l in range(w.num_layers):
-                    res.resolve(l, sel[t, l], out[l], cap)
-        torch.cuda.synchronize()
     s0 = res.stats()
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    if graph is not None:
-        graph.replay()
-    else:
-        for t in range(W, W + K):
-            step(t)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
+    elapsed = timed_run(use_prefetch)
     s1 = res.stats()
     code, el, er = res.error()
     if code:
         raise SystemExit(f"device error {code} at layer {el} request {er}")
-    del graph
 
     # Per-kernel durations: HIP events around every launch perturb the step
     # (about 1 us per event), so they are taken on a replay of the same steps
@@ -152,18 +185,32 @@ def main():
     if args.timing:
         res.reset()
         for t in range(W):
-            step(t)
+            step(t, sptr)
         res.set_option(hs.HS_OPT_TIMING, 1)
         res.timing(clear=True)
         r0 = res.stats()
+        anchors = set(range(0, w.num_layers, w.group)) if use_prefetch else set()
+        r0_layers = [res.stats(l) if l in anchors else None for l in range(w.num_layers)]
         for t in range(W, W + K):
-            step(t)
+            step(t, sptr)
         torch.cuda.synchronize()
         r1 = res.stats()
+        r1_layers = [res.stats(l) if l in anchors else None for l in range(w.num_layers)]
         tim = res.timing(clear=True)
         res.set_option(hs.HS_OPT_TIMING, 0)
         if r1.miss_bytes - r0.miss_bytes != s1.miss_bytes - s0.miss_bytes:
             raise SystemExit("instrumented replay moved different bytes than the timed run")
+
+    prefetch_cmp = None
+    if use_prefetch:
+        res.reset()
+        for t in range(W):
+            step(t, sptr, prefetch=False)
+        off = timed_run(False)
+        prefetch_cmp = {"ms_per_step_prefetch_on": elapsed * 1e3 / K, "ms_per_step_prefetch_off": off * 1e3 / K,
+                        "consumer_between_layers": bool(cs is not None),
+                        "saving": 1.0 - elapsed / off}
+        log(f"prefetch on {elapsed * 1e3 / K:.3f} ms/step, off {off * 1e3 / K:.3f} ms/step")
 
     sels = K * w.num_layers * w.num_req * w.k
     misses = s1.misses - s0.misses
@@ -197,6 +244,8 @@ def main():
         "selections_per_layer_step": w.num_req * w.k,
         "layer_steps_per_s": K * w.num_layers / elapsed,
     }
+    if prefetch_cmp:
+        result["prefetch"] = prefetch_cmp
 
     # peaks measured in the same run
     link_sdma = link_kernel = hbm_peak = None
@@ -226,8 +275,15 @@ def main():
         fetch_avg_ms = tim.fetch_ms / tim.fetch_launches
         plan_avg_ms = tim.plan_ms / tim.plan_launches
         # algorithmic bytes of the fetch kernel: every missed record crosses the
-        # host link once (and is written once to HBM)
-        achieved = miss_bytes / (tim.fetch_ms * 1e-3) / 1e9
+        # host link once (and is written once to HBM).  With prefetch, the main
+        # stream's fetch launches carry the anchors' misses only; the shared
+        # layers' copies are the replay launches on the side stream.
+        if use_prefetch:
+            fetch_bytes = sum(r1l.miss_bytes - r0l.miss_bytes for r0l, r1l in zip(r0_layers, r1_layers)
+                              if r0l is not None)
+        else:
+            fetch_bytes = miss_bytes
+        achieved = fetch_bytes / (tim.fetch_ms * 1e-3) / 1e9
         result["roofline"] = {
             "kernel": "fetch_kernel (host-mapped 16 B loads -> HBM cache rows)",
             "bound": "host_link",
@@ -240,8 +296,13 @@ def main():
             "peak_note": "peak = max(SDMA H2D copy, 16 B-load streaming kernel) measured in this run; "
                          f"published PCIe 5.0 x16 = {PCIE5_X16_GBPS} GB/s per direction",
             "avg_launch_ms": fetch_avg_ms,
-            "bytes_per_launch": miss_bytes / tim.fetch_launches,
+            "bytes_per_launch": fetch_bytes / tim.fetch_launches,
         }
+        if tim.replay_launches:
+            result["kernels_replay"] = {"replay_avg_ms": tim.replay_ms / tim.replay_launches,
+                                        "replay_launches": tim.replay_launches,
+                                        "publish_avg_ms": tim.publish_ms / max(1, tim.publish_launches),
+                                        "replay_GBps": (miss_bytes - fetch_bytes) / (tim.replay_ms * 1e-3) / 1e9}
         meta_bytes_per_layer_step = w.num_req * (4 * w.k + 4 * w.B + 4 * w.B + 4 * w.k)
         result["kernels"] = {
             "fetch_avg_ms": fetch_avg_ms, "fetch_launches": tim.fetch_launches,
@@ -255,7 +316,7 @@ def main():
     res.close()
 
     if not args.no_hit_only:
-        result["hit_only"] = hit_only_leg(hs, tg, torch, w, pool, dev, sptr, hbm_peak)
+        result["hit_only"] = hit_only_leg(hs, tg, torch, tg.WORKLOADS[args.hit_only_workload], dev, sptr, hbm_peak)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(tg, w, tr, pool, W, args.cpu_seconds)
@@ -264,14 +325,18 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def hit_only_leg(hs, tg, torch, w, pool, dev, sptr, hbm_peak, steps=64):
+def hit_only_leg(hs, tg, torch, w, dev, sptr, hbm_peak, steps=64):
     """Metadata path alone: every step after the first repeats it, so every
     selection hits and nothing crosses the host link.  Timed as captured HIP
-    graphs (one per variant) so that host launch cost does not enter."""
+    graphs (one per variant) so that host launch cost does not enter.  Only
+    the first (filling) step reads the pool, so every history aliases onto
+    one region of L_ctx rows."""
     wh = tg.hit_only(w)
     tr = torch.from_numpy(tg.trace(wh, steps=2)).to(dev)
-    res = hs.Resolver(w.num_req, w.num_layers, w.B, w.W_KV, hs.BF16, pool, w.L_ctx, w.pool_rows,
-                      region_row=w.region_rows())
+    pool = hs.HostPool.allocate(w.L_ctx * w.row_bytes)
+    tg.pool_fill(pool.ptr, 0, w.L_ctx * w.W_KV, w.pool_seed)
+    res = hs.Resolver(w.num_req, w.num_layers, w.B, w.W_KV, hs.BF16, pool, w.L_ctx, w.L_ctx,
+                      region_row=np.zeros(w.num_req * w.num_layers, dtype=np.int64))
     out = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
     for l in range(w.num_layers):
         res.resolve(l, tr[0, l], out[l], sptr)
@@ -280,6 +345,8 @@ def hit_only_leg(hs, tg, torch, w, pool, dev, sptr, hbm_peak, steps=64):
     # (4B); write the hit stamps (4k) and the published slots (4k)
     per_rl = 4 * w.k + 4 * w.k + 4 * w.B + 4 * w.k + 4 * w.k
     layers = list(range(w.num_layers))
+    nb = max(1, min(len(layers), 8192 // w.num_req, 32))  # layers per batched launch
+    batches = [layers[i:i + nb] for i in range(0, len(layers), nb)]
     torch.cuda.synchronize()
     g1, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     with torch.cuda.graph(g1):
@@ -290,7 +357,8 @@ def hit_only_leg(hs, tg, torch, w, pool, dev, sptr, hbm_peak, steps=64):
     with torch.cuda.graph(g2):
         cap = torch.cuda.current_stream().cuda_stream
         for _ in range(steps):
-            res.resolve_layers(layers, [tr[1, l] for l in layers], [out[l] for l in layers], cap)
+            for b in batches:
+                res.resolve_layers(b, [tr[1, l] for l in b], [out[l] for l in b], cap)
     torch.cuda.synchronize()
     g1.replay()  # warm
     torch.cuda.synchronize()
@@ -305,13 +373,16 @@ def hit_only_leg(hs, tg, torch, w, pool, dev, sptr, hbm_peak, steps=64):
     st = res.stats()
     del g1, g2
     res.close()
+    pool.free()
     total = per_rl * w.num_req * w.num_layers * steps
     r = {
+        "workload": f"{w.name} shapes: {w.num_req} requests x {w.num_layers} layers, k={w.k}, B={w.B}",
         "bytes_per_request_layer": per_rl,
         "per_layer_launch_GBps": total / per_layer / 1e9,
         "per_layer_resolve_us": per_layer / (steps * w.num_layers) * 1e6,
         "batched_all_layers_GBps": total / batched / 1e9,
-        "batched_resolve_us": batched / steps * 1e6,
+        "batched_step_us": batched / steps * 1e6,
+        "batched_launches_per_step": len(batches),
         "hbm_peak_GBps": hbm_peak,
         "hbm_published_GBps": 8000.0,
         "misses_after_fill": int(st.misses - w.num_req * w.num_layers * w.k),
@@ -321,7 +392,7 @@ def hit_only_leg(hs, tg, torch, w, pool, dev, sptr, hbm_peak, steps=64):
         r["per_layer_frac_of_hbm_peak"] = r["per_layer_launch_GBps"] / hbm_peak
         r["batched_frac_of_hbm_peak"] = r["batched_all_layers_GBps"] / hbm_peak
     log(f"hit-only: per-layer {r['per_layer_resolve_us']:.1f} us/resolve ({r['per_layer_launch_GBps']:.1f} GB/s), "
-        f"batched {r['batched_resolve_us']:.1f} us ({r['batched_all_layers_GBps']:.1f} GB/s)")
+        f"batched {r['batched_step_us']:.1f} us/step ({r['batched_all_layers_GBps']:.1f} GB/s)")
     return r
 
 

@@ -32,6 +32,7 @@ struct hisparse_ctx {
     std::vector<hipEvent_t> ev_plan, ev_join;
     std::vector<int> pending_anchor;   // shared layer -> anchor whose replay it must publish, or -1
     std::vector<char> join_outstanding;
+    std::vector<char> plan_in_capture, join_in_capture;  // event recorded while its stream was capturing
     std::vector<char> last_was_plan;
     std::vector<int64_t> steps;
     std::vector<int> last_k;
@@ -119,6 +120,24 @@ int init_state(hisparse_ctx* h, hipStream_t st) {
 }
 
 bool valid(hisparse_t h) { return h != nullptr && h->s.cache != nullptr; }
+
+bool capturing(hipStream_t st) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return cs == hipStreamCaptureStatusActive;
+}
+
+// Make `st` wait for `ev`.  Inside a graph capture, an event recorded before
+// the capture began cannot be waited on; such an event has completed (a
+// capture starts from an idle device), so the wait is dropped.
+int wait_event(hipStream_t st, hipEvent_t ev, bool ev_in_capture) {
+    if (capturing(st) && !ev_in_capture) return HS_OK;
+    HS_TRY(hipStreamWaitEvent(st, ev, 0));
+    return HS_OK;
+}
 
 // Launch `fn` bracketed by timing events when timing is on.
 template <typename F>
@@ -241,6 +260,8 @@ int hisparse_create(int num_req, int num_layers, int B, int W_KV, int dtype, con
     }
     h->pending_anchor.assign(num_layers, -1);
     h->join_outstanding.assign(num_layers, 0);
+    h->plan_in_capture.assign(num_layers, 0);
+    h->join_in_capture.assign(num_layers, 0);
     h->last_was_plan.assign(num_layers, 0);
     h->steps.assign(num_layers, 0);
     h->last_k.assign(num_layers, 0);
@@ -281,7 +302,8 @@ static int resolve_plan_path(hisparse_t h, int n, const int* layers, const int32
         const int l = layers[i];
         if (h->join_outstanding[l]) {
             // this anchor's previous replay may still read its plan and state
-            HS_TRY(hipStreamWaitEvent(st, h->ev_join[l], 0));
+            const int rc = wait_event(st, h->ev_join[l], h->join_in_capture[l]);
+            if (rc != HS_OK) return rc;
             h->join_outstanding[l] = 0;
         }
         lb.sel[i] = sel[i];
@@ -291,7 +313,11 @@ static int resolve_plan_path(hisparse_t h, int n, const int* layers, const int32
     }
     int rc = timed(h, K_PLAN, st, [&] { return hs::launch_plan(h->s, lb, st); });
     if (rc != HS_OK) return rc;
-    for (int i = 0; i < n; ++i) HS_TRY(hipEventRecord(h->ev_plan[layers[i]], st));
+    const bool cap = capturing(st);
+    for (int i = 0; i < n; ++i) {
+        HS_TRY(hipEventRecord(h->ev_plan[layers[i]], st));
+        h->plan_in_capture[layers[i]] = cap;
+    }
     rc = timed(h, K_FETCH, st, [&] { return hs::launch_fetch(h->s, fb, h->fetch_blocks, h->unroll, h->nt, st); });
     if (rc != HS_OK) return rc;
     for (int i = 0; i < n; ++i) {
@@ -313,7 +339,8 @@ int hisparse_resolve(hisparse_t h, int layer, const int32_t* d_sel, int k, int32
     const int anchor = h->pending_anchor[layer];
     if (anchor >= 0) {
         if (k != h->last_k[anchor]) return HS_E_ORDER;
-        HS_TRY(hipStreamWaitEvent(st, h->ev_join[anchor], 0));
+        rc = wait_event(st, h->ev_join[anchor], h->join_in_capture[anchor]);
+        if (rc != HS_OK) return rc;
         hs::LayerBatch lb{};
         lb.n = 1;
         lb.k = k;
@@ -365,7 +392,8 @@ int hisparse_prefetch(hisparse_t h, int anchor, const int* shared, int n, void* 
         if (h->pending_anchor[l] >= 0 || h->steps[l] != h->steps[anchor] - 1) return HS_E_ORDER;
     }
     hipStream_t side = static_cast<hipStream_t>(side_stream);
-    HS_TRY(hipStreamWaitEvent(side, h->ev_plan[anchor], 0));
+    const int wrc = wait_event(side, h->ev_plan[anchor], h->plan_in_capture[anchor]);
+    if (wrc != HS_OK) return wrc;
     hs::ReplayBatch rb{};
     hs::FetchBatch fb{};
     rb.anchor = anchor;
@@ -383,6 +411,7 @@ int hisparse_prefetch(hisparse_t h, int anchor, const int* shared, int n, void* 
     });
     if (rc != HS_OK) return rc;
     HS_TRY(hipEventRecord(h->ev_join[anchor], side));
+    h->join_in_capture[anchor] = capturing(side);
     h->join_outstanding[anchor] = 1;
     for (int i = 0; i < n; ++i) h->pending_anchor[shared[i]] = anchor;
     return HS_OK;

@@ -145,7 +145,17 @@ __global__ __launch_bounds__(kFetchThreads) void hbm_copy_kernel(const u32x4* sr
     }
 }
 
-// Consumer stand-in: one workgroup per request reads the k published records.
+// Consumer stand-in: reads the k published records of every request and
+// reduces them to one checksum per request.  grid = (request, chunk of
+// records); each workgroup adds its partial sum with a 64-bit atomic (the sum
+// is modulo 2^64, so the order of the additions does not matter).
+constexpr int kGatherRowsPerBlock = 32;
+
+__global__ __launch_bounds__(kFetchThreads) void gather_zero_kernel(uint64_t* out, int n) {
+    const int i = blockIdx.x * kFetchThreads + threadIdx.x;
+    if (i < n) out[i] = 0ull;
+}
+
 __global__ __launch_bounds__(kFetchThreads) void gather_checksum_kernel(StateBase s, int layer,
                                                                         const int32_t* slot_idx, int k,
                                                                         uint64_t* out) {
@@ -153,15 +163,18 @@ __global__ __launch_bounds__(kFetchThreads) void gather_checksum_kernel(StateBas
     const int r = blockIdx.x;
     const int64_t rl = static_cast<int64_t>(layer) * s.R + r;
     const int Q = static_cast<int>(s.row_bytes >> 3);
-    const int64_t n = static_cast<int64_t>(k) * Q;
+    const int j0 = blockIdx.y * kGatherRowsPerBlock;
+    const int j1 = min(k, j0 + kGatherRowsPerBlock);
+    const int64_t n = static_cast<int64_t>(j1 - j0) * Q;
     const int32_t* sidx = slot_idx + static_cast<int64_t>(r) * k;
     uint64_t acc = 0;
     for (int64_t i = threadIdx.x; i < n; i += kFetchThreads) {
-        const int j = static_cast<int>(i / Q), q = static_cast<int>(i - static_cast<int64_t>(j) * Q);
+        const int jj = static_cast<int>(i / Q), q = static_cast<int>(i - static_cast<int64_t>(jj) * Q);
+        const int j = j0 + jj;
         const int slot = sidx[j];
         if (slot < 0 || slot >= s.B) continue;
         const uint64_t w = reinterpret_cast<const uint64_t*>(s.cache + (rl * s.B + slot) * s.row_bytes)[q];
-        acc += w * (2ull * static_cast<uint64_t>(i) + 1ull);
+        acc += w * (2ull * (static_cast<uint64_t>(j) * static_cast<uint64_t>(Q) + static_cast<uint64_t>(q)) + 1ull);
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
@@ -170,7 +183,7 @@ __global__ __launch_bounds__(kFetchThreads) void gather_checksum_kernel(StateBas
     if (threadIdx.x == 0) {
         uint64_t t = 0;
         for (int w = 0; w < kFetchThreads / 64; ++w) t += part[w];
-        out[r] = t;
+        atomicAdd(reinterpret_cast<unsigned long long*>(out + r), static_cast<unsigned long long>(t));
     }
 }
 
@@ -198,7 +211,10 @@ hipError_t launch_fetch(const StateBase& s, const FetchBatch& fb, int blocks, in
 
 hipError_t launch_gather_checksum(const StateBase& s, int layer, const int32_t* slot_idx, int k, uint64_t* out,
                                   hipStream_t st) {
-    hipLaunchKernelGGL(gather_checksum_kernel, dim3(s.R), dim3(kFetchThreads), 0, st, s, layer, slot_idx, k, out);
+    hipLaunchKernelGGL(gather_zero_kernel, dim3((s.R + kFetchThreads - 1) / kFetchThreads), dim3(kFetchThreads), 0,
+                       st, out, s.R);
+    const dim3 grid(s.R, (k + kGatherRowsPerBlock - 1) / kGatherRowsPerBlock);
+    hipLaunchKernelGGL(gather_checksum_kernel, grid, dim3(kFetchThreads), 0, st, s, layer, slot_idx, k, out);
     return hipGetLastError();
 }
 

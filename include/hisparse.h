@@ -32,6 +32,10 @@
  *     slot_idx entry and its cache state is left unchanged.
  *   - A handle is not thread-safe.  Calls for one layer must be issued in
  *     decode-step order on one stream (or be ordered by the caller's events).
+ *   - Graph capture: resolve and prefetch may be captured (the prefetch side
+ *     stream must join the capture, e.g. by waiting on the capturing stream).
+ *     A capture must begin with the device idle: inside a capture the library
+ *     drops its waits on its own events that were recorded before the capture.
  *
  * Layouts (all row-major, C order)
  *   host pool      rows of W_KV*s bytes; the history of (request r, layer l)
