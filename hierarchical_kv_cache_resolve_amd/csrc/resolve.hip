@@ -209,6 +209,119 @@ __device__ inline void reject(const StateBase& s, int32_t* out, int k, int64_t r
 
 constexpr int kMaxSelPerLane = HS_MAX_K / kPlanThreads;  // 4
 
+// Histogram increment for this lane's bin (-1: none).  When every active
+// lane of the wave has the same bin (an empty cache, or one stamp shared by
+// the whole wave) a single atomic adds the count; otherwise one atomic per
+// lane.  Called by all lanes of the wave.
+__device__ inline void hist_add(int* hist, int bin) {
+    const unsigned long long act = __ballot(bin >= 0);
+    if (act == 0ull) return;
+    const int lead = __ffsll(static_cast<long long>(act)) - 1;
+    const int b0 = __shfl(bin, lead, 64);
+    if (__ballot(bin == b0) == act) {
+        if ((threadIdx.x & 63) == lead) atomicAdd(&hist[b0], __popcll(act));
+    } else if (bin >= 0) {
+        atomicAdd(&hist[bin], 1);
+    }
+}
+
+// With l.hist holding counts per bin (bin b at index b), find the bin where
+// the count taken from the top bin downwards first reaches `need`; `below`
+// is the count of the bins above it.  Leaves l.hist zeroed.  Barriers inside.
+__device__ inline void find_crossing_from_top(const PlanLds& l, int need, int& bin, int& below) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int my_bin = kHistBins - 1 - tid;
+    const int hb = l.hist[my_bin];
+    l.hist[my_bin] = 0;
+    const int incl = wave_incl_scan(hb);
+    if (lane == 63) l.misc[M_HIST + wave] = incl;
+    __syncthreads();
+    int excl = incl - hb;
+#pragma unroll
+    for (int w = 0; w < kPlanWaves; ++w)
+        if (w < wave) excl += l.misc[M_HIST + w];
+    if (excl < need && need <= excl + hb) {
+        l.misc[M_BIN] = my_bin;
+        l.misc[M_BELOW] = excl;
+    }
+    __syncthreads();
+    bin = l.misc[M_BIN];
+    below = l.misc[M_BELOW];
+}
+
+// General threshold search among the slots flagged in `elig` (this lane's
+// run): the m-th smallest stamp T and how many slots stamped exactly T are
+// taken.  Min/max reduction, then a radix select over stamps relative to the
+// minimum in 10-bit digits from the top.  Expects l.hist zeroed; leaves it
+// zeroed.  Barriers inside.
+template <int PER>
+__device__ inline void radix_select(const PlanLds& l, const uint32_t (&tsv)[PER], unsigned elig, int m,
+                                    uint32_t& T, int& need_eq) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    unsigned mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        if ((elig >> q) & 1u) {
+            mn = min(mn, tsv[q]);
+            mx = max(mx, tsv[q]);
+        }
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) {
+        l.misc[M_MIN + wave] = static_cast<int>(mn);
+        l.misc[M_MAX + wave] = static_cast<int>(mx);
+    }
+    __syncthreads();
+    mn = 0xFFFFFFFFu;
+    mx = 0u;
+#pragma unroll
+    for (int w = 0; w < kPlanWaves; ++w) {
+        mn = min(mn, static_cast<unsigned>(l.misc[M_MIN + w]));
+        mx = max(mx, static_cast<unsigned>(l.misc[M_MAX + w]));
+    }
+    if (mn == mx) {
+        T = mn;
+        need_eq = m;
+        return;
+    }
+    const int nbits = 32 - __clz(static_cast<int>(mx - mn));
+    uint64_t prefix = 0;
+    int remaining = m, pos = nbits;
+    while (pos > 0) {
+        const int d = pos < 10 ? pos : 10;
+        pos -= d;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            int bin = -1;
+            if ((elig >> q) & 1u) {
+                const uint64_t rel = static_cast<uint64_t>(tsv[q] - mn);
+                if ((rel >> (pos + d)) == prefix) bin = static_cast<int>((rel >> pos) & ((1u << d) - 1u));
+            }
+            hist_add(l.hist, bin);
+        }
+        __syncthreads();
+        const int hb = l.hist[tid];
+        l.hist[tid] = 0;
+        const int incl = wave_incl_scan(hb);
+        if (lane == 63) l.misc[M_HIST + wave] = incl;
+        __syncthreads();
+        int bl = incl - hb;
+#pragma unroll
+        for (int w = 0; w < kPlanWaves; ++w)
+            if (w < wave) bl += l.misc[M_HIST + w];
+        if (bl < remaining && remaining <= bl + hb) {
+            l.misc[M_BIN] = tid;
+            l.misc[M_BELOW] = bl;
+        }
+        __syncthreads();
+        prefix = (prefix << d) | static_cast<uint64_t>(l.misc[M_BIN]);
+        remaining -= l.misc[M_BELOW];
+    }
+    T = mn + static_cast<uint32_t>(prefix);
+    need_eq = remaining;
+}
+
 // The metadata half of RESOLVE for one (request, layer).
 //   1. every global read is issued up front: clock, selection, slot map and
 //      stamps of this lane's slot run, then the page-table entry of each
@@ -375,68 +488,36 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBa
             T = 0xFFFFFFFFu;  // every candidate is a victim (stamps never reach this value)
             need_eq = 0;
         } else {
-            unsigned mn = 0xFFFFFFFFu, mx = 0u;
+            // Histogram of candidate ages a = 2t - stamp (no stamp exceeds 2t
+            // before step t); ages of 1023 and more share the top bin.  The m
+            // victims are the oldest, so the crossing is counted from the top.
+            const uint32_t top = 2u * t;
+            unsigned cand_bits = 0;
 #pragma unroll
             for (int q = 0; q < PER; ++q) {
+                int bin = -1;
                 if (s0 + q < B && !((hitbits >> q) & 1u)) {
-                    mn = min(mn, tsv[q]);
-                    mx = max(mx, tsv[q]);
+                    cand_bits |= 1u << q;
+                    const uint32_t age = top - tsv[q];
+                    bin = age < kHistBins - 1 ? static_cast<int>(age) : kHistBins - 1;
                 }
-            }
-            mn = wave_min(mn);
-            mx = wave_max(mx);
-            if (lane == 0) {
-                l.misc[M_MIN + wave] = static_cast<int>(mn);
-                l.misc[M_MAX + wave] = static_cast<int>(mx);
+                hist_add(l.hist, bin);
             }
             __syncthreads();
-            mn = 0xFFFFFFFFu;
-            mx = 0u;
-#pragma unroll
-            for (int w = 0; w < kPlanWaves; ++w) {
-                mn = min(mn, static_cast<unsigned>(l.misc[M_MIN + w]));
-                mx = max(mx, static_cast<unsigned>(l.misc[M_MAX + w]));
-            }
-            if (mn == mx) {
-                T = mn;
-                need_eq = m;
+            int bin, below;
+            find_crossing_from_top(l, m, bin, below);
+            if (bin < kHistBins - 1) {
+                T = top - static_cast<uint32_t>(bin);
+                need_eq = m - below;
             } else {
-                // Radix select over stamps relative to the minimum, 10-bit
-                // digits from the top; usually one pass.
-                const int nbits = 32 - __clz(static_cast<int>(mx - mn));
-                uint64_t prefix = 0;
-                int remaining = m, pos = nbits;
-                while (pos > 0) {
-                    const int d = pos < 10 ? pos : 10;
-                    pos -= d;
+                // All m victims are at least 1023 ages old: select among those
+                // with a radix select on their stamps.
+                unsigned old_bits = 0;
 #pragma unroll
-                    for (int q = 0; q < PER; ++q) {
-                        if (s0 + q < B && !((hitbits >> q) & 1u)) {
-                            const uint64_t rel = static_cast<uint64_t>(tsv[q] - mn);
-                            if ((rel >> (pos + d)) == prefix)
-                                atomicAdd(&l.hist[static_cast<int>((rel >> pos) & ((1u << d) - 1u))], 1);
-                        }
-                    }
-                    __syncthreads();
-                    const int hb = l.hist[tid];
-                    l.hist[tid] = 0;  // ready for the next pass
-                    const int incl = wave_incl_scan(hb);
-                    if (lane == 63) l.misc[M_HIST + wave] = incl;
-                    __syncthreads();
-                    int below = incl - hb;
-#pragma unroll
-                    for (int w = 0; w < kPlanWaves; ++w)
-                        if (w < wave) below += l.misc[M_HIST + w];
-                    if (below < remaining && remaining <= below + hb) {
-                        l.misc[M_BIN] = tid;
-                        l.misc[M_BELOW] = below;
-                    }
-                    __syncthreads();
-                    prefix = (prefix << d) | static_cast<uint64_t>(l.misc[M_BIN]);
-                    remaining -= l.misc[M_BELOW];
-                }
-                T = mn + static_cast<uint32_t>(prefix);
-                need_eq = remaining;
+                for (int q = 0; q < PER; ++q)
+                    if (((cand_bits >> q) & 1u) && top - tsv[q] >= static_cast<uint32_t>(kHistBins - 1))
+                        old_bits |= 1u << q;
+                radix_select<PER>(l, tsv, old_bits, m, T, need_eq);
             }
         }
         HS_PHASE(6);

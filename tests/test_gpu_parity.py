@@ -229,3 +229,40 @@ def test_reset_refills_exactly(hs):
             assert np.array_equal(res.cache_layer(l)[occ], o.cache[l][occ])
     res.close()
     pool.free()
+
+
+def test_victims_older_than_histogram_range(hs):
+    """Victims whose stamps are more than 1023 apart from 2t (slots filled early
+    and never touched again) take the kernel's general radix-select path; a
+    hand-built trace forces it, the oracle decides."""
+    from oracle import Oracle
+    rng = np.random.default_rng(7)
+    R, L_ctx, k, B, W_KV = 2, 1000, 8, 32, 8
+    perm = [rng.permutation(L_ctx).astype(np.int32) for _ in range(R)]
+    steps = []
+    for t in range(4):                        # fill 32 slots at 4 different stamps
+        steps.append(np.stack([p[8 * t:8 * t + 8] for p in perm]))
+    for _ in range(4, 700):                   # then only step 3's positions, all hits
+        steps.append(steps[3].copy())
+    for t in range(700, 712):                 # bursts of new positions
+        steps.append(np.stack([p[32 + 8 * (t - 700):40 + 8 * (t - 700)] for p in perm]))
+    w = tg.Workload("old_victims", R, 1, L_ctx, W_KV, 2, k, B, len(steps), seed_index=41)
+    pool = make_pool(hs, w)
+    pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
+    res = make_resolver(hs, w, pool)
+    o = Oracle(R, 1, B, L_ctx, w.row_bytes)
+    dev = torch.device("cuda:0")
+    out = torch.empty((R, k), dtype=torch.int32, device=dev)
+    for t, S in enumerate(steps):
+        res.resolve(0, torch.from_numpy(S).to(dev), out)
+        ref = o.resolve(0, S, pool_np, w.region_rows())
+        if t >= 690 or t < 6:
+            got = out.cpu().numpy()
+            assert np.array_equal(got, ref["slot_idx"]), f"step {t}"
+            st = res.state(0)
+            assert np.array_equal(st["slot_pos"], o.slot_pos[0]) and np.array_equal(st["ts"], o.ts[0]), f"step {t}"
+            m = int(ref["miss_count"][0])
+            assert np.array_equal(st["plan"][0, :m], ref["plan"][0, :m]), f"plan step {t}"
+    assert res.error()[0] == 0
+    res.close()
+    pool.free()
