@@ -28,6 +28,7 @@ struct hisparse_ctx {
     int unroll = 4;
     bool nt = true;
     bool timing = false;
+    int probe = HS_PROBE_PAGE_TABLE;
     // ordering of resolve / prefetch (host-side bookkeeping only)
     std::vector<hipEvent_t> ev_plan, ev_join;
     std::vector<int> pending_anchor;   // shared layer -> anchor whose replay it must publish, or -1
@@ -297,6 +298,7 @@ static int resolve_plan_path(hisparse_t h, int n, const int* layers, const int32
     lb.n = n;
     lb.k = k;
     lb.hash_bits = hash_bits_for(k);
+    lb.probe = h->probe;
     fb.n = n;
     for (int i = 0; i < n; ++i) {
         const int l = layers[i];
@@ -503,6 +505,10 @@ int hisparse_set_option(hisparse_t h, int key, int64_t value) {
         case HS_OPT_FETCH_UNROLL:
             if (value != 1 && value != 2 && value != 4 && value != 8) return HS_E_INVAL;
             h->unroll = static_cast<int>(value);
+            return HS_OK;
+        case HS_OPT_PROBE:
+            if (value != HS_PROBE_PAGE_TABLE && value != HS_PROBE_SLOT_SCAN) return HS_E_INVAL;
+            h->probe = static_cast<int>(value);
             return HS_OK;
         case HS_OPT_NT_LOADS:
             h->nt = value != 0;

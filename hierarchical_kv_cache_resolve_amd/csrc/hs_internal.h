@@ -57,6 +57,7 @@ struct LayerBatch {
     int n;
     int k;
     int hash_bits;
+    int probe;  // HS_PROBE_PAGE_TABLE or HS_PROBE_SLOT_SCAN
 };
 
 struct FetchBatch {

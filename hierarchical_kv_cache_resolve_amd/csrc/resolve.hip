@@ -106,6 +106,19 @@ __device__ inline bool bucket_insert(const PlanLds& l, unsigned nbm, int bucket_
     }
 }
 
+__device__ inline int bucket_find(const PlanLds& l, unsigned nbm, int bucket_bits, int p) {
+    unsigned b = hash_bucket(p, bucket_bits);
+    for (;;) {
+        const int4 kk = *reinterpret_cast<const int4*>(l.bkey + 4 * b);
+        if (kk.x == p) return l.bval[4 * b];
+        if (kk.y == p) return l.bval[4 * b + 1];
+        if (kk.z == p) return l.bval[4 * b + 2];
+        if (kk.w == p) return l.bval[4 * b + 3];
+        if (kk.w == kEmpty) return -1;  // entries fill in order: a bucket with room ends the chain
+        b = (b + 1) & nbm;
+    }
+}
+
 __device__ inline int wave_incl_scan(int x) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -335,7 +348,7 @@ __device__ inline void radix_select(const PlanLds& l, const uint32_t (&tsv)[PER]
 //   5. the i-th miss takes the i-th victim in slot order; slot map, stamps
 //      (2t+1 for misses, 2t+2 for hits), page table and plan are written and
 //      every selection's slot is published.
-template <int PER, bool VEC>
+template <int PER, bool VEC, bool SCAN>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBatch lb) {
     extern __shared__ int lds_raw[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -367,7 +380,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBa
     int spos[PER];
     uint32_t tsv[PER];
     load_run<PER, VEC, int>(spos_g, s0, B, spos, kEmpty);
-    load_run<PER, VEC, uint32_t>(ts_g, s0, B, tsv, 0xFFFFFFFFu);
+    if constexpr (!SCAN) load_run<PER, VEC, uint32_t>(ts_g, s0, B, tsv, 0xFFFFFFFFu);
     int bad = 0, bad_at = 0;
     int ptv[kMaxSelPerLane];
 #pragma unroll
@@ -379,20 +392,25 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBa
             if (p < 0 || static_cast<int64_t>(p) >= s.L_ctx) {
                 bad |= 1;
                 bad_at = j + 1;
-            } else {
+            } else if constexpr (!SCAN) {
                 ptv[q] = pt[p];
             }
         }
     }
 
     for (int i = tid; i < H; i += kPlanThreads) l.bkey[i] = kEmpty;
-    for (int i = tid; i < hitmap_words(B); i += kPlanThreads) l.hitmap[i] = 0u;
+    if constexpr (SCAN) {
+        for (int j = tid; j < k; j += kPlanThreads) l.sidx[j] = -1;
+    } else {
+        for (int i = tid; i < hitmap_words(B); i += kPlanThreads) l.hitmap[i] = 0u;
+    }
     l.hist[tid] = 0;
     if (tid < kMisc) l.misc[tid] = 0;
     __syncthreads();
     HS_PHASE(1);
 
-    // 2. hits into the slot bitmap, misses into the hash
+    // 2. page-table probe: hits into the slot bitmap, misses into the hash.
+    //    slot-scan probe: every selected position into the hash.
 #pragma unroll
     for (int q = 0; q < kMaxSelPerLane; ++q) {
         const int j = tid + q * kPlanThreads;
@@ -400,7 +418,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBa
             const int p = selv[q];
             const int slot = ptv[q];
             l.sel[j] = p;
-            if (slot >= 0) {
+            if (SCAN) {
+                if (!bucket_insert(l, nbm, bucket_bits, p, j)) {
+                    bad |= 2;
+                    bad_at = j + 1;
+                }
+            } else if (slot >= 0) {
                 l.sidx[j] = slot;
                 if (slot >= B) {
                     bad |= 1;  // a page-table entry outside the cache: treat like a bad position
@@ -430,9 +453,25 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBa
         reject(s, out, k, rl, layer, r, (flags & 1) ? HS_DEV_RANGE : HS_DEV_DUP, l.misc[M_BADAT] - 1);
         return;
     }
-    // this lane's slots that hold a selected position (PER divides 32)
-    const unsigned hitbits =
-        s0 < B ? (l.hitmap[s0 >> 5] >> (s0 & 31)) & ((PER == 32) ? 0xFFFFFFFFu : ((1u << PER) - 1u)) : 0u;
+    // this lane's slots that hold a selected position
+    unsigned hitbits = 0;
+    if constexpr (SCAN) {
+        // the pages' probe: every cached position looked up in the hash
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            if (s0 + q < B && spos[q] >= 0) {
+                const int j = bucket_find(l, nbm, bucket_bits, spos[q]);
+                if (j >= 0) {
+                    l.sidx[j] = s0 + q;
+                    hitbits |= 1u << q;
+                }
+            }
+        }
+        __syncthreads();
+    } else {
+        // PER divides 32, so the run's bits lie in one word
+        hitbits = s0 < B ? (l.hitmap[s0 >> 5] >> (s0 & 31)) & ((PER == 32) ? 0xFFFFFFFFu : ((1u << PER) - 1u)) : 0u;
+    }
     HS_PHASE(3);
 
     // 3. miss list in ascending j: each lane owns the contiguous run
@@ -471,12 +510,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBa
     if (m == 0) {
         // Every selection hit: only the hit stamps change.
         if (hitbits) {
+            if constexpr (SCAN) {
 #pragma unroll
-            for (int q = 0; q < PER; ++q)
-                if ((hitbits >> q) & 1u) tsv[q] = ts_hit;
-            store_run<PER, VEC, uint32_t>(ts_g, s0, B, tsv);
+                for (int q = 0; q < PER; ++q)
+                    if ((hitbits >> q) & 1u) ts_g[s0 + q] = ts_hit;
+            } else {
+#pragma unroll
+                for (int q = 0; q < PER; ++q)
+                    if ((hitbits >> q) & 1u) tsv[q] = ts_hit;
+                store_run<PER, VEC, uint32_t>(ts_g, s0, B, tsv);
+            }
         }
     } else {
+        if constexpr (SCAN) load_run<PER, VEC, uint32_t>(ts_g, s0, B, tsv, 0xFFFFFFFFu);
         __syncthreads();  // miss list complete
         HS_PHASE(5);
         const int ncand = B - h;
@@ -745,20 +791,27 @@ size_t plan_lds_bytes(int k, int hash_bits, int B) {
                           kHistBins + kMisc);
 }
 
-template <int PER, bool VEC>
+template <int PER, bool VEC, bool SCAN>
 static hipError_t launch_plan_t(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&plan_kernel<PER, VEC>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&plan_kernel<PER, VEC, SCAN>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((plan_kernel<PER, VEC>), dim3(s.R, lb.n), dim3(kPlanThreads), lds, st, s, lb);
+    hipLaunchKernelGGL((plan_kernel<PER, VEC, SCAN>), dim3(s.R, lb.n), dim3(kPlanThreads), lds, st, s, lb);
     return hipGetLastError();
+}
+
+template <int PER, bool SCAN>
+static hipError_t launch_plan_s(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
+    return (s.B & 3) == 0 ? launch_plan_t<PER, true, SCAN>(s, lb, lds, st)
+                          : launch_plan_t<PER, false, SCAN>(s, lb, lds, st);
 }
 
 template <int PER>
 static hipError_t launch_plan_p(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
-    return (s.B & 3) == 0 ? launch_plan_t<PER, true>(s, lb, lds, st) : launch_plan_t<PER, false>(s, lb, lds, st);
+    return lb.probe == HS_PROBE_SLOT_SCAN ? launch_plan_s<PER, true>(s, lb, lds, st)
+                                          : launch_plan_s<PER, false>(s, lb, lds, st);
 }
 
 hipError_t launch_plan(const StateBase& s, const LayerBatch& lb, hipStream_t st) {

@@ -98,6 +98,17 @@ def test_ragged_shapes(hs, w):
     run_parity(hs, w)
 
 
+SCAN_SUBSET = [w for w in RAGGED if w.name in ("ragged_b_not_mult4", "per1_small", "per4_mla", "per16_maxb",
+                                              "b_equals_k", "uniform_small_ctx", "k1_b3", "hit_only")]
+
+
+@pytest.mark.parametrize("w", SCAN_SUBSET, ids=[w.name for w in SCAN_SUBSET])
+def test_slot_scan_probe(hs, w):
+    """The pages' probe (hash over the selection, every cached slot looked up)
+    gives the same results as the page-table probe."""
+    run_parity(hs, w, options={hs.HS_OPT_PROBE: hs.HS_PROBE_SLOT_SCAN})
+
+
 @pytest.mark.parametrize("unroll,blocks,nt", [(1, 7, 0), (2, 64, 1), (8, 4096, 0)])
 def test_fetch_launch_shapes(hs, unroll, blocks, nt):
     w = wl("fetch_shape", B=1000, k=600, W_KV=200, steps=6)
@@ -250,19 +261,26 @@ def test_victims_older_than_histogram_range(hs):
     pool = make_pool(hs, w)
     pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
     res = make_resolver(hs, w, pool)
+    scan = make_resolver(hs, w, pool)
+    scan.set_option(hs.HS_OPT_PROBE, hs.HS_PROBE_SLOT_SCAN)
     o = Oracle(R, 1, B, L_ctx, w.row_bytes)
     dev = torch.device("cuda:0")
     out = torch.empty((R, k), dtype=torch.int32, device=dev)
+    out2 = torch.empty_like(out)
     for t, S in enumerate(steps):
-        res.resolve(0, torch.from_numpy(S).to(dev), out)
+        Sd = torch.from_numpy(S).to(dev)
+        res.resolve(0, Sd, out)
+        scan.resolve(0, Sd, out2)
         ref = o.resolve(0, S, pool_np, w.region_rows())
         if t >= 690 or t < 6:
             got = out.cpu().numpy()
             assert np.array_equal(got, ref["slot_idx"]), f"step {t}"
+            assert np.array_equal(out2.cpu().numpy(), ref["slot_idx"]), f"slot-scan step {t}"
             st = res.state(0)
             assert np.array_equal(st["slot_pos"], o.slot_pos[0]) and np.array_equal(st["ts"], o.ts[0]), f"step {t}"
             m = int(ref["miss_count"][0])
             assert np.array_equal(st["plan"][0, :m], ref["plan"][0, :m]), f"plan step {t}"
-    assert res.error()[0] == 0
+    assert res.error()[0] == 0 and scan.error()[0] == 0
     res.close()
+    scan.close()
     pool.free()
