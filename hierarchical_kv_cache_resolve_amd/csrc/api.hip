@@ -150,11 +150,12 @@ int timed(hisparse_ctx* h, int kind, hipStream_t st, F fn) {
         ++h->dropped;
         return fn() == hipSuccess ? HS_OK : HS_E_HIP;
     }
-    auto& t = h->ring[h->ring_used++];
+    auto& t = h->ring[h->ring_used];
     t.kind = kind;
     HS_TRY(hipEventRecord(t.a, st));
-    if (fn() != hipSuccess) return HS_E_HIP;
+    if (fn() != hipSuccess) return HS_E_HIP;  // the slot stays free: its stop event was never recorded
     HS_TRY(hipEventRecord(t.b, st));
+    ++h->ring_used;
     return HS_OK;
 }
 
