@@ -140,3 +140,9 @@ def test_full_gqa_record(hs):
 @pytest.mark.timeout(900)
 def test_full_shared_prefetch(hs):
     full_parity(hs, tg.PREFETCH, prefetch=True)
+
+
+@pytest.mark.timeout(900)
+def test_full_page_records(hs):
+    """Block-granular records: 18 KB pages of 16 tokens selected by page index."""
+    full_parity(hs, tg.PAGES)

@@ -140,7 +140,14 @@ GQA = Workload("gqa_record", 64, 16, 131072, 2048, 2, 2048, 4096, 128, LOCALITY,
 PREFETCH = Workload("shared_prefetch", 8, 8, 524288, 576, 2, 2048, 4096, 64, LOCALITY, 0.87, group=4,
                     seed_index=5)
 
-WORKLOADS = {w.name: w for w in (TINY, MLA, NOLOCALITY, GQA, PREFETCH)}
+# Block-granular records (a selector that picks pages of 16 tokens, Quest-style):
+# a record is 16 tokens x 576 bf16 elements = 18 KB, positions are page
+# indices, and k = 128 pages covers the same 2048 tokens as the token-level
+# workloads.
+PAGES = Workload("page_records", 16, 8, 8192, 16 * 576, 2, 128, 256, 128, LOCALITY, 0.87, window=4,
+                 seed_index=6)
+
+WORKLOADS = {w.name: w for w in (TINY, MLA, NOLOCALITY, GQA, PREFETCH, PAGES)}
 
 
 def hit_only(w: Workload) -> Workload:
