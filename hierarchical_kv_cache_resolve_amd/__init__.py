@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libhisparse.so")
 HS_OK = 0
 HS_E_INVAL, HS_E_HANDLE, HS_E_LAYER, HS_E_K, HS_E_ALIGN = -1, -2, -3, -4, -5
 HS_E_POOL, HS_E_NOMEM, HS_E_HIP, HS_E_DEVICE, HS_E_ORDER = -6, -7, -8, -9, -10
-HS_DEV_RANGE, HS_DEV_DUP, HS_DEV_NOT_RESIDENT, HS_DEV_DIVERGED = 1, 2, 3, 4
+HS_DEV_RANGE, HS_DEV_DUP, HS_DEV_NOT_RESIDENT, HS_DEV_DIVERGED, HS_DEV_FULL = 1, 2, 3, 4, 5
 HS_MAX_B, HS_MAX_K, HS_MAX_REQ = 16384, 4096, 1024
 BF16, FP16, FP8, FP32 = 0, 1, 2, 3
 ELEM_BYTES = {BF16: 2, FP16: 2, FP8: 1, FP32: 4}
@@ -71,6 +71,9 @@ _sig("hisparse_resolve_layers", _i32, _vp, _i32, ctypes.POINTER(_i32), ctypes.PO
      ctypes.POINTER(_vp), _vp)
 _sig("hisparse_prefetch", _i32, _vp, _i32, ctypes.POINTER(_i32), _i32, _vp)
 _sig("hisparse_destroy", _i32, _vp)
+_sig("hisparse_append", _i32, _vp, _i32, _vp, _vp)
+_sig("hisparse_set_lengths", _i32, _vp, _vp)
+_sig("hisparse_get_lengths", _i32, _vp, _vp)
 _sig("hisparse_kv_bytes", _sz, _i32, _i32, _i32, _i32, _i32)
 _sig("hisparse_hbm_bytes", _sz, _vp)
 _sig("hisparse_meta_bytes", _sz, _vp)
@@ -150,6 +153,21 @@ def hisparse_prefetch(h, anchor, shared, side_stream) -> int:
 
 def hisparse_destroy(h) -> int:
     return _lib.hisparse_destroy(h)
+
+
+def hisparse_append(h, layer, d_rows, stream) -> int:
+    return _lib.hisparse_append(h, layer, d_rows, stream)
+
+
+def hisparse_set_lengths(h, lengths) -> int:
+    a = np.ascontiguousarray(lengths, dtype=np.int64)
+    return _check("hisparse_set_lengths", _lib.hisparse_set_lengths(h, a.ctypes.data))
+
+
+def hisparse_get_lengths(h, n) -> np.ndarray:
+    a = np.empty(n, dtype=np.int64)
+    _check("hisparse_get_lengths", _lib.hisparse_get_lengths(h, a.ctypes.data))
+    return a
 
 
 def hisparse_kv_bytes(num_req, num_layers, B, W_KV, dtype) -> int:
@@ -302,6 +320,17 @@ class Resolver:
 
     def set_option(self, key, value):
         hisparse_set_option(self.h, key, value)
+
+    def append(self, layer, rows, stream=None):
+        """rows: device tensor [num_req][row_bytes] (any dtype of that byte size)."""
+        _check("hisparse_append", hisparse_append(self.h, layer, _ptr(rows), _stream(stream)))
+
+    def set_lengths(self, lengths):
+        """lengths [num_req][num_layers] (or flat, index r*num_layers + l)."""
+        hisparse_set_lengths(self.h, np.asarray(lengths).reshape(-1))
+
+    def lengths(self):
+        return hisparse_get_lengths(self.h, self.num_req * self.num_layers).reshape(self.num_req, self.num_layers)
 
     def timing(self, clear=False):
         return hisparse_timing(self.h, clear)

@@ -76,7 +76,7 @@ int hash_bits_for(int k) {
 void free_all(hisparse_ctx* h) {
     hs::StateBase& s = h->s;
     void* ptrs[] = {s.cache, s.slot_pos, s.ts, s.page_table, s.clock, s.plan, s.miss_count,
-                    s.hit_mask, s.status, s.err, s.stats, s.phase, h->d_region_row};
+                    s.hit_mask, s.status, s.err, s.stats, s.phase, s.length, h->d_region_row};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     for (hipEvent_t e : h->ev_plan)
@@ -236,6 +236,7 @@ int hisparse_create(int num_req, int num_layers, int B, int W_KV, int dtype, con
     HS_ALLOC(status, int32_t, static_cast<size_t>(nrl))
     HS_ALLOC(err, int32_t, 4)
     HS_ALLOC(stats, unsigned long long, static_cast<size_t>(num_layers) * 4)
+    HS_ALLOC(length, int32_t, static_cast<size_t>(nrl))
 #undef HS_ALLOC
     if ((rc = alloc_dev(&p, sizeof(int64_t) * static_cast<size_t>(nrl))) != HS_OK) {
         free_all(h);
@@ -244,7 +245,7 @@ int hisparse_create(int num_req, int num_layers, int B, int W_KV, int dtype, con
     }
     h->d_region_row = static_cast<int64_t*>(p);
     s.region_row = h->d_region_row;
-    s.pool = static_cast<const uint8_t*>(dpool);
+    s.pool = static_cast<uint8_t*>(dpool);
     s.L_ctx = pool->L_ctx;
     s.row_bytes = row_bytes;
     s.R = num_req;
@@ -267,8 +268,10 @@ int hisparse_create(int num_req, int num_layers, int B, int W_KV, int dtype, con
     h->last_was_plan.assign(num_layers, 0);
     h->steps.assign(num_layers, 0);
     h->last_k.assign(num_layers, 0);
+    const std::vector<int32_t> full(static_cast<size_t>(nrl), static_cast<int32_t>(pool->L_ctx));
     if (hipMemcpy(h->d_region_row, region.data(), sizeof(int64_t) * region.size(), hipMemcpyHostToDevice) !=
-        hipSuccess) {
+            hipSuccess ||
+        hipMemcpy(s.length, full.data(), sizeof(int32_t) * full.size(), hipMemcpyHostToDevice) != hipSuccess) {
         free_all(h);
         delete h;
         return HS_E_HIP;
@@ -417,6 +420,46 @@ int hisparse_prefetch(hisparse_t h, int anchor, const int* shared, int n, void* 
     h->join_in_capture[anchor] = capturing(side);
     h->join_outstanding[anchor] = 1;
     for (int i = 0; i < n; ++i) h->pending_anchor[shared[i]] = anchor;
+    return HS_OK;
+}
+
+int hisparse_append(hisparse_t h, int layer, const void* d_rows, void* stream) {
+    if (!valid(h)) return HS_E_HANDLE;
+    if (layer < 0 || layer >= h->NL) return HS_E_LAYER;
+    if (!d_rows) return HS_E_INVAL;
+    return hs::launch_append(h->s, layer, static_cast<const uint8_t*>(d_rows), static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? HS_OK
+               : HS_E_HIP;
+}
+
+int hisparse_set_lengths(hisparse_t h, const int64_t* lengths) {
+    if (!valid(h)) return HS_E_HANDLE;
+    if (!lengths) return HS_E_INVAL;
+    const size_t nrl = static_cast<size_t>(h->R) * h->NL;
+    std::vector<int32_t> dev(nrl);
+    for (int r = 0; r < h->R; ++r) {
+        for (int l = 0; l < h->NL; ++l) {
+            const int64_t v = lengths[static_cast<size_t>(r) * h->NL + l];
+            if (v < 0 || v > h->L_ctx) return HS_E_INVAL;
+            dev[static_cast<size_t>(l) * h->R + r] = static_cast<int32_t>(v);
+        }
+    }
+    HS_TRY(hipDeviceSynchronize());
+    HS_TRY(hipMemcpy(h->s.length, dev.data(), sizeof(int32_t) * nrl, hipMemcpyHostToDevice));
+    return HS_OK;
+}
+
+int hisparse_get_lengths(hisparse_t h, int64_t* lengths) {
+    if (!valid(h)) return HS_E_HANDLE;
+    if (!lengths) return HS_E_INVAL;
+    const size_t nrl = static_cast<size_t>(h->R) * h->NL;
+    std::vector<int32_t> dev(nrl);
+    HS_TRY(hipDeviceSynchronize());
+    HS_TRY(hipMemcpy(dev.data(), h->s.length, sizeof(int32_t) * nrl, hipMemcpyDeviceToHost));
+    for (int r = 0; r < h->R; ++r)
+        for (int l = 0; l < h->NL; ++l)
+            lengths[static_cast<size_t>(r) * h->NL + l] = dev[static_cast<size_t>(l) * h->R + r];
     return HS_OK;
 }
 

@@ -115,6 +115,27 @@ __global__ __launch_bounds__(kFetchThreads) void fetch_kernel(StateBase s, Fetch
     }
 }
 
+// Decode-time append: the record of each request's new token goes to the
+// next position of its history in the host pool, written by GPU lanes with
+// 16-byte stores to host-mapped memory; the history grows by one.  A full
+// history (length == L_ctx) is left as it is and reported.
+__global__ __launch_bounds__(kFetchThreads) void append_kernel(StateBase s, int layer, const uint8_t* rows) {
+    const int r = blockIdx.x;
+    const int64_t rl = static_cast<int64_t>(layer) * s.R + r;
+    const int pos = s.length[rl];
+    if (pos >= s.L_ctx) {
+        if (threadIdx.x == 0) record_error(s.err, HS_DEV_FULL, layer, r, pos);
+        return;
+    }
+    const int row16 = static_cast<int>(s.row_bytes >> 4);
+    const u32x4* src = reinterpret_cast<const u32x4*>(rows + static_cast<int64_t>(r) * s.row_bytes);
+    u32x4* dst = reinterpret_cast<u32x4*>(
+        s.pool + (s.region_row[static_cast<int64_t>(r) * s.NL + layer] + pos) * s.row_bytes);
+    for (int c = threadIdx.x; c < row16; c += kFetchThreads) dst[c] = src[c];
+    __syncthreads();
+    if (threadIdx.x == 0) s.length[rl] = pos + 1;
+}
+
 // Link probe: stream `n16` 16-byte pieces from host memory into HBM.
 template <int U>
 __global__ __launch_bounds__(kFetchThreads) void link_read_kernel(const u32x4* src, u32x4* dst, int64_t n16) {
@@ -215,6 +236,11 @@ hipError_t launch_gather_checksum(const StateBase& s, int layer, const int32_t* 
                        st, out, s.R);
     const dim3 grid(s.R, (k + kGatherRowsPerBlock - 1) / kGatherRowsPerBlock);
     hipLaunchKernelGGL(gather_checksum_kernel, grid, dim3(kFetchThreads), 0, st, s, layer, slot_idx, k, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_append(const StateBase& s, int layer, const uint8_t* rows, hipStream_t st) {
+    hipLaunchKernelGGL(append_kernel, dim3(s.R), dim3(kFetchThreads), 0, st, s, layer, rows);
     return hipGetLastError();
 }
 

@@ -14,6 +14,7 @@
 //   miss_count int32  [layer][req]
 //   hit_mask   uint8  [layer][req][B]
 //   status     int32  [layer][req]       0, or the device error code of the last step
+//   length     int32  [layer][req]       positions of the history written so far (<= L_ctx)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -43,7 +44,8 @@ struct StateBase {
     int32_t* err;                   // sticky {code, layer, req, detail}
     unsigned long long* stats;      // [layer][4]: hits, misses, miss bytes, resolves
     unsigned long long* phase;      // [layer][req][kPhaseSlots] wall-clock stamps, or null (off)
-    const uint8_t* pool;            // device-visible pointer to the host pool
+    uint8_t* pool;                  // device-visible pointer to the host pool
+    int32_t* length;                // [layer][req] positions written so far in each history
     const int64_t* region_row;      // [req * num_layers + layer]
     int64_t L_ctx;
     int64_t row_bytes;
@@ -78,6 +80,7 @@ hipError_t launch_plan(const StateBase& s, const LayerBatch& lb, hipStream_t st)
 hipError_t launch_publish(const StateBase& s, const LayerBatch& lb, hipStream_t st);
 hipError_t launch_fetch(const StateBase& s, const FetchBatch& fb, int blocks, int unroll, bool nt, hipStream_t st);
 hipError_t launch_replay_meta(const StateBase& s, const ReplayBatch& rb, hipStream_t st);
+hipError_t launch_append(const StateBase& s, int layer, const uint8_t* rows, hipStream_t st);
 hipError_t launch_gather_checksum(const StateBase& s, int layer, const int32_t* slot_idx, int k, uint64_t* out,
                                   hipStream_t st);
 hipError_t launch_link_read(const void* src, void* dst, size_t bytes, hipStream_t st);

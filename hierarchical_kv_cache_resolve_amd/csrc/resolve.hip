@@ -370,6 +370,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBa
 
     // 1. global reads
     const uint32_t t = s.clock[rl];
+    const int64_t hist_len = s.length[rl];
     int selv[kMaxSelPerLane];
 #pragma unroll
     for (int q = 0; q < kMaxSelPerLane; ++q) {
@@ -389,7 +390,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBa
         ptv[q] = -1;
         if (j < k) {
             const int p = selv[q];
-            if (p < 0 || static_cast<int64_t>(p) >= s.L_ctx) {
+            if (p < 0 || static_cast<int64_t>(p) >= hist_len) {
                 bad |= 1;
                 bad_at = j + 1;
             } else if constexpr (!SCAN) {
@@ -678,9 +679,10 @@ __global__ __launch_bounds__(kPlanThreads) void publish_kernel(StateBase s, Laye
     if (tid == 0) pub_flags = 0;
     __syncthreads();
     int bad_range = 0, bad_dup = 0, bad_res = 0, bad_at = -1;
+    const int64_t hist_len = s.length[rl];
     for (int j = tid; j < k; j += kPlanThreads) {
         const int p = sel[j];
-        if (p < 0 || static_cast<int64_t>(p) >= s.L_ctx) {
+        if (p < 0 || static_cast<int64_t>(p) >= hist_len) {
             bad_range = 1;
             bad_at = j;
             continue;

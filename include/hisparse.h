@@ -26,7 +26,7 @@
  *   - Every entry point returns HS_OK (0) or a negative HS_E_* code.  Argument
  *     and setup errors are reported synchronously and leave all state as it
  *     was.  Errors found in the data on the device (a position outside
- *     [0, L_ctx), a repeated position, a shared layer whose selection is not
+ *     [0, length) of its history, a repeated position, a shared layer whose selection is not
  *     what its anchor installed) set a sticky device error word that
  *     hisparse_get_error() reads; the offending request publishes -1 in every
  *     slot_idx entry and its cache state is left unchanged.
@@ -78,6 +78,7 @@ typedef struct hisparse_ctx* hisparse_t;
 #define HS_DEV_DUP 2          /* a position repeated within one request's selection */
 #define HS_DEV_NOT_RESIDENT 3 /* shared layer: a selected position is not where the anchor's plan put it */
 #define HS_DEV_DIVERGED 4     /* shared layer: its cache state no longer mirrors its anchor's */
+#define HS_DEV_FULL 5         /* append: the history already holds L_ctx positions */
 
 /* ---- limits --------------------------------------------------------------- */
 #define HS_MAX_B 16384        /* slots per (request, layer) */
@@ -130,6 +131,24 @@ int hisparse_resolve_layers(hisparse_t h, int n, const int* layers, const int32_
  * only publishes; its selection must equal the anchor's.  Async on both
  * streams.  Errors: HS_E_HANDLE, HS_E_LAYER, HS_E_INVAL, HS_E_ORDER, HS_E_HIP. */
 int hisparse_prefetch(hisparse_t h, int anchor_layer, const int* shared_layers, int n_shared, void* side_stream);
+
+/* Decode-time append (async).  d_rows [num_req][W_KV*s] holds the record of
+ * each request's new token for `layer`; it is written to the next position
+ * of that (request, layer) history in the host pool, the authoritative copy
+ * (blog section 2, item 1: records go straight to pinned host memory), and
+ * the history grows by one.  The record enters the GPU cache only when a
+ * later selection names it.  A history already holding L_ctx positions is
+ * left unchanged and sets HS_DEV_FULL.  Errors: HS_E_HANDLE, HS_E_LAYER,
+ * HS_E_INVAL, HS_E_HIP. */
+int hisparse_append(hisparse_t h, int layer, const void* d_rows, void* stream);
+
+/* Set the number of positions already written in every history (e.g. the
+ * prefill lengths): lengths [num_req*num_layers], index r*num_layers + l,
+ * each in [0, L_ctx].  Selections must name positions below the length.
+ * At create every history has length L_ctx.  Synchronises the device. */
+int hisparse_set_lengths(hisparse_t h, const int64_t* lengths);
+/* Read the history lengths into lengths [num_req*num_layers] (synchronises). */
+int hisparse_get_lengths(hisparse_t h, int64_t* lengths);
 
 /* Free everything the handle owns (synchronises the device first). */
 int hisparse_destroy(hisparse_t h);

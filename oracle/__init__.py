@@ -19,7 +19,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-E_OK, E_RANGE, E_DUP, E_K = 0, 1, 2, 3
+E_OK, E_RANGE, E_DUP, E_K, E_FULL = 0, 1, 2, 3, 4
 
 _lib = None
 
@@ -42,6 +42,10 @@ def _load():
     for name in ("oracle_slot_pos", "oracle_ts", "oracle_page_table", "oracle_clock", "oracle_cache"):
         getattr(lib, name).restype = vp
         getattr(lib, name).argtypes = [vp]
+    lib.oracle_length.restype = vp
+    lib.oracle_length.argtypes = [vp]
+    lib.oracle_append.restype = ctypes.c_int
+    lib.oracle_append.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp]
     lib.oracle_resolve.restype = ctypes.c_int
     lib.oracle_resolve.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
     _lib = lib
@@ -71,6 +75,7 @@ class Oracle:
         self.ts = _view(self.lib.oracle_ts(self.h), np.uint32, (nl, nr, B))
         self.page_table = _view(self.lib.oracle_page_table(self.h), np.int32, (nl, nr, L_ctx))
         self.clock = _view(self.lib.oracle_clock(self.h), np.uint32, (nl, nr))
+        self.length = _view(self.lib.oracle_length(self.h), np.int64, (nl, nr))
         self.cache = (_view(self.lib.oracle_cache(self.h), np.uint8, (nl, nr, B, row_bytes))
                       if model_bytes else None)
 
@@ -87,6 +92,18 @@ class Oracle:
 
     def reset(self):
         self.lib.oracle_reset(self.h)
+
+    def append(self, layer, rows, pool, region_row=None):
+        """rows: uint8 [num_req][row_bytes]; pool: writable uint8 array holding the host pool."""
+        rows = np.ascontiguousarray(rows, dtype=np.uint8)
+        assert rows.shape == (self.num_req, self.row_bytes)
+        err = np.empty(self.num_req, np.int32)
+        rr = None
+        if region_row is not None:
+            region_row = np.ascontiguousarray(region_row, dtype=np.int64)
+            rr = region_row.ctypes.data
+        self.lib.oracle_append(self.h, layer, rows.ctypes.data, pool.ctypes.data, rr, err.ctypes.data)
+        return err
 
     def resolve(self, layer, sel, pool=None, region_row=None):
         """sel: int32 [num_req][k].  Returns dict of slot_idx, hit_mask, miss_count, plan, err."""

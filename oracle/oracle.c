@@ -39,6 +39,11 @@
  *     in ascending slot order.
  *   - a request whose selection holds an out-of-range or repeated position
  *     is rejected: its slots publish -1 and its state is left unchanged.
+ *   - decode-time append (the pages describe only prefill writes): a new
+ *     token's record goes to the next position of its history in the host
+ *     pool, the authoritative copy, like prefill records (blog section 2,
+ *     item 1); positions at or beyond a history's length are out of range;
+ *     the record enters the GPU cache only when a later selection names it.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -51,10 +56,11 @@ typedef struct {
     uint32_t* ts;         /* [l][r][B] */
     int32_t* page_table;  /* [l][r][L_ctx] */
     uint32_t* clock;      /* [l][r] */
+    int64_t* length;      /* [l][r] positions written in each history */
     uint8_t* cache;       /* [l][r][B][row_bytes], or NULL when bytes are not modelled */
 } oracle_t;
 
-enum { OR_OK = 0, OR_E_RANGE = 1, OR_E_DUP = 2, OR_E_K = 3 };
+enum { OR_OK = 0, OR_E_RANGE = 1, OR_E_DUP = 2, OR_E_K = 3, OR_E_FULL = 4 };
 
 void oracle_reset(oracle_t* o) {
     const int64_t nrl = (int64_t)o->num_req * o->num_layers;
@@ -66,7 +72,7 @@ void oracle_reset(oracle_t* o) {
 
 void oracle_destroy(oracle_t* o) {
     if (!o) return;
-    free(o->slot_pos); free(o->ts); free(o->page_table); free(o->clock); free(o->cache);
+    free(o->slot_pos); free(o->ts); free(o->page_table); free(o->clock); free(o->length); free(o->cache);
     free(o);
 }
 
@@ -80,11 +86,13 @@ oracle_t* oracle_create(int num_req, int num_layers, int B, int64_t L_ctx, int64
     o->ts = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)(nrl * B));
     o->page_table = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nrl * L_ctx));
     o->clock = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)nrl);
+    o->length = (int64_t*)malloc(sizeof(int64_t) * (size_t)nrl);
     o->cache = model_bytes ? (uint8_t*)malloc((size_t)(nrl * B * row_bytes)) : NULL;
-    if (!o->slot_pos || !o->ts || !o->page_table || !o->clock || (model_bytes && !o->cache)) {
+    if (!o->slot_pos || !o->ts || !o->page_table || !o->clock || !o->length || (model_bytes && !o->cache)) {
         oracle_destroy(o);
         return NULL;
     }
+    for (int64_t i = 0; i < nrl; ++i) o->length[i] = L_ctx;
     oracle_reset(o);
     return o;
 }
@@ -95,6 +103,31 @@ uint32_t* oracle_ts(oracle_t* o) { return o->ts; }
 int32_t* oracle_page_table(oracle_t* o) { return o->page_table; }
 uint32_t* oracle_clock(oracle_t* o) { return o->clock; }
 uint8_t* oracle_cache(oracle_t* o) { return o->cache; }
+int64_t* oracle_length(oracle_t* o) { return o->length; }
+
+/* Decode-time append: rows [num_req][row_bytes] go to position length of
+ * each (request, layer) history in `pool`; err[r] = OR_E_FULL for a history
+ * that already holds L_ctx positions (nothing written).  Returns the number
+ * of full histories. */
+int oracle_append(oracle_t* o, int layer, const uint8_t* rows, uint8_t* pool, const int64_t* region_row,
+                  int32_t* err) {
+    int n_full = 0;
+    for (int r = 0; r < o->num_req; ++r) {
+        const int64_t rl = (int64_t)layer * o->num_req + r;
+        const int64_t pos = o->length[rl];
+        if (pos >= o->L_ctx) {
+            err[r] = OR_E_FULL;
+            ++n_full;
+            continue;
+        }
+        const int64_t base = region_row ? region_row[(int64_t)r * o->num_layers + layer]
+                                        : ((int64_t)r * o->num_layers + layer) * o->L_ctx;
+        memcpy(pool + (base + pos) * o->row_bytes, rows + (int64_t)r * o->row_bytes, (size_t)o->row_bytes);
+        o->length[rl] = pos + 1;
+        err[r] = OR_OK;
+    }
+    return n_full;
+}
 
 /* The set of selected positions, kept as (position, j) pairs sorted by
  * position; membership is a binary search.  It plays the part of the hash
@@ -156,12 +189,12 @@ int oracle_resolve(oracle_t* o, int layer, const int32_t* sel, int k, const uint
         int32_t* pt = o->page_table + rl * o->L_ctx;
         const uint32_t t = o->clock[rl];
 
-        /* Validate: B >= k (blog section 2, item 2), every position in range,
-         * all positions distinct. */
+        /* Validate: B >= k (blog section 2, item 2), every position already
+         * written in this history, all positions distinct. */
         int code = OR_OK;
         if (k < 1 || k > B) code = OR_E_K;
         for (int j = 0; code == OR_OK && j < k; ++j)
-            if (S[j] < 0 || (int64_t)S[j] >= o->L_ctx) code = OR_E_RANGE;
+            if (S[j] < 0 || (int64_t)S[j] >= o->length[rl]) code = OR_E_RANGE;
         /* Stage 1: the set of selected positions. */
         for (int j = 0; code == OR_OK && j < k; ++j) { set[j].pos = S[j]; set[j].j = j; }
         if (code == OR_OK) {

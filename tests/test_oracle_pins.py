@@ -223,3 +223,30 @@ def test_rejected_inputs_leave_state():
     o2 = Oracle(1, 1, 2, 50, 4, model_bytes=False)
     r = o2.resolve(0, np.array([[1, 2, 3]], np.int32))
     assert r["err"][0] != 0
+
+
+def test_append_grows_history_and_is_fetched_on_first_selection():
+    """Decode-time append: the record goes to the history's next position in
+    the pool; positions at or beyond the length are out of range; the first
+    selection of the appended position is a miss that copies exactly the
+    appended bytes; a full history refuses the append."""
+    from oracle import E_FULL
+    R, L_ctx, B, row = 2, 12, 4, 16
+    pool = np.zeros((R * L_ctx, row), np.uint8)
+    o = Oracle(R, 1, B, L_ctx, row)
+    o.length[0, :] = 5
+    r0 = o.resolve(0, np.array([[0, 5], [1, 2]], np.int32), pool)   # position 5 not written yet
+    assert r0["err"].tolist() == [E_RANGE, 0]
+    rows = np.arange(R * row, dtype=np.uint8).reshape(R, row) + 1
+    assert o.append(0, rows, pool).tolist() == [0, 0]
+    assert o.length[0].tolist() == [6, 6]
+    assert np.array_equal(pool[5], rows[0]) and np.array_equal(pool[L_ctx + 5], rows[1])
+    r1 = o.resolve(0, np.array([[5, 0], [5, 1]], np.int32), pool)
+    assert r1["err"].tolist() == [0, 0]
+    assert r1["hit_mask"][0, 0] == 0 and r1["hit_mask"][1, 0] == 0 and r1["hit_mask"][1, 1] == 1
+    assert np.array_equal(o.cache[0, 0, r1["slot_idx"][0, 0]], rows[0])
+    assert np.array_equal(o.cache[0, 1, r1["slot_idx"][1, 0]], rows[1])
+    o.length[0, :] = L_ctx
+    before = pool.copy()
+    assert o.append(0, rows, pool).tolist() == [E_FULL, E_FULL]
+    assert np.array_equal(pool, before) and o.length[0].tolist() == [L_ctx, L_ctx]
