@@ -89,6 +89,7 @@ _sig("hisparse_phase_trace", _i32, _vp, _i32, _vp, ctypes.POINTER(ctypes.c_doubl
 _sig("hisparse_host_alloc", _i32, _sz, _i32, ctypes.POINTER(_vp))
 _sig("hisparse_host_free", _i32, _vp)
 _sig("hisparse_gather_checksum", _i32, _vp, _i32, _vp, _i32, _vp, _vp)
+_sig("hisparse_attend_mla", _i32, _vp, _i32, _vp, _i32, _vp, _i32, ctypes.c_float, _vp, _vp, _vp)
 for _n in ("hisparse_probe_link_sdma", "hisparse_probe_link_kernel", "hisparse_probe_hbm"):
     _sig(_n, _i32, _vp, _vp, _sz, _i32, _vp, ctypes.POINTER(ctypes.c_double))
 
@@ -244,6 +245,10 @@ def hisparse_gather_checksum(h, layer, d_slot_idx, k, d_out, stream) -> int:
     return _lib.hisparse_gather_checksum(h, layer, d_slot_idx, k, d_out, stream)
 
 
+def hisparse_attend_mla(h, layer, d_q, num_heads, d_slot_idx, k, scale, d_out, d_lse, stream) -> int:
+    return _lib.hisparse_attend_mla(h, layer, d_q, num_heads, d_slot_idx, k, scale, d_out, d_lse, stream)
+
+
 def _probe(name, src, dst, nbytes, iters, stream):
     g = ctypes.c_double()
     _check(name, getattr(_lib, name)(src, dst, nbytes, iters, stream, ctypes.byref(g)))
@@ -358,6 +363,12 @@ class Resolver:
     def gather_checksum(self, layer, slot_idx, out, stream=None):
         _check("hisparse_gather_checksum", hisparse_gather_checksum(
             self.h, layer, _ptr(slot_idx), int(slot_idx.shape[-1]), _ptr(out), _stream(stream)))
+
+    def attend_mla(self, layer, q, slot_idx, scale, out, lse=None, stream=None):
+        """q: bf16 device tensor [num_req][H][576]; out fp32 [num_req][H][512]; lse fp32 [num_req][H] or None."""
+        _check("hisparse_attend_mla", hisparse_attend_mla(
+            self.h, layer, _ptr(q), int(q.shape[1]), _ptr(slot_idx), int(slot_idx.shape[-1]), float(scale),
+            _ptr(out), _ptr(lse), _stream(stream)))
 
     def _d2h(self, dptr, dtype, shape):
         a = np.empty(shape, dtype=dtype)

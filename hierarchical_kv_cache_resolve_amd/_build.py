@@ -6,7 +6,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["csrc/api.hip", "csrc/resolve.hip", "csrc/fetch.hip"]
+SOURCES = ["csrc/api.hip", "csrc/resolve.hip", "csrc/fetch.hip", "csrc/attend.hip"]
 LIB = os.path.join(HERE, "libhisparse.so")
 
 HIPCC_FLAGS = [

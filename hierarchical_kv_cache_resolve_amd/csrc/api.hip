@@ -29,6 +29,8 @@ struct hisparse_ctx {
     bool nt = true;
     bool timing = false;
     int probe = HS_PROBE_PAGE_TABLE;
+    float* attn_ws = nullptr;       // consumer workspace (partials per chunk)
+    size_t attn_ws_floats = 0;
     // ordering of resolve / prefetch (host-side bookkeeping only)
     std::vector<hipEvent_t> ev_plan, ev_join;
     std::vector<int> pending_anchor;   // shared layer -> anchor whose replay it must publish, or -1
@@ -87,6 +89,7 @@ void free_all(hisparse_ctx* h) {
         (void)hipEventDestroy(t.a);
         (void)hipEventDestroy(t.b);
     }
+    if (h->attn_ws) (void)hipFree(h->attn_ws);
 }
 
 int alloc_dev(void** p, size_t bytes) {
@@ -662,6 +665,32 @@ int hisparse_gather_checksum(hisparse_t h, int layer, const int32_t* d_slot_idx,
     if (k < 1 || k > h->B) return HS_E_K;
     return hs::launch_gather_checksum(h->s, layer, d_slot_idx, k, d_out, static_cast<hipStream_t>(stream)) ==
                    hipSuccess
+               ? HS_OK
+               : HS_E_HIP;
+}
+
+int hisparse_attend_mla(hisparse_t h, int layer, const void* d_q, int num_heads, const int32_t* d_slot_idx, int k,
+                        float scale, float* d_out, float* d_lse, void* stream) {
+    if (!valid(h)) return HS_E_HANDLE;
+    if (layer < 0 || layer >= h->NL) return HS_E_LAYER;
+    if (!d_q || !d_slot_idx || !d_out || num_heads < 64 || num_heads % 64 != 0) return HS_E_INVAL;
+    if (h->dtype != HS_BF16 || h->W_KV != 576) return HS_E_INVAL;
+    if (k < 1 || k > h->B) return HS_E_K;
+    const int chunk = hs::attend_chunk(h->R, num_heads, k);
+    const int nchunk = (k + chunk - 1) / chunk;
+    const size_t need = hs::attend_workspace_floats(h->R, num_heads, nchunk);
+    if (need > h->attn_ws_floats) {
+        HS_TRY(hipDeviceSynchronize());
+        if (h->attn_ws) (void)hipFree(h->attn_ws);
+        h->attn_ws = nullptr;
+        h->attn_ws_floats = 0;
+        void* p = nullptr;
+        if (alloc_dev(&p, need * sizeof(float)) != HS_OK) return HS_E_NOMEM;
+        h->attn_ws = static_cast<float*>(p);
+        h->attn_ws_floats = need;
+    }
+    return hs::launch_attend_mla(h->s, layer, static_cast<const uint16_t*>(d_q), num_heads, d_slot_idx, k, scale,
+                                 d_out, d_lse, h->attn_ws, chunk, static_cast<hipStream_t>(stream)) == hipSuccess
                ? HS_OK
                : HS_E_HIP;
 }

@@ -241,6 +241,22 @@ int hisparse_host_free(void* p);
 int hisparse_gather_checksum(hisparse_t h, int layer, const int32_t* d_slot_idx, int k, uint64_t* d_out,
                              void* stream);
 
+/* The consumer: sparse MLA decode attention over the k records each request
+ * of `layer` published (async; blog section 5: attention reads exactly the
+ * selected records and its math is unchanged).  Needs bf16 records of
+ * W_KV = 576 elements (512 compressed-KV + 64 rotary-key elements).
+ *   d_q     bf16 [num_req][num_heads][576], each head's query in record space
+ *   d_out   fp32 [num_req][num_heads][512]:
+ *           out[h] = sum_j softmax_j(scale * q[h] . rec_j) * rec_j[0:512]
+ *   d_lse   fp32 [num_req][num_heads] log-sum-exp of the scaled scores, or NULL
+ * A record whose slot is -1 (a rejected request) is left out; a request
+ * with none gives zeros and lse = -inf.  num_heads must be a multiple of
+ * 64.  The first call for a larger shape allocates the handle's workspace
+ * (make that call before capturing a graph).
+ * Errors: HS_E_HANDLE, HS_E_LAYER, HS_E_INVAL, HS_E_K, HS_E_NOMEM, HS_E_HIP. */
+int hisparse_attend_mla(hisparse_t h, int layer, const void* d_q, int num_heads, const int32_t* d_slot_idx, int k,
+                        float scale, float* d_out, float* d_lse, void* stream);
+
 /* Peak probes (synchronous; time `iters` repetitions with HIP events):
  *   link_sdma  : hipMemcpyAsync host -> device (copy engines);
  *   link_kernel: a streaming kernel reading host memory with 16-byte loads;
