@@ -10,14 +10,30 @@
 // with whole records and the values are the records' first 512 elements.
 //
 // Work split (flash-decoding): workgroup = (request, 64 heads, a chunk of
-// records); 4 wave64s, one per 16 heads.  For each 64-record sub-chunk the
-// records named by slot_idx are gathered from the HBM cache into LDS twice --
-// row-major for S = Q K^T and transposed for O = P V -- so every MFMA operand
-// is one 16-byte LDS read.  Scores use v_mfma_f32_16x16x32_bf16 with the
-// query fragments held in registers; the softmax is online (running maximum
-// and sum per head, in log2 units) and the probabilities go through LDS as
-// bf16 to become the A operand of the value product.  A second kernel
-// combines the chunks of each (request, head).
+// records); 4 wave64s.  Records move HBM -> LDS with
+// global_load_lds (16 bytes a lane, no registers), 64 records per sub-chunk
+// into one of two LDS buffers, so the loads of sub-chunk i+1 are in flight
+// while sub-chunk i is computed.
+//
+// LDS buffer layout: [9 lines][64 records][8 slots of 16 B]; line L of a
+// record is its bytes 128L..128L+127 (one HBM cache line) and slot j holds
+// piece 8L + (j ^ swz(rec)).  One global_load_lds moves whole lines of 8
+// records (8 lanes a line, so every access is a full coalesced line), a lane
+// loads the same two records for the whole sub-chunk, and the XOR swizzle
+// keeps both operand reads below free of bank conflicts:
+//   scores  wave w: S^T = K Q^T for heads 16w..16w+15 (v_mfma_f32_16x16x32_bf16,
+//           K from LDS, Q fragments in registers); online softmax; the
+//           probabilities go to LDS as bf16 MFMA fragments;
+//   output  wave w: O^T = V^T P^T for output dimensions 128w..128w+127 of all
+//           64 heads; V^T comes from the gfx950 transposing LDS read
+//           (ds_read_b64_tr_b16, the costliest LDS access here, so each wave
+//           reads only its quarter of the values), P^T fragments from LDS.
+// The record order inside each 32-wide k-step is permuted identically on
+// both operands of O^T = V^T P^T, so the probability fragments are written
+// exactly as the score registers hold them.  A lane of the score phase owns
+// one head: running maximum and sum are per lane (log2 units) and reduce over
+// the 4 lanes holding the same head.  A second kernel combines the chunks of
+// each (request, head).
 #include "hs_internal.h"
 
 namespace hs {
@@ -25,199 +41,338 @@ namespace hs {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kAttnThreads = 256;
+constexpr int kAttnWaves = kAttnThreads / 64;
 constexpr int kHeadsPerWG = 64;
-constexpr int kSub = 64;                 // records per LDS sub-chunk
+constexpr int kSub = 64;                       // records per LDS sub-chunk
 constexpr int kDqk = 576, kDv = 512;
-constexpr int kKcStride = kDqk + 8;      // bf16 per LDS record row (+16 B against bank conflicts)
-constexpr int kVtStride = kSub + 8;      // bf16 per LDS transposed-value row
-constexpr int kPwStride = kSub + 8;      // bf16 per LDS probability row
-constexpr int kQSteps = kDqk / 32;       // 18 MFMA k-steps for the scores
-constexpr int kDTiles = kDv / 16;        // 32 output tiles of 16 dimensions
-constexpr size_t kAttnLds = sizeof(uint16_t) * (static_cast<size_t>(kSub) * kKcStride +
-                                                static_cast<size_t>(kDv) * kVtStride +
-                                                4 * 16 * static_cast<size_t>(kPwStride)) +
-                            sizeof(int) * kSub;
+constexpr int kRecBytes = kDqk * 2;            // 1152
+constexpr int kRecPieces = kRecBytes / 16;     // 72 pieces of 16 bytes
+constexpr int kLines = kRecBytes / 128;        // 9 lines of 128 bytes a record
+constexpr int kLineBlock = kSub * 128;         // 8 KB: one line of every record
+constexpr int kBufBytes = kLines * kLineBlock; // 73728 per buffer
+constexpr int kQSteps = kDqk / 32;             // 18 MFMA k-steps for the scores
+constexpr int kDTiles = kDv / 16;              // 32 output tiles of 16 dimensions
+constexpr int kPBytes = 4 * 2 * 1024;         // P fragments: [head tile][k-step][64 lanes][16 B]
+constexpr size_t kAttnLds = 2 * static_cast<size_t>(kBufBytes) + kPBytes + kHeadsPerWG * sizeof(float);
+constexpr int kDimsPerWave = kDv / kAttnWaves; // 128 output dimensions a wave
+constexpr int kWaveDTiles = kDimsPerWave / 16; // 8
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt == 0 only:
+// vmcnt 0 (bits 3:0, 15:14), expcnt 7 (bits 6:4), lgkmcnt 15 (bits 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
+constexpr float kRescaleSlack = 8.f;           // log2 units
+constexpr int kSDepth = 2;                     // score k-steps read ahead
+constexpr int kVDepth = 3;                     // value tiles read ahead
 
-__device__ inline uint16_t f32_to_bf16_bits(float f) {
+// a record of zeros: the source of every record left out (slot -1)
+__device__ __align__(16) uint4 g_zero_record[kRecPieces];
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     // round to nearest even (finite inputs: probabilities in [0, 1])
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+    ua += 0x7FFFu + ((ua >> 16) & 1u);
+    ub += 0x7FFFu + ((ub >> 16) & 1u);
+    return (ua >> 16) | (ub & 0xFFFF0000u);
 }
 
-__global__ __launch_bounds__(kAttnThreads) void mla_partial_kernel(StateBase s, int layer, const uint16_t* q,
-                                                                   int H, const int32_t* slot_idx, int k,
-                                                                   int chunk, float scale_log2, float* part_o,
-                                                                   float* part_ml) {
-    extern __shared__ __align__(16) uint16_t attn_lds[];
-    uint16_t* Kc = attn_lds;                                  // [kSub][kKcStride]
-    uint16_t* Vt = Kc + kSub * kKcStride;                     // [kDv][kVtStride]
-    uint16_t* Pw = Vt + kDv * kVtStride;                      // [4 waves][16][kPwStride]
-    int* rvalid = reinterpret_cast<int*>(Pw + 4 * 16 * kPwStride);  // [kSub]
+// slot of piece p%8 inside line p/8 of LDS record rec is (p%8) ^ swz(rec).
+// swz maps record bits {1,2,3} onto slot bits {1,2,0}: 16 consecutive
+// records read at one piece, and 4 + 4 records read at two adjacent pieces,
+// land on distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int rec) { return (rec & 6) | ((rec >> 3) & 1); }
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
-    const int nchunk = gridDim.x;
-    const int h0 = g * kHeadsPerWG + wave * 16;               // this wave's first head
-    const int row = lane & 15, grp = lane >> 4;               // MFMA fragment coordinates
+// This wave's share of one sub-chunk, HBM -> LDS: records 16w..16w+15, all 9
+// lines (18 instructions of 1 KB).  `src_a` / `src_b` point at this lane's
+// piece of line 0 of record 16w + lane/8 and 16w + 8 + lane/8.  The loads are
+// issued as inline assembly on purpose: the compiler would otherwise guard
+// the transposing LDS reads of the other buffer with a full vmcnt wait (it
+// cannot tell the buffers apart), serialising loads and compute.  Their
+// completion is waited for explicitly before the barrier that publishes a
+// buffer.
+__device__ __forceinline__ void issue_records(uint8_t* buf, const uint8_t* src_a, const uint8_t* src_b, int wave) {
+#pragma unroll
+    for (int L = 0; L < kLines; ++L) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint8_t* dst = buf + L * kLineBlock + (2 * wave + h) * 1024;
+            const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)dst));
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                         :
+                         : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"((h ? src_b : src_a) + 128 * L)
+                         : "memory", "m0");
+        }
+    }
+}
+
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla_partial_kernel(StateBase s, int layer, const uint16_t* q,
+                                                                   int H, const int32_t* slot_idx, int k,
+                                                                   int chunk, int nchunk, float scale_log2,
+                                                                   float* part_o, float* part_ml) {
+    extern __shared__ __align__(16) uint8_t attn_lds[];
+    uint8_t* pfrag = attn_lds + 2 * kBufBytes;                          // [4][2][64][16 B]
+    float* alpha_lds = reinterpret_cast<float*>(pfrag + kPBytes);       // [64] rescale of each head
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, grp = lane >> 4;                 // MFMA fragment coordinates
+    // workgroup -> (chunk, head group, request); when the grid divides into the
+    // 8 XCDs, consecutive tiles (the head groups of one chunk) share an XCD and
+    // so its L2
+    const int G = H / kHeadsPerWG;
+    const int nwg = gridDim.x;
+    int T = blockIdx.x;
+    if ((nwg & 7) == 0) T = (T & 7) * (nwg >> 3) + (T >> 3);
+    const int g = T % G, c = (T / G) % nchunk, r = T / (G * nchunk);
+    const int h0 = g * kHeadsPerWG + wave * 16;               // first head of this wave's scores
     const int j_begin = c * chunk, j_end = min(k, j_begin + chunk);
+    const int nsub = (j_end - j_begin + kSub - 1) / kSub;
     const int64_t rl = static_cast<int64_t>(layer) * s.R + r;
     const uint8_t* cache = s.cache + rl * s.B * s.row_bytes;
     const int32_t* sidx = slot_idx + static_cast<int64_t>(r) * k;
-    uint16_t* Pme = Pw + wave * 16 * kPwStride;
 
-    // query fragments of this wave's 16 heads, held for the whole chunk
+    // slot of record i of sub-chunk `sub`: the raw load (index clamped into the
+    // chunk, so it can be issued early and unconditionally), then the check
+    auto raw_slot = [&](int sub, int i) -> int { return sidx[min(j_begin + sub * kSub + i, j_end - 1)]; };
+    auto checked = [&](int sub, int i, int v) -> int {
+        return (j_begin + sub * kSub + i < j_end && v >= 0 && v < s.B) ? v : -1;
+    };
+    // the two records this lane loads, and its piece slot inside each line
+    const int rec_a = 16 * wave + (lane >> 3), rec_b = rec_a + 8;
+    const int pa = 16 * ((lane & 7) ^ swz(rec_a)), pb = 16 * ((lane & 7) ^ swz(rec_b));
+    auto record_src = [&](int slot, int piece_off) -> const uint8_t* {
+        return (slot >= 0 ? cache + static_cast<int64_t>(slot) * kRecBytes
+                          : reinterpret_cast<const uint8_t*>(g_zero_record)) + piece_off;
+    };
+    issue_records(attn_lds, record_src(checked(0, rec_a, raw_slot(0, rec_a)), pa),
+                  record_src(checked(0, rec_b, raw_slot(0, rec_b)), pb), wave);
+    // slots are read one sub-chunk ahead of their use: `mk_*` names record
+    // `lane` (validity mask), `la_*` / `lb_*` the records this lane loads
+    int mk_cur = raw_slot(0, lane);
+    int la_nxt = raw_slot(1, rec_a), lb_nxt = raw_slot(1, rec_b);
+    int mk_nxt = raw_slot(1, lane);
+
+    // query fragments of this wave's 16 heads (B operand of S^T = K Q^T)
     bf16x8 aq[kQSteps];
     {
-        const uint16_t* qrow = q + (static_cast<int64_t>(r) * H + h0 + row) * kDqk + 8 * grp;
+        const uint16_t* qrow = q + (static_cast<int64_t>(r) * H + h0 + n) * kDqk + 8 * grp;
 #pragma unroll
         for (int st = 0; st < kQSteps; ++st) aq[st] = *reinterpret_cast<const bf16x8*>(qrow + 32 * st);
     }
-
-    f32x4 acc_o[kDTiles];
+    // output accumulators: dimension tile dt (dims 128w + 16dt ..) x head tile ht;
+    // lane (grp, n) holds dims +4grp+i of head 16ht + n
+    f32x4 acc_o[kWaveDTiles][4];
 #pragma unroll
-    for (int t = 0; t < kDTiles; ++t) acc_o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[4], l_run[4];
+    for (int dt = 0; dt < kWaveDTiles; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        m_run[i] = -INFINITY;
-        l_run[i] = 0.f;
-    }
+        for (int ht = 0; ht < 4; ++ht) acc_o[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
 
-    for (int j0 = j_begin; j0 < j_end; j0 += kSub) {
-        // gather the sub-chunk's records: row-major into Kc, values transposed into Vt
-        if (tid < kSub) {
-            const int j = j0 + tid;
-            const int slot = j < j_end ? sidx[j] : -1;
-            rvalid[tid] = (slot >= 0 && slot < s.B) ? slot : -1;
-        }
-        __syncthreads();
-        constexpr int kPieces = kSub * (kDqk / 8);            // 16-byte pieces per sub-chunk
-        for (int p = tid; p < kPieces; p += kAttnThreads) {
-            const int rec = p / (kDqk / 8), off = p - rec * (kDqk / 8);
-            const int slot = rvalid[rec];
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (slot >= 0) v = *reinterpret_cast<const uint4*>(cache + static_cast<int64_t>(slot) * s.row_bytes + 16 * off);
-            *reinterpret_cast<uint4*>(Kc + rec * kKcStride + 8 * off) = v;
-            if (off < kDv / 8) {
-                const uint16_t e[8] = {static_cast<uint16_t>(v.x), static_cast<uint16_t>(v.x >> 16),
-                                       static_cast<uint16_t>(v.y), static_cast<uint16_t>(v.y >> 16),
-                                       static_cast<uint16_t>(v.z), static_cast<uint16_t>(v.z >> 16),
-                                       static_cast<uint16_t>(v.w), static_cast<uint16_t>(v.w >> 16)};
-#pragma unroll
-                for (int i = 0; i < 8; ++i) Vt[(8 * off + i) * kVtStride + rec] = e[i];
-            }
-        }
-        __syncthreads();
+    // per-lane LDS offsets of the two operand reads (the rest are immediates)
+    //   score read: record 16nt + n, piece 4st + grp = line st/2, slot
+    //   (4(st&1) + grp) ^ swz(n)
+    const int s_even = 128 * n + 16 * (grp ^ swz(n));
+    const int s_odd = 128 * n + 16 * ((4 + grp) ^ swz(n));
+    //   transposing read: lane (grp, e, qq) points at dims 4qq..4qq+3 of record
+    //   32ks + 16hi + 4grp + e, i.e. piece 2t + (qq >> 1) = line t/4, slot
+    //   (2(t&3) + (qq>>1)) ^ swz = 2(t&3) ^ gv, half qq & 1
+    const int e = n >> 2, qq = n & 3;
+    const int gv = (qq >> 1) ^ swz(4 * grp + e);
+    // (this wave's dimension tiles are t = 8w + dt, so t & 3 = dt & 3)
+    const int v_base = 128 * (4 * grp + e) + 8 * (qq & 1);
+    const int v_off[4] = {v_base + 16 * (0 ^ gv), v_base + 16 * (2 ^ gv), v_base + 16 * (4 ^ gv),
+                          v_base + 16 * (6 ^ gv)};
 
-        // S = Q K^T for 16 heads x 64 records (4 tiles of 16 records)
+    for (int sub = 0; sub < nsub; ++sub) {
+        uint8_t* buf = attn_lds + (sub & 1) * kBufBytes;
+        // vmcnt(0): this wave's record loads (and everything else) have landed;
+        // the builtin form lets the compiler know no load is outstanding
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();                          // sub-chunk `sub` is in LDS
+        const uint64_t valid = __ballot(checked(sub, lane, mk_cur) >= 0);
+        if (sub + 1 < nsub)
+            issue_records(attn_lds + ((sub + 1) & 1) * kBufBytes, record_src(checked(sub + 1, rec_a, la_nxt), pa),
+                          record_src(checked(sub + 1, rec_b, lb_nxt), pb), wave);
+        mk_cur = mk_nxt;
+        la_nxt = raw_slot(sub + 2, rec_a);
+        lb_nxt = raw_slot(sub + 2, rec_b);
+        mk_nxt = raw_slot(sub + 2, lane);
+
+        // S^T = K Q^T: tile nt covers records 16nt..16nt+15; this lane ends with
+        // head h0+n against records 16nt + 4grp + i
+        // Software-pipelined: the fragments of step st + kSDepth are read while
+        // step st multiplies; sched_barrier keeps the compiler from undoing it.
+        auto k_frag = [&](int st, int nt) -> bf16x8 {
+            return *reinterpret_cast<const bf16x8*>(buf + ((st & 1) ? s_odd : s_even) + (st >> 1) * kLineBlock +
+                                                    2048 * nt);
+        };
         f32x4 sacc[4];
+        bf16x8 kf[kSDepth + 1][4];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint16_t* brow = Kc + (16 * nt + row) * kKcStride + 8 * grp;
+        for (int nt = 0; nt < 4; ++nt) sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int st = 0; st < kQSteps; ++st) {
-                const bf16x8 b = *reinterpret_cast<const bf16x8*>(brow + 32 * st);
-                sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[st], b, sacc[nt], 0, 0, 0);
+        for (int d = 0; d < kSDepth; ++d)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) kf[d][nt] = k_frag(d, nt);
+#pragma unroll
+        for (int st = 0; st < kQSteps; ++st) {
+            if (st + kSDepth < kQSteps) {
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) kf[(st + kSDepth) % (kSDepth + 1)][nt] = k_frag(st + kSDepth, nt);
             }
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[st % (kSDepth + 1)][nt], aq[st], sacc[nt], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // online softmax; this lane holds heads 4*grp + i and record 16*nt + row
-        float mloc[4], alpha[4];
+        // online softmax for head h0+n over the sub-chunk's 64 records, with a
+        // lazily moved reference: probabilities are 2^(s - m_ref), and m_ref is
+        // raised (rescaling the accumulators) only when some lane of the wave
+        // sees a score above m_ref + kRescaleSlack.  Probabilities stay below
+        // 2^kRescaleSlack, so nothing overflows; the final normalisation by the
+        // running sum makes the result independent of m_ref.
+        float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float mx = -INFINITY;
+        for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const bool ok = rvalid[16 * nt + row] >= 0;
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = (valid >> (16 * nt + 4 * grp + i)) & 1ull;
                 const float v = ok ? sacc[nt][i] * scale_log2 : -INFINITY;
                 sacc[nt][i] = v;
                 mx = fmaxf(mx, v);
             }
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-            mloc[i] = mx;
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        float alpha = 1.f;
+        if (__builtin_amdgcn_read_exec() & __ballot(mx > m_run + kRescaleSlack)) {   // wave-uniform
+            const float m_new = fmaxf(m_run, mx);
+            alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+            l_run *= alpha;
+            m_run = m_new;
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float m_new = fmaxf(m_run[i], mloc[i]);
-            alpha[i] = (m_new == -INFINITY) ? 1.f : exp2f(m_run[i] - m_new);
-            float sum = 0.f;
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const float pr = (m_new == -INFINITY) ? 0.f : exp2f(sacc[nt][i] - m_new);
-                sacc[nt][i] = pr;
-                sum += pr;
-            }
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off, 64);
-            l_run[i] = l_run[i] * alpha[i] + sum;
-            m_run[i] = m_new;
-        }
-#pragma unroll
-        for (int t = 0; t < kDTiles; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc_o[t][i] *= alpha[i];
-        // probabilities to LDS as bf16, [head][record], for the A operand
+        float sum = 0.f;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Pme[(4 * grp + i) * kPwStride + 16 * nt + row] = f32_to_bf16_bits(sacc[nt][i]);
-        __syncthreads();
-
-        // O += P V: 16 heads x 512 dims, k = 64 records in two steps of 32
+            for (int i = 0; i < 4; ++i) {
+                const float pr = (m_run == -INFINITY) ? 0.f : exp2f(sacc[nt][i] - m_run);
+                sacc[nt][i] = pr;
+                sum += pr;
+            }
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        l_run += sum;
+        // publish: P fragments of this head tile (k-step ks takes records
+        // 32ks + 4grp + i and 32ks + 16 + 4grp + i, i < 4: the score registers
+        // of tiles 2ks and 2ks+1) and the rescale factor of each head
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Pme + row * kPwStride + 32 * ks + 8 * grp);
+            const uint32_t w4[4] = {pack_bf16x2(sacc[2 * ks][0], sacc[2 * ks][1]),
+                                    pack_bf16x2(sacc[2 * ks][2], sacc[2 * ks][3]),
+                                    pack_bf16x2(sacc[2 * ks + 1][0], sacc[2 * ks + 1][1]),
+                                    pack_bf16x2(sacc[2 * ks + 1][2], sacc[2 * ks + 1][3])};
+            *reinterpret_cast<uint4*>(pfrag + ((wave * 2 + ks) * 64 + lane) * 16) =
+                make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        }
+        if (grp == 0) alpha_lds[wave * 16 + n] = alpha;
+        __syncthreads();                          // P and the rescale factors are visible
+
+        // rescale this wave's accumulators where a score phase moved its reference
+        float a_ht[4];
 #pragma unroll
-            for (int t = 0; t < kDTiles; ++t) {
-                const bf16x8 b = *reinterpret_cast<const bf16x8*>(Vt + (16 * t + row) * kVtStride + 32 * ks + 8 * grp);
-                acc_o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc_o[t], 0, 0, 0);
+        for (int ht = 0; ht < 4; ++ht) a_ht[ht] = alpha_lds[ht * 16 + n];
+        if (sub > 0 && (__builtin_amdgcn_read_exec() &
+                        __ballot(a_ht[0] != 1.f || a_ht[1] != 1.f || a_ht[2] != 1.f || a_ht[3] != 1.f))) {
+#pragma unroll
+            for (int dt = 0; dt < kWaveDTiles; ++dt)
+#pragma unroll
+                for (int ht = 0; ht < 4; ++ht) acc_o[dt][ht] *= a_ht[ht];
+        }
+
+        // O^T += V^T P^T for dims 128w.. of all 64 heads
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 pf[4];
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht)
+                pf[ht] = *reinterpret_cast<const bf16x8*>(pfrag + ((ht * 2 + ks) * 64 + lane) * 16);
+            const uint8_t* vb = buf + 4096 * ks + (wave * kWaveDTiles / 4) * kLineBlock;
+            auto v_frag = [&](int dt) -> bf16x8 {
+                const uint8_t* va = vb + v_off[dt & 3] + (dt >> 2) * kLineBlock;
+                const s16x4 vv[2] = {__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)va),
+                                     __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(va + 2048))};
+                return *reinterpret_cast<const bf16x8*>(vv);
+            };
+            bf16x8 vf[kVDepth + 1];
+#pragma unroll
+            for (int d = 0; d < kVDepth; ++d) vf[d] = v_frag(d);
+#pragma unroll
+            for (int dt = 0; dt < kWaveDTiles; ++dt) {
+                if (dt + kVDepth < kWaveDTiles) vf[(dt + kVDepth) % (kVDepth + 1)] = v_frag(dt + kVDepth);
+#pragma unroll
+                for (int ht = 0; ht < 4; ++ht)
+                    acc_o[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt % (kVDepth + 1)], pf[ht],
+                                                                            acc_o[dt][ht], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        __syncthreads();  // Kc, Vt and Pw are refilled by the next sub-chunk
+        // no barrier here: the next sub-chunk's first barrier (before any wave
+        // issues loads into this buffer or rewrites P) orders it
     }
 
-    // partials: unnormalised O, running maximum and sum (log2 units)
-    const int64_t base = ((static_cast<int64_t>(r) * nchunk + c) * H);
+    // partials: unnormalised O, running maximum and sum (log2 units); lane
+    // (grp, n) holds dims 128w + 16dt + 4grp + i of head 16ht + n, and the
+    // score-phase statistics of head h0 + n
+    const int64_t hbase = (static_cast<int64_t>(r) * nchunk + c) * H + g * kHeadsPerWG;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int h = h0 + 4 * grp + i;
-        float* orow = part_o + (base + h) * kDv;
+    for (int ht = 0; ht < 4; ++ht) {
+        float* orow = part_o + (hbase + ht * 16 + n) * kDv + wave * kDimsPerWave + 4 * grp;
 #pragma unroll
-        for (int t = 0; t < kDTiles; ++t) orow[16 * t + row] = acc_o[t][i];
-        if (row == 0) {
-            part_ml[(base + h) * 2 + 0] = m_run[i];
-            part_ml[(base + h) * 2 + 1] = l_run[i];
-        }
+        for (int dt = 0; dt < kWaveDTiles; ++dt) *reinterpret_cast<f32x4*>(orow + 16 * dt) = acc_o[dt][ht];
+    }
+    if (grp == 0) {
+        part_ml[(hbase + wave * 16 + n) * 2 + 0] = m_run;
+        part_ml[(hbase + wave * 16 + n) * 2 + 1] = l_run;
     }
 }
 
 // Combine the chunks of each (request, head): out = sum_c w_c O_c / sum_c w_c l_c
-// with w_c = 2^(m_c - max_c m_c); lse in natural-log units.
-__global__ __launch_bounds__(kAttnThreads) void mla_combine_kernel(const float* part_o, const float* part_ml, int H,
-                                                                   int nchunk, float* out, float* lse) {
+// with w_c = 2^(m_c - max_c m_c); lse in natural-log units.  128 lanes, four
+// dimensions each; the partial loads of up to kCombineBatch chunks are all
+// issued before any is used.
+constexpr int kCombineThreads = kDv / 4;
+constexpr int kCombineBatch = 8;
+
+__global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const float* part_o, const float* part_ml,
+                                                                      int H, int nchunk, float* out, float* lse) {
     const int h = blockIdx.x, r = blockIdx.y;
+    const int64_t first = static_cast<int64_t>(r) * nchunk * H + h;   // chunk c at first + c * H
     float M = -INFINITY;
-    for (int c = 0; c < nchunk; ++c) M = fmaxf(M, part_ml[((static_cast<int64_t>(r) * nchunk + c) * H + h) * 2]);
+    for (int c = 0; c < nchunk; ++c) M = fmaxf(M, part_ml[(first + static_cast<int64_t>(c) * H) * 2]);
     float denom = 0.f;
-    for (int c = 0; c < nchunk; ++c) {
-        const float* ml = part_ml + ((static_cast<int64_t>(r) * nchunk + c) * H + h) * 2;
-        if (ml[0] != -INFINITY) denom += exp2f(ml[0] - M) * ml[1];
-    }
-    float* orow = out + (static_cast<int64_t>(r) * H + h) * kDv;
-    for (int d = threadIdx.x; d < kDv; d += kAttnThreads) {
-        float acc = 0.f;
-        for (int c = 0; c < nchunk; ++c) {
-            const int64_t idx = (static_cast<int64_t>(r) * nchunk + c) * H + h;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < nchunk; c0 += kCombineBatch) {
+        f32x4 o[kCombineBatch];
+        float wgt[kCombineBatch];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            const int c = min(c0 + u, nchunk - 1);
+            const int64_t idx = first + static_cast<int64_t>(c) * H;
+            o[u] = *reinterpret_cast<const f32x4*>(part_o + idx * kDv + 4 * threadIdx.x);
             const float m = part_ml[idx * 2];
-            if (m != -INFINITY) acc += exp2f(m - M) * part_o[idx * kDv + d];
+            wgt[u] = (c0 + u < nchunk && m != -INFINITY) ? exp2f(m - M) : 0.f;
+            denom += wgt[u] * part_ml[idx * 2 + 1];
         }
-        orow[d] = denom > 0.f ? acc / denom : 0.f;
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u)
+            if (wgt[u] != 0.f) acc += wgt[u] * o[u];
     }
+    const float inv = denom > 0.f ? 1.f / denom : 0.f;
+    *reinterpret_cast<f32x4*>(out + (static_cast<int64_t>(r) * H + h) * kDv + 4 * threadIdx.x) = acc * inv;
     if (threadIdx.x == 0 && lse)
         lse[static_cast<int64_t>(r) * H + h] = denom > 0.f ? (M + log2f(denom)) * 0.69314718055994530942f : -INFINITY;
 }
@@ -246,9 +401,10 @@ hipError_t launch_attend_mla(const StateBase& s, int layer, const uint16_t* q, i
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kAttnLds));
     if (e != hipSuccess) return e;
     const float scale_log2 = scale * 1.44269504088896340736f;
-    hipLaunchKernelGGL(mla_partial_kernel, dim3(nchunk, H / kHeadsPerWG, s.R), dim3(kAttnThreads), kAttnLds, st, s,
-                       layer, q, H, slot_idx, k, chunk, scale_log2, part_o, part_ml);
-    hipLaunchKernelGGL(mla_combine_kernel, dim3(H, s.R), dim3(kAttnThreads), 0, st, part_o, part_ml, H, nchunk, out,
+    const int nwg = nchunk * (H / kHeadsPerWG) * s.R;
+    hipLaunchKernelGGL(mla_partial_kernel, dim3(nwg), dim3(kAttnThreads), kAttnLds, st, s, layer, q, H, slot_idx, k,
+                       chunk, nchunk, scale_log2, part_o, part_ml);
+    hipLaunchKernelGGL(mla_combine_kernel, dim3(H, s.R), dim3(kCombineThreads), 0, st, part_o, part_ml, H, nchunk, out,
                        lse);
     return hipGetLastError();
 }
