@@ -27,6 +27,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PCIE5_X16_GBPS = 63.0  # 32 GT/s x 16 lanes, 128b/130b line code, per direction
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 
 
 def fetch_traffic():
@@ -71,8 +73,13 @@ def parse():
     ap.add_argument("--timing", type=int, default=1, help="replay the timed steps with HIP events on every launch")
     ap.add_argument("--graph", type=int, default=1, help="run the timed steps as one captured HIP graph")
     ap.add_argument("--prefetch", type=int, default=1, help="shared-selection workloads: replay anchor plans")
-    ap.add_argument("--consumer", type=int, default=-1,
-                    help="run the gather-checksum consumer after every layer (default: on for shared workloads)")
+    ap.add_argument("--consumer", default="auto", choices=["auto", "none", "checksum", "attention"],
+                    help="kernel run after every layer's RESOLVE inside the timed steps (auto: shared-selection "
+                         "workloads get MLA attention when the records are 576-element bf16 latents, else the "
+                         "gather checksum; other workloads none)")
+    ap.add_argument("--heads", type=int, default=128, help="query heads of the MLA attention consumer")
+    ap.add_argument("--no-attention-leg", action="store_true",
+                    help="skip the separate timing of the MLA attention consumer on the workload's shape")
     ap.add_argument("--hit-only-workload", default="gqa_record",
                     help="shapes of the hit-only leg (its pool aliases every history onto one region)")
     return ap.parse_args()
@@ -90,8 +97,11 @@ def main():
     import tracegen as tg
 
     w = tg.WORKLOADS[args.workload]
-    if args.consumer < 0:
-        args.consumer = 1 if w.group > 1 else 0
+    mla_records = w.W_KV == 576 and w.elem_bytes == 2
+    if args.consumer == "auto":
+        args.consumer = ("attention" if mla_records else "checksum") if w.group > 1 else "none"
+    if args.consumer == "attention" and not mla_records:
+        raise SystemExit("the attention consumer needs 576-element bf16 records")
     W, K = args.warmup, args.steps
     nthreads = max(1, min(16, os.cpu_count() or 1))
     dev = torch.device("cuda:0")
@@ -120,14 +130,24 @@ def main():
 
     use_prefetch = w.group > 1 and args.prefetch
     side = torch.cuda.Stream() if use_prefetch else None
-    cs = torch.empty((w.num_layers, w.num_req), dtype=torch.int64, device=dev) if args.consumer else None
+    cs = torch.empty((w.num_layers, w.num_req), dtype=torch.int64, device=dev) if args.consumer == "checksum" else None
+    attn = None
+    if args.consumer == "attention":
+        attn = attention_buffers(torch, w, args.heads, dev)
+        res.attend_mla(0, attn["q"], out[0], attn["scale"], attn["o"], attn["lse"])   # sizes the workspace
+        torch.cuda.synchronize()
+
+    def consume(l, sp):
+        if cs is not None:
+            res.gather_checksum(l, out[l], cs[l], sp)
+        elif attn is not None:
+            res.attend_mla(l, attn["q"], out[l], attn["scale"], attn["o"], attn["lse"], sp)
 
     def step(t, sp, capturing=False, prefetch=use_prefetch):
         if not prefetch:
             for l in range(w.num_layers):
                 res.resolve(l, sel[t, l], out[l], sp)
-                if cs is not None:
-                    res.gather_checksum(l, out[l], cs[l], sp)
+                consume(l, sp)
             return
         # shared-selection groups: anchor, replay of its plan on the side
         # stream, then the shared layers only publish
@@ -137,12 +157,10 @@ def main():
             if capturing:
                 side.wait_stream(torch.cuda.current_stream())
             res.prefetch(g0, shared, side)
-            if cs is not None:
-                res.gather_checksum(g0, out[g0], cs[g0], sp)
+            consume(g0, sp)
             for l in shared:
                 res.resolve(l, sel[t, l], out[l], sp)
-                if cs is not None:
-                    res.gather_checksum(l, out[l], cs[l], sp)
+                consume(l, sp)
 
     def timed_run(prefetch):
         """Run steps W..W+K-1 (as one captured graph unless --graph 0); returns seconds."""
@@ -208,7 +226,7 @@ def main():
             step(t, sptr, prefetch=False)
         off = timed_run(False)
         prefetch_cmp = {"ms_per_step_prefetch_on": elapsed * 1e3 / K, "ms_per_step_prefetch_off": off * 1e3 / K,
-                        "consumer_between_layers": bool(cs is not None),
+                        "consumer_between_layers": args.consumer,
                         "saving": 1.0 - elapsed / off}
         log(f"prefetch on {elapsed * 1e3 / K:.3f} ms/step, off {off * 1e3 / K:.3f} ms/step")
 
@@ -313,6 +331,9 @@ def main():
         }
         log(f"fetch avg {fetch_avg_ms * 1e3:.1f} us ({achieved:.1f} GB/s), plan avg {plan_avg_ms * 1e3:.1f} us")
 
+    if not args.no_attention_leg and mla_records:
+        result["attention"] = attention_leg(hs, torch, res, w, out, args.heads, dev, hbm_peak)
+
     res.close()
 
     if not args.no_hit_only:
@@ -323,6 +344,48 @@ def main():
 
     pool.free()
     print(json.dumps(result), flush=True)
+
+
+def attention_buffers(torch, w, heads, dev):
+    """Query, output and log-sum-exp buffers of the MLA decode consumer: seeded
+    N(0,1) queries in bf16, one per head, in the 576-element record space."""
+    g = torch.Generator(device="cpu").manual_seed(260807)
+    q = torch.randn((w.num_req, heads, 576), generator=g).to(torch.bfloat16).to(dev).view(torch.int16)
+    return {"q": q, "scale": 1.0 / 24.0,
+            "o": torch.empty((w.num_req, heads, 512), dtype=torch.float32, device=dev),
+            "lse": torch.empty((w.num_req, heads), dtype=torch.float32, device=dev)}
+
+
+def attention_leg(hs, torch, res, w, out, heads, dev, hbm_peak, iters=20):
+    """The consumer alone: sparse MLA decode attention over the slots the last
+    timed step published, every layer, timed with HIP events on the stream
+    the kernels run on.  Algorithmic work per (request, layer): k records of
+    1152 B read once, heads x k x (576 + 512) multiply-adds."""
+    a = attention_buffers(torch, w, heads, dev)
+    for l in range(w.num_layers):
+        res.attend_mla(l, a["q"], out[l], a["scale"], a["o"], a["lse"])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        for l in range(w.num_layers):
+            res.attend_mla(l, a["q"], out[l], a["scale"], a["o"], a["lse"])
+    e1.record()
+    torch.cuda.synchronize()
+    res.check_error()
+    us = e0.elapsed_time(e1) * 1e3 / (iters * w.num_layers)
+    flops = 2.0 * w.num_req * heads * w.k * (576 + 512)
+    rec_bytes = w.num_req * w.k * w.row_bytes
+    io_bytes = rec_bytes + w.num_req * heads * (576 * 2 + 512 * 4 + 4) + w.num_req * w.k * 4
+    tflops = flops / (us * 1e-6) / 1e12
+    gbps = io_bytes / (us * 1e-6) / 1e9
+    log(f"attention: {us:.1f} us per layer ({tflops:.0f} TFLOP/s, {gbps:.0f} GB/s of records+q+out)")
+    return {"kernels": "mla_partial_kernel + mla_combine_kernel", "heads": heads, "k": w.k,
+            "requests": w.num_req, "us_per_layer": us, "TFLOPs": tflops,
+            "mfma_frac": tflops / MFMA_BF16_TFLOPS, "algorithmic_GBps": gbps,
+            "hbm_frac_published": gbps / HBM_PEAK_GBPS,
+            "hbm_frac_measured_copy": gbps / hbm_peak if hbm_peak else None,
+            "algorithmic_bytes": io_bytes, "flops": flops}
 
 
 def hit_only_leg(hs, tg, torch, w, dev, sptr, hbm_peak, steps=64):

@@ -389,12 +389,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBa
         const int j = tid + q * kPlanThreads;
         ptv[q] = -1;
         if (j < k) {
+            // the page-table load depends on the static table bound only, so it
+            // does not wait for the history length
             const int p = selv[q];
-            if (p < 0 || static_cast<int64_t>(p) >= hist_len) {
+            const bool in_table = p >= 0 && static_cast<int64_t>(p) < s.L_ctx;
+            if (!in_table || static_cast<int64_t>(p) >= hist_len) {
                 bad |= 1;
                 bad_at = j + 1;
-            } else if constexpr (!SCAN) {
-                ptv[q] = pt[p];
+            }
+            if constexpr (!SCAN) {
+                if (in_table) ptv[q] = pt[p];
             }
         }
     }
@@ -682,12 +686,17 @@ __global__ __launch_bounds__(kPlanThreads) void publish_kernel(StateBase s, Laye
     const int64_t hist_len = s.length[rl];
     for (int j = tid; j < k; j += kPlanThreads) {
         const int p = sel[j];
-        if (p < 0 || static_cast<int64_t>(p) >= hist_len) {
+        if (p < 0 || static_cast<int64_t>(p) >= s.L_ctx) {
             bad_range = 1;
             bad_at = j;
             continue;
         }
-        const int slot = pt[p];
+        const int slot = pt[p];                    // issued before the length check resolves
+        if (static_cast<int64_t>(p) >= hist_len) {
+            bad_range = 1;
+            bad_at = j;
+            continue;
+        }
         if (slot < 0 || slot >= B || spos[slot] != p) {
             bad_res = 1;
             bad_at = j;
