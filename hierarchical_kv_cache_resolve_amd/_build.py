@@ -43,5 +43,21 @@ def build_library(verbose: bool = False) -> str:
     return LIB
 
 
+POLICY_LIB = os.path.join(HERE, "libhspolicy.so")
+
+
+def build_policy(verbose: bool = False) -> str:
+    """The CPU trace-replay library of the cache-policy study (plain C++)."""
+    tmp = POLICY_LIB + ".tmp"
+    cmd = ["g++", "-O2", "-Wall", "-std=c++17", "-shared", "-fPIC", "-pthread", "-I" + os.path.join(ROOT, "include"),
+           "-o", tmp, os.path.join(HERE, "csrc", "policy.cpp")]
+    if verbose:
+        print("+", " ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, POLICY_LIB)
+    return POLICY_LIB
+
+
 if __name__ == "__main__":
     build_library(verbose=True)
+    build_policy(verbose=True)

@@ -38,3 +38,12 @@ def test_no_oracle_on_product_path():
             if f.endswith((".py", ".hip", ".h", ".cpp", ".c")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
+
+
+def test_policy_library_exports_every_declared_symbol():
+    src = open(os.path.join(ROOT, "include", "hspolicy.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = sorted(set(re.findall(r"\b(hs_policy_[a-z0-9_]+)\s*\(", src)))
+    assert names == ["hs_policy_replay", "hs_policy_replay_many"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "hierarchical_kv_cache_resolve_amd", "libhspolicy.so"))
+    assert all(hasattr(lib, n) for n in names)
