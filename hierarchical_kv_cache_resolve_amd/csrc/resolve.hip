@@ -349,7 +349,10 @@ __device__ inline void radix_select(const PlanLds& l, const uint32_t (&tsv)[PER]
 //      (2t+1 for misses, 2t+2 for hits), page table and plan are written and
 //      every selection's slot is published.
 template <int PER, bool VEC, bool SCAN>
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(StateBase s, LayerBatch lb) {
+// Up to B = 4096 (PER <= 4) the kernel fits 8 waves per SIMD, so two workgroups share a CU
+// in batched launches over many (request, layer) units.
+__global__ __launch_bounds__(kPlanThreads) __attribute__((amdgpu_waves_per_eu(PER <= 4 ? 8 : 1)))
+void plan_kernel(StateBase s, LayerBatch lb) {
     extern __shared__ int lds_raw[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = blockIdx.x;
