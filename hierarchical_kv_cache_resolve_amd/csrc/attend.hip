@@ -101,10 +101,13 @@ __device__ __forceinline__ void issue_records(uint8_t* buf, const uint8_t* src_a
         for (int h = 0; h < 2; ++h) {
             const uint8_t* dst = buf + L * kLineBlock + (2 * wave + h) * 1024;
             const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)dst));
-            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                         :
-                         : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"((h ? src_b : src_a) + 128 * L)
-                         : "memory", "m0");
+            // M0 carries the LDS destination; its previous value is restored
+            uint32_t m0_saved;
+            asm volatile(
+                "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+                : "=&s"(m0_saved)
+                : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"((h ? src_b : src_a) + 128 * L)
+                : "memory");
         }
     }
 }

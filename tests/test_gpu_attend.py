@@ -180,3 +180,54 @@ def test_attend_full_size(hs):
     print("attend full size", flush=True)
     out, lse = run_attend(hs, res, 0, q_np, slot_idx, 1.0 / 24.0, dev)
     check(hs, q_np, records(w, pool_np, 0, sel), 1.0 / 24.0, out, lse)
+
+
+def test_attend_in_a_captured_graph(hs):
+    """RESOLVE + attention captured together and replayed over several steps,
+    with eager work between replays: every replay equals the eager run."""
+    w = tg.Workload("attend_graph", 2, 2, 8192, 576, 2, 256, 512, 6, tg.LOCALITY, 0.8, seed_index=67)
+    sel_all = torch.from_numpy(tg.trace(w)).to(torch.device("cuda:0"))
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(11)
+    q = torch.from_numpy(rand_bits(rng, (w.num_req, 64, D_QK)).view(np.int16)).to(dev)
+
+    def run(res, graph_steps):
+        outs = []
+        slot = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
+        o = torch.empty((w.num_layers, w.num_req, 64, D_V), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.num_layers, w.num_req, 64), dtype=torch.float32, device=dev)
+        res.resolve(0, sel_all[0, 0], slot[0])
+        res.attend_mla(0, q, slot[0], 0.1, o[0], lse[0])      # sizes the workspace before any capture
+        torch.cuda.synchronize()
+        res.reset()
+        if graph_steps:
+            g = torch.cuda.CUDAGraph()
+            # the captured step reads its selection from a fixed buffer
+            cur = torch.empty_like(sel_all[0])
+            with torch.cuda.graph(g):
+                for l in range(w.num_layers):
+                    res.resolve(l, cur[l], slot[l])
+                    res.attend_mla(l, q, slot[l], 0.1, o[l], lse[l])
+            for t in range(w.steps):
+                cur.copy_(sel_all[t])
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                _ = torch.ones(1024, device=dev).sum().item()       # eager work between replays
+                outs.append((o.cpu().clone(), lse.cpu().clone()))
+            del g
+        else:
+            for t in range(w.steps):
+                for l in range(w.num_layers):
+                    res.resolve(l, sel_all[t, l], slot[l])
+                    res.attend_mla(l, q, slot[l], 0.1, o[l], lse[l])
+                torch.cuda.synchronize()
+                outs.append((o.cpu().clone(), lse.cpu().clone()))
+        res.check_error()
+        return outs
+
+    pool = make_pool(hs, w)
+    eager = run(make_resolver(hs, w, pool), False)
+    graph = run(make_resolver(hs, w, pool), True)
+    for t, ((oe, le), (og, lg)) in enumerate(zip(eager, graph)):
+        assert torch.equal(oe, og) and torch.equal(le, lg), f"step {t}"
