@@ -289,6 +289,22 @@ class HostPool:
             self.ptr = 0
 
 
+def _dev_arg(t, nbytes, itemsize, name):
+    """Refuse a device tensor that the kernels would index out of bounds: it
+    must be a contiguous GPU tensor of the element size the call expects and
+    hold at least nbytes."""
+    if t is None or isinstance(t, int):
+        return                                           # raw pointers are the caller's responsibility
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name}: expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if itemsize and t.element_size() != itemsize:
+        raise ValueError(f"{name}: expected {itemsize}-byte elements, got {t.element_size()}")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, need {nbytes}")
+
+
 class Resolver:
     """One handle: num_req x num_layers GPU caches of B slots over a host pool."""
 
@@ -313,10 +329,15 @@ class Resolver:
 
     def resolve(self, layer, sel, out, stream=None):
         k = int(sel.shape[-1])
+        _dev_arg(sel, 4 * self.num_req * k, 4, "sel")
+        _dev_arg(out, 4 * self.num_req * k, 4, "out")
         _check("hisparse_resolve", hisparse_resolve(self.h, layer, _ptr(sel), k, _ptr(out), _stream(stream)))
 
     def resolve_layers(self, layers, sels, outs, stream=None):
         k = int(sels[0].shape[-1])
+        for s_, o_ in zip(sels, outs):
+            _dev_arg(s_, 4 * self.num_req * k, 4, "sel")
+            _dev_arg(o_, 4 * self.num_req * k, 4, "out")
         _check("hisparse_resolve_layers", hisparse_resolve_layers(
             self.h, list(layers), [_ptr(s) for s in sels], k, [_ptr(o) for o in outs], _stream(stream)))
 
@@ -328,6 +349,7 @@ class Resolver:
 
     def append(self, layer, rows, stream=None):
         """rows: device tensor [num_req][row_bytes] (any dtype of that byte size)."""
+        _dev_arg(rows, self.num_req * self.row_bytes, 0, "rows")
         _check("hisparse_append", hisparse_append(self.h, layer, _ptr(rows), _stream(stream)))
 
     def set_lengths(self, lengths):
@@ -361,11 +383,18 @@ class Resolver:
             raise HisparseError(f"device error code {code} at layer {layer} request {req}", HS_E_DEVICE)
 
     def gather_checksum(self, layer, slot_idx, out, stream=None):
+        _dev_arg(slot_idx, 4 * self.num_req * int(slot_idx.shape[-1]), 4, "slot_idx")
+        _dev_arg(out, 8 * self.num_req, 8, "out")
         _check("hisparse_gather_checksum", hisparse_gather_checksum(
             self.h, layer, _ptr(slot_idx), int(slot_idx.shape[-1]), _ptr(out), _stream(stream)))
 
     def attend_mla(self, layer, q, slot_idx, scale, out, lse=None, stream=None):
         """q: bf16 device tensor [num_req][H][576]; out fp32 [num_req][H][512]; lse fp32 [num_req][H] or None."""
+        R, H, k = self.num_req, int(q.shape[1]), int(slot_idx.shape[-1])
+        _dev_arg(q, 2 * R * H * 576, 2, "q")
+        _dev_arg(slot_idx, 4 * R * k, 4, "slot_idx")
+        _dev_arg(out, 4 * R * H * 512, 4, "out")
+        _dev_arg(lse, 4 * R * H, 4, "lse")
         _check("hisparse_attend_mla", hisparse_attend_mla(
             self.h, layer, _ptr(q), int(q.shape[1]), _ptr(slot_idx), int(slot_idx.shape[-1]), float(scale),
             _ptr(out), _ptr(lse), _stream(stream)))

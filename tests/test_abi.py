@@ -47,3 +47,36 @@ def test_policy_library_exports_every_declared_symbol():
     assert names == ["hs_policy_replay", "hs_policy_replay_many"]
     lib = ctypes.CDLL(os.path.join(ROOT, "hierarchical_kv_cache_resolve_amd", "libhspolicy.so"))
     assert all(hasattr(lib, n) for n in names)
+
+
+def test_binding_refuses_tensors_the_kernels_would_overrun():
+    import hierarchical_kv_cache_resolve_amd as hs
+    import pytest
+    import torch
+
+    class FakeDev:
+        is_cuda = True
+
+        def __init__(self, n, size, contiguous=True):
+            self.n, self.size, self.c = n, size, contiguous
+
+        def is_contiguous(self):
+            return self.c
+
+        def element_size(self):
+            return self.size
+
+        def numel(self):
+            return self.n
+
+    hs._dev_arg(None, 100, 4, "x")                     # optional argument
+    hs._dev_arg(12345, 100, 4, "x")                    # raw pointer: the caller's responsibility
+    hs._dev_arg(FakeDev(25, 4), 100, 4, "x")
+    with pytest.raises(ValueError):
+        hs._dev_arg(torch.zeros(25, dtype=torch.int32), 100, 4, "x")     # host tensor
+    with pytest.raises(ValueError):
+        hs._dev_arg(FakeDev(24, 4), 100, 4, "x")        # too small
+    with pytest.raises(ValueError):
+        hs._dev_arg(FakeDev(50, 2), 100, 4, "x")        # wrong element size
+    with pytest.raises(ValueError):
+        hs._dev_arg(FakeDev(25, 4, contiguous=False), 100, 4, "x")

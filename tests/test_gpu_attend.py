@@ -157,7 +157,7 @@ def test_attend_rejects_bad_arguments(hs):
     pool2 = make_pool(hs, w2)
     res2 = make_resolver(hs, w2, pool2)
     with pytest.raises(hs.HisparseError):
-        res2.attend_mla(0, q[:, :32], idx, 0.1, out)   # heads not a multiple of 64
+        res2.attend_mla(0, q[:, :32].contiguous(), idx, 0.1, out)   # heads not a multiple of 64
     with pytest.raises(hs.HisparseError):
         res2.attend_mla(1, q, idx, 0.1, out)           # no such layer
 
