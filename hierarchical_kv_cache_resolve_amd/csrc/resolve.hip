@@ -348,10 +348,12 @@ __device__ inline void radix_select(const PlanLds& l, const uint32_t (&tsv)[PER]
 //   5. the i-th miss takes the i-th victim in slot order; slot map, stamps
 //      (2t+1 for misses, 2t+2 for hits), page table and plan are written and
 //      every selection's slot is published.
-template <int PER, bool VEC, bool SCAN>
-// Up to B = 4096 (PER <= 4) the kernel fits 8 waves per SIMD, so two workgroups share a CU
-// in batched launches over many (request, layer) units.
-__global__ __launch_bounds__(kPlanThreads) __attribute__((amdgpu_waves_per_eu(PER <= 4 ? 8 : 1)))
+// WIDE: the instantiation for launches over many (request, layer) units.  Up
+// to B = 4096 (PER <= 4) it is held to 8 waves per SIMD, so two workgroups
+// share a CU; per-layer launches (a few units) use the unconstrained build,
+// whose scalar registers need not spill.
+template <int PER, bool VEC, bool SCAN, bool WIDE>
+__global__ __launch_bounds__(kPlanThreads) __attribute__((amdgpu_waves_per_eu(WIDE && PER <= 4 ? 8 : 1)))
 void plan_kernel(StateBase s, LayerBatch lb) {
     extern __shared__ int lds_raw[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -805,15 +807,22 @@ size_t plan_lds_bytes(int k, int hash_bits, int B) {
                           kHistBins + kMisc);
 }
 
-template <int PER, bool VEC, bool SCAN>
-static hipError_t launch_plan_t(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
+template <int PER, bool VEC, bool SCAN, bool WIDE>
+static hipError_t launch_plan_w(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&plan_kernel<PER, VEC, SCAN>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&plan_kernel<PER, VEC, SCAN, WIDE>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((plan_kernel<PER, VEC, SCAN>), dim3(s.R, lb.n), dim3(kPlanThreads), lds, st, s, lb);
+    hipLaunchKernelGGL((plan_kernel<PER, VEC, SCAN, WIDE>), dim3(s.R, lb.n), dim3(kPlanThreads), lds, st, s, lb);
     return hipGetLastError();
+}
+
+template <int PER, bool VEC, bool SCAN>
+static hipError_t launch_plan_t(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
+    // enough units that two per CU matter: more than one workgroup per CU
+    return static_cast<int64_t>(s.R) * lb.n > 256 ? launch_plan_w<PER, VEC, SCAN, true>(s, lb, lds, st)
+                                                 : launch_plan_w<PER, VEC, SCAN, false>(s, lb, lds, st);
 }
 
 template <int PER, bool SCAN>

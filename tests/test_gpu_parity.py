@@ -284,3 +284,32 @@ def test_victims_older_than_histogram_range(hs):
     res.close()
     scan.close()
     pool.free()
+
+
+def test_batched_launch_over_many_units(hs):
+    """One launch over 512 (request, layer) units (the build held to two
+    workgroups per CU) against the oracle, with misses and all-hit steps."""
+    from oracle import Oracle
+    w = tg.Workload("batched_wide", 64, 8, 8192, 8, 2, 256, 512, 6, tg.LOCALITY, 0.85, seed_index=95)
+    tr = tg.trace(w)
+    tr[3] = tr[2]                         # an all-hit step
+    pool = make_pool(hs, w)
+    pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
+    res = make_resolver(hs, w, pool)
+    o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes)
+    dev = torch.device("cuda:0")
+    layers = list(range(w.num_layers))
+    sel = torch.from_numpy(tr).to(dev)
+    out = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
+    for t in range(w.steps):
+        res.resolve_layers(layers, [sel[t, l] for l in layers], [out[l] for l in layers])
+        torch.cuda.synchronize()
+        for l in layers:
+            ref = o.resolve(l, tr[t, l], pool_np, w.region_rows())
+            assert np.array_equal(out[l].cpu().numpy(), ref["slot_idx"]), f"step {t} layer {l}"
+        st = res.state(w.num_layers - 1)
+        assert np.array_equal(st["ts"], o.ts[w.num_layers - 1])
+        assert np.array_equal(st["slot_pos"], o.slot_pos[w.num_layers - 1])
+    assert res.error()[0] == 0
+    res.close()
+    pool.free()
