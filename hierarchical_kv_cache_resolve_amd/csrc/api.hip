@@ -673,7 +673,8 @@ int hisparse_attend_mla(hisparse_t h, int layer, const void* d_q, int num_heads,
                         float scale, float* d_out, float* d_lse, void* stream) {
     if (!valid(h)) return HS_E_HANDLE;
     if (layer < 0 || layer >= h->NL) return HS_E_LAYER;
-    if (!d_q || !d_slot_idx || !d_out || num_heads < 64 || num_heads % 64 != 0) return HS_E_INVAL;
+    if (!d_q || !d_slot_idx || !d_out || num_heads < 64 || num_heads % 64 != 0 || num_heads > HS_MAX_HEADS)
+        return HS_E_INVAL;
     if (h->dtype != HS_BF16 || h->W_KV != 576) return HS_E_INVAL;
     if (k < 1 || k > h->B) return HS_E_K;
     const int chunk = hs::attend_chunk(h->R, num_heads, k);

@@ -400,9 +400,14 @@ hipError_t launch_attend_mla(const StateBase& s, int layer, const uint16_t* q, i
     const int nchunk = (k + chunk - 1) / chunk;
     float* part_o = workspace;
     float* part_ml = workspace + static_cast<size_t>(s.R) * nchunk * H * kDv;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mla_partial_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kAttnLds));
-    if (e != hipSuccess) return e;
+    static bool lds_attr_set = false;  // the attribute belongs to the kernel: set it once per process
+    if (!lds_attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mla_partial_kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(kAttnLds));
+        if (e != hipSuccess) return e;
+        lds_attr_set = true;
+    }
     const float scale_log2 = scale * 1.44269504088896340736f;
     const int nwg = nchunk * (H / kHeadsPerWG) * s.R;
     hipLaunchKernelGGL(mla_partial_kernel, dim3(nwg), dim3(kAttnThreads), kAttnLds, st, s, layer, q, H, slot_idx, k,

@@ -84,6 +84,7 @@ typedef struct hisparse_ctx* hisparse_t;
 #define HS_MAX_B 16384        /* slots per (request, layer) */
 #define HS_MAX_K 4096         /* selections per (request, layer, step) */
 #define HS_MAX_REQ 1024       /* requests per handle */
+#define HS_MAX_HEADS 1024     /* query heads per hisparse_attend_mla call */
 
 typedef enum { HS_BF16 = 0, HS_FP16 = 1, HS_FP8 = 2, HS_FP32 = 3 } hs_dtype; /* sets s only */
 
@@ -251,7 +252,7 @@ int hisparse_gather_checksum(hisparse_t h, int layer, const int32_t* d_slot_idx,
  *   d_lse   fp32 [num_req][num_heads] log-sum-exp of the scaled scores, or NULL
  * A record whose slot is -1 (a rejected request) is left out; a request
  * with none gives zeros and lse = -inf.  num_heads must be a multiple of
- * 64.  The first call for a larger shape allocates the handle's workspace
+ * 64, at most HS_MAX_HEADS.  The first call for a larger shape allocates the handle's workspace
  * (make that call before capturing a graph).
  * Errors: HS_E_HANDLE, HS_E_LAYER, HS_E_INVAL, HS_E_K, HS_E_NOMEM, HS_E_HIP. */
 int hisparse_attend_mla(hisparse_t h, int layer, const void* d_q, int num_heads, const int32_t* d_slot_idx, int k,

@@ -160,6 +160,10 @@ def test_attend_rejects_bad_arguments(hs):
         res2.attend_mla(0, q[:, :32].contiguous(), idx, 0.1, out)   # heads not a multiple of 64
     with pytest.raises(hs.HisparseError):
         res2.attend_mla(1, q, idx, 0.1, out)           # no such layer
+    q_many = torch.zeros((1, 1088, D_QK), dtype=torch.int16, device=dev)
+    out_many = torch.zeros((1, 1088, D_V), dtype=torch.float32, device=dev)
+    with pytest.raises(hs.HisparseError):
+        res2.attend_mla(0, q_many, idx, 0.1, out_many)  # more heads than HS_MAX_HEADS
 
 
 def test_attend_full_size(hs):
