@@ -677,7 +677,8 @@ int hisparse_attend_mla(hisparse_t h, int layer, const void* d_q, int num_heads,
         return HS_E_INVAL;
     if (h->dtype != HS_BF16 || h->W_KV != 576) return HS_E_INVAL;
     if (k < 1 || k > h->B) return HS_E_K;
-    const int chunk = hs::attend_chunk(h->R, num_heads, k);
+    const int ht = hs::attend_head_tiles(h->R, num_heads, k);
+    const int chunk = hs::attend_chunk(h->R, num_heads, k, ht);
     const int nchunk = (k + chunk - 1) / chunk;
     const size_t need = hs::attend_workspace_floats(h->R, num_heads, nchunk);
     if (need > h->attn_ws_floats) {
@@ -691,7 +692,7 @@ int hisparse_attend_mla(hisparse_t h, int layer, const void* d_q, int num_heads,
         h->attn_ws_floats = need;
     }
     return hs::launch_attend_mla(h->s, layer, static_cast<const uint16_t*>(d_q), num_heads, d_slot_idx, k, scale,
-                                 d_out, d_lse, h->attn_ws, chunk, static_cast<hipStream_t>(stream)) == hipSuccess
+                                 d_out, d_lse, h->attn_ws, ht, chunk, static_cast<hipStream_t>(stream)) == hipSuccess
                ? HS_OK
                : HS_E_HIP;
 }

@@ -9,8 +9,8 @@
 // each head lives in the 576-element record space, scores are dot products
 // with whole records and the values are the records' first 512 elements.
 //
-// Work split (flash-decoding): workgroup = (request, 64 heads, a chunk of
-// records); 4 wave64s.  Records move HBM -> LDS with
+// Work split (flash-decoding): workgroup = (request, 32 or 64 heads, a chunk
+// of records); 4 wave64s.  Records move HBM -> LDS with
 // global_load_lds (16 bytes a lane, no registers), 64 records per sub-chunk
 // into one of two LDS buffers, so the loads of sub-chunk i+1 are in flight
 // while sub-chunk i is computed.
@@ -21,18 +21,21 @@
 // records (8 lanes a line, so every access is a full coalesced line), a lane
 // loads the same two records for the whole sub-chunk, and the XOR swizzle
 // keeps both operand reads below free of bank conflicts:
-//   scores  wave w: S^T = K Q^T for heads 16w..16w+15 (v_mfma_f32_16x16x32_bf16,
-//           K from LDS, Q fragments in registers); online softmax; the
+//   scores  wave w: S^T = K Q^T for one tile of 16 heads over all 64 records
+//           of the sub-chunk (64 heads a workgroup) or over 32 of them (32
+//           heads: two waves share a tile) (v_mfma_f32_16x16x32_bf16, K from
+//           LDS, Q fragments in registers); online softmax; the
 //           probabilities go to LDS as bf16 MFMA fragments;
 //   output  wave w: O^T = V^T P^T for output dimensions 128w..128w+127 of all
-//           64 heads; V^T comes from the gfx950 transposing LDS read
+//           the workgroup's heads; V^T comes from the gfx950 transposing LDS read
 //           (ds_read_b64_tr_b16, the costliest LDS access here, so each wave
 //           reads only its quarter of the values), P^T fragments from LDS.
 // The record order inside each 32-wide k-step is permuted identically on
 // both operands of O^T = V^T P^T, so the probability fragments are written
 // exactly as the score registers hold them.  A lane of the score phase owns
 // one head: running maximum and sum are per lane (log2 units) and reduce over
-// the 4 lanes holding the same head.  A second kernel combines the chunks of
+// the 4 lanes holding the same head (and, at 32 heads, over the two waves
+// sharing the head, through LDS).  A second kernel combines the chunks of
 // each (request, head).
 #include "hs_internal.h"
 
@@ -48,7 +51,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = kAttnThreads / 64;
-constexpr int kHeadsPerWG = 64;
+constexpr int kMaxHeadTiles = 4;               // a workgroup takes 2 or 4 tiles of 16 heads
 constexpr int kSub = 64;                       // records per LDS sub-chunk
 constexpr int kDqk = 576, kDv = 512;
 constexpr int kRecBytes = kDqk * 2;            // 1152
@@ -58,8 +61,10 @@ constexpr int kLineBlock = kSub * 128;         // 8 KB: one line of every record
 constexpr int kBufBytes = kLines * kLineBlock; // 73728 per buffer
 constexpr int kQSteps = kDqk / 32;             // 18 MFMA k-steps for the scores
 constexpr int kDTiles = kDv / 16;              // 32 output tiles of 16 dimensions
-constexpr int kPBytes = 4 * 2 * 1024;         // P fragments: [head tile][k-step][64 lanes][16 B]
-constexpr size_t kAttnLds = 2 * static_cast<size_t>(kBufBytes) + kPBytes + kHeadsPerWG * sizeof(float);
+constexpr int kPBytes = kMaxHeadTiles * 2 * 1024;   // P fragments: [head tile][k-step][64 lanes][16 B]
+constexpr int kXBytes = 2 * 16 * kMaxHeadTiles * 4;  // [record half][head] partial maxima / sums
+constexpr size_t kAttnLds =
+    2 * static_cast<size_t>(kBufBytes) + kPBytes + 16 * kMaxHeadTiles * sizeof(float) + kXBytes;
 constexpr int kDimsPerWave = kDv / kAttnWaves; // 128 output dimensions a wave
 constexpr int kWaveDTiles = kDimsPerWave / 16; // 8
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt == 0 only:
@@ -112,13 +117,24 @@ __device__ __forceinline__ void issue_records(uint8_t* buf, const uint8_t* src_a
     }
 }
 
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla_partial_kernel(StateBase s, int layer, const uint16_t* q,
-                                                                   int H, const int32_t* slot_idx, int k,
-                                                                   int chunk, int nchunk, float scale_log2,
-                                                                   float* part_o, float* part_ml) {
+// HT: head tiles of 16 per workgroup.  The score phase spreads the HT tiles
+// over the 4 waves: RS = 4 / HT waves share a tile, each taking 64 / RS of
+// the sub-chunk's records (HT score tiles of 16 records) and exchanging its
+// partial maximum through LDS; the value phase is split by output dimensions
+// as always.  HT = 2 halves the partial outputs per record read, which pays
+// when the split over records is deep (few requests); HT = 4 reads each
+// record into fewer workgroups.
+template <int HT>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_partial_kernel(StateBase s, int layer, const uint16_t* q, int H, const int32_t* slot_idx, int k, int chunk,
+                        int nchunk, float scale_log2, float* part_o, float* part_ml) {
+    constexpr int HPW = 16 * HT;         // heads per workgroup
+    constexpr int RS = kAttnWaves / HT;  // waves sharing a head tile in the score phase
+    constexpr int TPW = 4 / RS;          // score tiles (of 16 records) per wave
     extern __shared__ __align__(16) uint8_t attn_lds[];
-    uint8_t* pfrag = attn_lds + 2 * kBufBytes;                          // [4][2][64][16 B]
-    float* alpha_lds = reinterpret_cast<float*>(pfrag + kPBytes);       // [64] rescale of each head
+    uint8_t* pfrag = attn_lds + 2 * kBufBytes;                          // [HT][2][64][16 B]
+    float* alpha_lds = reinterpret_cast<float*>(pfrag + kPBytes);       // [HPW] rescale of each head
+    float* xchg = alpha_lds + 16 * kMaxHeadTiles;                       // [RS][HPW] per record share
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -126,12 +142,15 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(1,
     // workgroup -> (chunk, head group, request); when the grid divides into the
     // 8 XCDs, consecutive tiles (the head groups of one chunk) share an XCD and
     // so its L2
-    const int G = H / kHeadsPerWG;
+    const int G = H / HPW;
     const int nwg = gridDim.x;
     int T = blockIdx.x;
     if ((nwg & 7) == 0) T = (T & 7) * (nwg >> 3) + (T >> 3);
     const int g = T % G, c = (T / G) % nchunk, r = T / (G * nchunk);
-    const int h0 = g * kHeadsPerWG + wave * 16;               // first head of this wave's scores
+    // score phase: wave w takes head tile w % HT and record share w / HT of each
+    // sub-chunk (score tiles rh*TPW .. rh*TPW + TPW - 1)
+    const int hts = wave % HT, rh = wave / HT;
+    const int h0 = g * HPW + hts * 16;                        // first head of this wave's scores
     const int j_begin = c * chunk, j_end = min(k, j_begin + chunk);
     const int nsub = (j_end - j_begin + kSub - 1) / kSub;
     const int64_t rl = static_cast<int64_t>(layer) * s.R + r;
@@ -168,11 +187,11 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(1,
     }
     // output accumulators: dimension tile dt (dims 128w + 16dt ..) x head tile ht;
     // lane (grp, n) holds dims +4grp+i of head 16ht + n
-    f32x4 acc_o[kWaveDTiles][4];
+    f32x4 acc_o[kWaveDTiles][HT];
 #pragma unroll
     for (int dt = 0; dt < kWaveDTiles; ++dt)
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) acc_o[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ht = 0; ht < HT; ++ht) acc_o[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
     // per-lane LDS offsets of the two operand reads (the rest are immediates)
@@ -213,23 +232,24 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(1,
             return *reinterpret_cast<const bf16x8*>(buf + ((st & 1) ? s_odd : s_even) + (st >> 1) * kLineBlock +
                                                     2048 * nt);
         };
-        f32x4 sacc[4];
-        bf16x8 kf[kSDepth + 1][4];
+        f32x4 sacc[TPW];                          // tiles nt = rh*TPW + u
+        bf16x8 kf[kSDepth + 1][TPW];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < TPW; ++u) sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int d = 0; d < kSDepth; ++d)
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) kf[d][nt] = k_frag(d, nt);
+            for (int u = 0; u < TPW; ++u) kf[d][u] = k_frag(d, rh * TPW + u);
 #pragma unroll
         for (int st = 0; st < kQSteps; ++st) {
             if (st + kSDepth < kQSteps) {
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) kf[(st + kSDepth) % (kSDepth + 1)][nt] = k_frag(st + kSDepth, nt);
+                for (int u = 0; u < TPW; ++u)
+                    kf[(st + kSDepth) % (kSDepth + 1)][u] = k_frag(st + kSDepth, rh * TPW + u);
             }
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-                sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[st % (kSDepth + 1)][nt], aq[st], sacc[nt], 0, 0, 0);
+            for (int u = 0; u < TPW; ++u)
+                sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[st % (kSDepth + 1)][u], aq[st], sacc[u], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         // online softmax for head h0+n over the sub-chunk's 64 records, with a
@@ -240,16 +260,25 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(1,
         // running sum makes the result independent of m_ref.
         float mx = -INFINITY;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int u = 0; u < TPW; ++u)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool ok = (valid >> (16 * nt + 4 * grp + i)) & 1ull;
-                const float v = ok ? sacc[nt][i] * scale_log2 : -INFINITY;
-                sacc[nt][i] = v;
+                const bool ok = (valid >> (16 * (rh * TPW + u) + 4 * grp + i)) & 1ull;
+                const float v = ok ? sacc[u][i] * scale_log2 : -INFINITY;
+                sacc[u][i] = v;
                 mx = fmaxf(mx, v);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if constexpr (RS > 1) {
+            // the waves of a head tile see different records: all take the
+            // maximum over the 64, so all move the reference identically
+            if (grp == 0) xchg[rh * HPW + hts * 16 + n] = mx;
+            __syncthreads();
+#pragma unroll
+            for (int o = 0; o < RS; ++o)
+                if (o != rh) mx = fmaxf(mx, xchg[o * HPW + hts * 16 + n]);
+        }
         float alpha = 1.f;
         if (__builtin_amdgcn_read_exec() & __ballot(mx > m_run + kRescaleSlack)) {   // wave-uniform
             const float m_new = fmaxf(m_run, mx);
@@ -259,49 +288,54 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(1,
         }
         float sum = 0.f;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int u = 0; u < TPW; ++u)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float pr = (m_run == -INFINITY) ? 0.f : exp2f(sacc[nt][i] - m_run);
-                sacc[nt][i] = pr;
+                const float pr = (m_run == -INFINITY) ? 0.f : exp2f(sacc[u][i] - m_run);
+                sacc[u][i] = pr;
                 sum += pr;
             }
         sum += __shfl_xor(sum, 16, 64);
         sum += __shfl_xor(sum, 32, 64);
-        l_run += sum;
-        // publish: P fragments of this head tile (k-step ks takes records
-        // 32ks + 4grp + i and 32ks + 16 + 4grp + i, i < 4: the score registers
-        // of tiles 2ks and 2ks+1) and the rescale factor of each head
+        l_run += sum;                             // this record share's part; the shares add at the end
+        // publish: P fragments of this head tile for the k-steps its tiles cover
+        // (k-step ks takes records 32ks + 4grp + i and 32ks + 16 + 4grp + i,
+        // i < 4: the score registers of tiles 2ks and 2ks+1) and the rescale
+        // factor of each head
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const uint32_t w4[4] = {pack_bf16x2(sacc[2 * ks][0], sacc[2 * ks][1]),
-                                    pack_bf16x2(sacc[2 * ks][2], sacc[2 * ks][3]),
-                                    pack_bf16x2(sacc[2 * ks + 1][0], sacc[2 * ks + 1][1]),
-                                    pack_bf16x2(sacc[2 * ks + 1][2], sacc[2 * ks + 1][3])};
-            *reinterpret_cast<uint4*>(pfrag + ((wave * 2 + ks) * 64 + lane) * 16) =
+        for (int kl = 0; kl < TPW / 2; ++kl) {
+            const int ks = rh * (TPW / 2) + kl;
+            const uint32_t w4[4] = {pack_bf16x2(sacc[2 * kl][0], sacc[2 * kl][1]),
+                                    pack_bf16x2(sacc[2 * kl][2], sacc[2 * kl][3]),
+                                    pack_bf16x2(sacc[2 * kl + 1][0], sacc[2 * kl + 1][1]),
+                                    pack_bf16x2(sacc[2 * kl + 1][2], sacc[2 * kl + 1][3])};
+            *reinterpret_cast<uint4*>(pfrag + ((hts * 2 + ks) * 64 + lane) * 16) =
                 make_uint4(w4[0], w4[1], w4[2], w4[3]);
         }
-        if (grp == 0) alpha_lds[wave * 16 + n] = alpha;
+        if (grp == 0 && rh == 0) alpha_lds[hts * 16 + n] = alpha;
         __syncthreads();                          // P and the rescale factors are visible
 
         // rescale this wave's accumulators where a score phase moved its reference
-        float a_ht[4];
+        float a_ht[HT];
+        bool moved = false;
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) a_ht[ht] = alpha_lds[ht * 16 + n];
-        if (sub > 0 && (__builtin_amdgcn_read_exec() &
-                        __ballot(a_ht[0] != 1.f || a_ht[1] != 1.f || a_ht[2] != 1.f || a_ht[3] != 1.f))) {
+        for (int ht = 0; ht < HT; ++ht) {
+            a_ht[ht] = alpha_lds[ht * 16 + n];
+            moved |= a_ht[ht] != 1.f;
+        }
+        if (sub > 0 && (__builtin_amdgcn_read_exec() & __ballot(moved))) {
 #pragma unroll
             for (int dt = 0; dt < kWaveDTiles; ++dt)
 #pragma unroll
-                for (int ht = 0; ht < 4; ++ht) acc_o[dt][ht] *= a_ht[ht];
+                for (int ht = 0; ht < HT; ++ht) acc_o[dt][ht] *= a_ht[ht];
         }
 
-        // O^T += V^T P^T for dims 128w.. of all 64 heads
+        // O^T += V^T P^T for dims 128w.. of the workgroup's heads
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 pf[4];
+            bf16x8 pf[HT];
 #pragma unroll
-            for (int ht = 0; ht < 4; ++ht)
+            for (int ht = 0; ht < HT; ++ht)
                 pf[ht] = *reinterpret_cast<const bf16x8*>(pfrag + ((ht * 2 + ks) * 64 + lane) * 16);
             const uint8_t* vb = buf + 4096 * ks + (wave * kWaveDTiles / 4) * kLineBlock;
             auto v_frag = [&](int dt) -> bf16x8 {
@@ -317,7 +351,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(1,
             for (int dt = 0; dt < kWaveDTiles; ++dt) {
                 if (dt + kVDepth < kWaveDTiles) vf[(dt + kVDepth) % (kVDepth + 1)] = v_frag(dt + kVDepth);
 #pragma unroll
-                for (int ht = 0; ht < 4; ++ht)
+                for (int ht = 0; ht < HT; ++ht)
                     acc_o[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt % (kVDepth + 1)], pf[ht],
                                                                             acc_o[dt][ht], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
@@ -330,16 +364,24 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(1,
     // partials: unnormalised O, running maximum and sum (log2 units); lane
     // (grp, n) holds dims 128w + 16dt + 4grp + i of head 16ht + n, and the
     // score-phase statistics of head h0 + n
-    const int64_t hbase = (static_cast<int64_t>(r) * nchunk + c) * H + g * kHeadsPerWG;
+    const int64_t hbase = (static_cast<int64_t>(r) * nchunk + c) * H + g * HPW;
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
+    for (int ht = 0; ht < HT; ++ht) {
         float* orow = part_o + (hbase + ht * 16 + n) * kDv + wave * kDimsPerWave + 4 * grp;
 #pragma unroll
         for (int dt = 0; dt < kWaveDTiles; ++dt) *reinterpret_cast<f32x4*>(orow + 16 * dt) = acc_o[dt][ht];
     }
-    if (grp == 0) {
-        part_ml[(hbase + wave * 16 + n) * 2 + 0] = m_run;
-        part_ml[(hbase + wave * 16 + n) * 2 + 1] = l_run;
+    // the running sum of each head is split over its record shares
+    float l_tot = l_run;
+    if constexpr (RS > 1) {
+        if (grp == 0 && rh > 0) xchg[(rh - 1) * HPW + hts * 16 + n] = l_run;
+        __syncthreads();
+#pragma unroll
+        for (int o = 1; o < RS; ++o) l_tot += xchg[(o - 1) * HPW + hts * 16 + n];
+    }
+    if (grp == 0 && rh == 0) {
+        part_ml[(hbase + hts * 16 + n) * 2 + 0] = m_run;
+        part_ml[(hbase + hts * 16 + n) * 2 + 1] = l_tot;
     }
 }
 
@@ -386,32 +428,49 @@ size_t attend_workspace_floats(int R, int H, int nchunk) {
     return static_cast<size_t>(R) * nchunk * H * (kDv + 2);
 }
 
-int attend_chunk(int R, int H, int k) {
+int attend_chunk(int R, int H, int k, int ht) {
     // enough workgroups to cover the chip (about 256), in multiples of the sub-chunk
-    const int64_t per = (static_cast<int64_t>(k) * R * (H / kHeadsPerWG) + 255) / 256;
+    const int64_t per = (static_cast<int64_t>(k) * R * (H / (16 * ht)) + 255) / 256;
     int chunk = static_cast<int>(((per + kSub - 1) / kSub) * kSub);
     if (chunk < kSub) chunk = kSub;
     if (chunk > k) chunk = ((k + kSub - 1) / kSub) * kSub;
     return chunk;
 }
 
+int attend_head_tiles(int R, int H, int k) {
+    // 64 heads per workgroup read each record into the fewest workgroups; when
+    // that leaves few records per workgroup, so that the split over records is
+    // deep (eight chunks or more), the fp32 partials it writes and reads back
+    // cost more than the extra record reads of 32 heads per workgroup
+    const int c4 = attend_chunk(R, H, k, 4);
+    return (k + c4 - 1) / c4 >= 8 ? 2 : 4;
+}
+
 hipError_t launch_attend_mla(const StateBase& s, int layer, const uint16_t* q, int H, const int32_t* slot_idx, int k,
-                             float scale, float* out, float* lse, float* workspace, int chunk, hipStream_t st) {
+                             float scale, float* out, float* lse, float* workspace, int ht, int chunk,
+                             hipStream_t st) {
+    if (ht != 2 && ht != 4) return hipErrorInvalidValue;
     const int nchunk = (k + chunk - 1) / chunk;
     float* part_o = workspace;
     float* part_ml = workspace + static_cast<size_t>(s.R) * nchunk * H * kDv;
-    static bool lds_attr_set = false;  // the attribute belongs to the kernel: set it once per process
-    if (!lds_attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mla_partial_kernel),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 static_cast<int>(kAttnLds));
+    // the attribute belongs to each kernel instance: set it once per process
+    static bool lds_attr_set[2] = {false, false};
+    const void* fn = ht == 2 ? reinterpret_cast<const void*>(&mla_partial_kernel<2>)
+                             : reinterpret_cast<const void*>(&mla_partial_kernel<4>);
+    if (!lds_attr_set[ht / 4]) {
+        const hipError_t e =
+            hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kAttnLds));
         if (e != hipSuccess) return e;
-        lds_attr_set = true;
+        lds_attr_set[ht / 4] = true;
     }
     const float scale_log2 = scale * 1.44269504088896340736f;
-    const int nwg = nchunk * (H / kHeadsPerWG) * s.R;
-    hipLaunchKernelGGL(mla_partial_kernel, dim3(nwg), dim3(kAttnThreads), kAttnLds, st, s, layer, q, H, slot_idx, k,
-                       chunk, nchunk, scale_log2, part_o, part_ml);
+    const int nwg = nchunk * (H / (16 * ht)) * s.R;
+    if (ht == 2)
+        hipLaunchKernelGGL(mla_partial_kernel<2>, dim3(nwg), dim3(kAttnThreads), kAttnLds, st, s, layer, q, H,
+                           slot_idx, k, chunk, nchunk, scale_log2, part_o, part_ml);
+    else
+        hipLaunchKernelGGL(mla_partial_kernel<4>, dim3(nwg), dim3(kAttnThreads), kAttnLds, st, s, layer, q, H,
+                           slot_idx, k, chunk, nchunk, scale_log2, part_o, part_ml);
     hipLaunchKernelGGL(mla_combine_kernel, dim3(H, s.R), dim3(kCombineThreads), 0, st, part_o, part_ml, H, nchunk, out,
                        lse);
     return hipGetLastError();

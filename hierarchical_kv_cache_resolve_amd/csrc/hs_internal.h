@@ -85,9 +85,11 @@ hipError_t launch_gather_checksum(const StateBase& s, int layer, const int32_t* 
                                   hipStream_t st);
 hipError_t launch_link_read(const void* src, void* dst, size_t bytes, hipStream_t st);
 size_t attend_workspace_floats(int R, int H, int nchunk);
-int attend_chunk(int R, int H, int k);
+int attend_chunk(int R, int H, int k, int ht);
+int attend_head_tiles(int R, int H, int k);
 hipError_t launch_attend_mla(const StateBase& s, int layer, const uint16_t* q, int H, const int32_t* slot_idx, int k,
-                             float scale, float* out, float* lse, float* workspace, int chunk, hipStream_t st);
+                             float scale, float* out, float* lse, float* workspace, int ht, int chunk,
+                             hipStream_t st);
 hipError_t launch_hbm_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 
 // Record the first device-side data error in the sticky word.

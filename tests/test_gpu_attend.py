@@ -75,8 +75,12 @@ def run_attend(hs, res, layer, q_np, slot_idx, scale, dev):
 
 
 def test_attend_after_resolve_ragged(hs):
-    """k from 1 to 1000 (ragged sub-chunks and chunks), 64 and 128 heads, two scales."""
-    w = tg.Workload("attend", 3, 2, 8192, 576, 2, 1000, 1024, 6, tg.LOCALITY, 0.8, seed_index=61)
+    """k from 1 to 1000 (ragged sub-chunks and chunks), 64 and 128 heads, two scales.
+
+    With three requests, k = 513, 777 and 1000 split over eight chunks or more
+    and take the 32-heads-a-workgroup kernel; the other cases take 64 heads a
+    workgroup."""
+    w = tg.Workload("attend", 3, 2, 8192, 576, 2, 1000, 1024, 8, tg.LOCALITY, 0.8, seed_index=61)
     sel_all = tg.trace(w)
     pool = make_pool(hs, w)
     pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
@@ -84,7 +88,7 @@ def test_attend_after_resolve_ragged(hs):
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(7)
     cases = [(1, 64, 0.0417), (37, 128, 0.25), (64, 64, 0.0417), (65, 128, 0.0417), (200, 64, 0.25),
-             (1000, 128, 0.0417)]
+             (513, 64, 0.25), (777, 128, 0.0417), (1000, 128, 0.0417)]
     for t, (k, H, scale) in enumerate(cases):
         for l in range(w.num_layers):
             sel = np.ascontiguousarray(sel_all[t, l, :, :k])
