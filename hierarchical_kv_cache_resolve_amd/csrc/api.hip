@@ -28,7 +28,7 @@ struct hisparse_ctx {
     int unroll = 4;
     bool nt = true;
     bool timing = false;
-    int probe = HS_PROBE_PAGE_TABLE;
+    int probe = HS_PROBE_SLOT_SCAN;
     float* attn_ws = nullptr;       // consumer workspace (partials per chunk)
     size_t attn_ws_floats = 0;
     // ordering of resolve / prefetch (host-side bookkeeping only)
@@ -554,7 +554,8 @@ int hisparse_set_option(hisparse_t h, int key, int64_t value) {
             h->unroll = static_cast<int>(value);
             return HS_OK;
         case HS_OPT_PROBE:
-            if (value != HS_PROBE_PAGE_TABLE && value != HS_PROBE_SLOT_SCAN) return HS_E_INVAL;
+            if (value != HS_PROBE_PAGE_TABLE && value != HS_PROBE_SLOT_SCAN && value != HS_PROBE_SLOT_SCAN_HASH)
+                return HS_E_INVAL;
             h->probe = static_cast<int>(value);
             return HS_OK;
         case HS_OPT_NT_LOADS:

@@ -59,7 +59,8 @@ struct LayerBatch {
     int n;
     int k;
     int hash_bits;
-    int probe;  // HS_PROBE_PAGE_TABLE or HS_PROBE_SLOT_SCAN
+    int probe;    // HS_PROBE_PAGE_TABLE, HS_PROBE_SLOT_SCAN or HS_PROBE_SLOT_SCAN_HASH
+    int lk_half;  // ints in each of the metadata kernel's two lookup arrays (set by launch_plan)
 };
 
 struct FetchBatch {
@@ -75,7 +76,7 @@ struct ReplayBatch {
 };
 
 // Host launchers (defined in the .hip files).
-size_t plan_lds_bytes(int k, int hash_bits, int B);
+size_t plan_lds_bytes(int k, int half, int B);
 hipError_t launch_plan(const StateBase& s, const LayerBatch& lb, hipStream_t st);
 hipError_t launch_publish(const StateBase& s, const LayerBatch& lb, hipStream_t st);
 hipError_t launch_fetch(const StateBase& s, const FetchBatch& fb, int blocks, int unroll, bool nt, hipStream_t st);

@@ -5,10 +5,12 @@
 // covers several independent layers with grid.y.  The five stages follow the
 // pith review's "Core claim" / "What carries the argument" (shared-memory hash
 // table over the selected positions, a parallel probe and scan to mark hits and
-// choose victims, page-table publication); the host fetch of the misses is the
-// separate streaming kernel in fetch.hip, launched right after on the same
-// stream, because the miss rows of all requests are best spread over the whole
-// chip rather than over one workgroup per request.
+// choose victims, page-table publication); where the history's positions fit,
+// the shared-memory structure is a bitmap over them with per-word ranks rather
+// than a hash, which gives each probe one lookup and no chains.  The host
+// fetch of the misses is the separate streaming kernel in fetch.hip, launched
+// right after on the same stream, because the miss rows of all requests are
+// best spread over the whole chip rather than over one workgroup per request.
 //
 // Determinism: victims are the m candidate slots with the smallest
 // (stamp, slot) keys, assigned in ascending slot order to the misses in
@@ -40,6 +42,14 @@ enum : int {
     M_HIST = 82,     // [16] histogram-scan wave totals
     M_BIN = 98,      // crossing bin of the current radix pass
     M_BELOW = 99,    // candidates below the crossing bin
+    M_RANK = 100,    // [16] selected positions per wave's run of bitmap words
+};
+
+// How the slot-scan probe maps a cached position to its selection index.
+enum : int {
+    PROBE_TABLE = 0,   // no slot scan: page-table lookups
+    PROBE_HASH = 1,    // bucketed LDS hash of the selection
+    PROBE_BITMAP = 2,  // LDS bitmap of the selected positions with per-word ranks
 };
 
 __device__ inline unsigned hash_bucket(int p, int bucket_bits) {
@@ -52,10 +62,11 @@ __device__ inline unsigned long long lanemask_lt() {
     return lane ? (~0ull >> (64 - lane)) : 0ull;
 }
 
-// LDS carve-up of the metadata kernel (ints): miss-hash keys [H], miss-hash
-// values [H], slot per selection [k], miss list [k], selection copy [k],
-// hit bitmap over slots [B/32 rounded up to 4], histogram [kHistBins], misc
-// [kMisc].  Keys come first so 16-byte bucket reads are aligned.
+// LDS carve-up of the metadata kernel (ints): the lookup structure's two
+// arrays of `half` ints each (hash keys and values, or the position bitmap and
+// its per-word ranks), slot per selection [k], miss list [k], selection copy
+// [k], hit bitmap over slots [B/32 rounded up to 4], histogram [kHistBins],
+// misc [kMisc].  Keys come first so 16-byte bucket reads are aligned.
 struct PlanLds {
     int* bkey;
     int* bval;
@@ -69,11 +80,11 @@ struct PlanLds {
 
 __device__ inline int hitmap_words(int B) { return ((B + 127) >> 7) << 2; }
 
-__device__ inline PlanLds carve(int* base, int H, int k, int B) {
+__device__ inline PlanLds carve(int* base, int half, int k, int B) {
     PlanLds l;
     l.bkey = base;
-    l.bval = l.bkey + H;
-    l.sidx = l.bval + H;
+    l.bval = l.bkey + half;
+    l.sidx = l.bval + half;
     l.mlist = l.sidx + k;
     l.sel = l.mlist + k;
     l.hitmap = reinterpret_cast<unsigned*>(l.sel + k);
@@ -207,17 +218,21 @@ __device__ inline void reject(const StateBase& s, int32_t* out, int k, int64_t r
     }
 }
 
-// Optional per-phase wall-clock stamps (constant-rate clock).  Lane 0 keeps
-// them in registers and writes them once at the end, so tracing adds no
-// global store that a later barrier would have to wait for.
-#define HS_PHASE(i)                                                      \
-    do {                                                                 \
-        if (s.phase != nullptr && tid == 0) stamp[(i)] = wall_clock64(); \
+// Optional per-phase wall-clock stamps (constant-rate clock).  Every wave
+// takes them (the clock read is a scalar instruction, so they stay in scalar
+// registers) and lane 0 writes its wave's once at the end, so tracing adds no
+// global store that a later barrier would have to wait for.  Slots: 0 start,
+// 1 global reads issued and LDS cleared, 2 selection inserted, 3 probe done,
+// 4 miss list, 5-8 victim stages, 9 metadata written, 10 published; the
+// bitmap probe also stamps 11 word counts, 12 ranks, 13 rank -> selection map.
+#define HS_PHASE(i)                                          \
+    do {                                                     \
+        if (s.phase != nullptr) stamp[(i)] = wall_clock64(); \
     } while (0)
 #define HS_PHASE_FLUSH()                                                                \
     do {                                                                                \
         if (s.phase != nullptr && tid == 0)                                             \
-            for (int i_ = 0; i_ < 11; ++i_) s.phase[rl * kPhaseSlots + i_] = stamp[i_]; \
+            for (int i_ = 0; i_ < 14; ++i_) s.phase[rl * kPhaseSlots + i_] = stamp[i_]; \
     } while (0)
 
 constexpr int kMaxSelPerLane = HS_MAX_K / kPlanThreads;  // 4
@@ -337,11 +352,19 @@ __device__ inline void radix_select(const PlanLds& l, const uint32_t (&tsv)[PER]
 
 // The metadata half of RESOLVE for one (request, layer).
 //   1. every global read is issued up front: clock, selection, slot map and
-//      stamps of this lane's slot run, then the page-table entry of each
-//      selected position (which says where the position is cached, if at all);
-//   2. hits are marked in an LDS bitmap over the slots (a slot claimed twice
-//      means a repeated position); the positions that missed go into an LDS
-//      hash table, which catches repeats among them;
+//      stamps of this lane's slot run, then (page-table probe) the page-table
+//      entry of each selected position (which says where the position is
+//      cached, if at all);
+//   2. page-table probe: hits are marked in an LDS bitmap over the slots (a
+//      slot claimed twice means a repeated position); the positions that
+//      missed go into an LDS hash table, which catches repeats among them.
+//      Slot-scan probe: every selected position goes into an LDS lookup
+//      structure (a repeat is caught on insertion) and every cached slot's
+//      position is looked up in it.  The structure is the hash table, or,
+//      when the history's positions fit, a bitmap over them with the rank
+//      of each word (selected positions in the words before it): the rank of
+//      a position is then its index among the selected positions in
+//      ascending order, which maps it to its selection index in O(1);
 //   3. misses are compacted in ascending j with wave ballots;
 //   4. the m victims are the non-hit slots with the smallest (stamp, slot)
 //      keys (radix select on the stamps, then one ballot-counted pass);
@@ -352,9 +375,10 @@ __device__ inline void radix_select(const PlanLds& l, const uint32_t (&tsv)[PER]
 // to B = 4096 (PER <= 4) it is held to 8 waves per SIMD, so two workgroups
 // share a CU; per-layer launches (a few units) use the unconstrained build,
 // whose scalar registers need not spill.
-template <int PER, bool VEC, bool SCAN, bool WIDE>
+template <int PER, bool VEC, int PROBE, bool WIDE>
 __global__ __launch_bounds__(kPlanThreads) __attribute__((amdgpu_waves_per_eu(WIDE && PER <= 4 ? 8 : 1)))
 void plan_kernel(StateBase s, LayerBatch lb) {
+    constexpr bool SCAN = PROBE != PROBE_TABLE;
     extern __shared__ int lds_raw[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = blockIdx.x;
@@ -368,9 +392,12 @@ void plan_kernel(StateBase s, LayerBatch lb) {
     int32_t* spos_g = s.slot_pos + rl * B;
     uint32_t* ts_g = s.ts + rl * B;
     int32_t* pt = s.page_table + rl * s.L_ctx;
-    const PlanLds l = carve(lds_raw, H, k, B);
+    const PlanLds l = carve(lds_raw, lb.lk_half, k, B);
+    // bitmap probe: word w of the position bitmap, and the rank of word w
+    unsigned* const pbits = reinterpret_cast<unsigned*>(l.bkey);
+    int* const prank = l.bval;
     const unsigned long long lt = lanemask_lt();
-    unsigned long long stamp[11] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    unsigned long long stamp[14] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     HS_PHASE(0);
 
     // 1. global reads
@@ -408,7 +435,13 @@ void plan_kernel(StateBase s, LayerBatch lb) {
         }
     }
 
-    for (int i = tid; i < H; i += kPlanThreads) l.bkey[i] = kEmpty;
+    if constexpr (PROBE == PROBE_BITMAP) {
+        // the whole region, padding words included (ranks read 16-byte groups)
+        for (int i = tid; i < (lb.lk_half >> 2); i += kPlanThreads)
+            reinterpret_cast<uint4*>(pbits)[i] = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+        for (int i = tid; i < H; i += kPlanThreads) l.bkey[i] = kEmpty;
+    }
     if constexpr (SCAN) {
         for (int j = tid; j < k; j += kPlanThreads) l.sidx[j] = -1;
     } else {
@@ -420,7 +453,7 @@ void plan_kernel(StateBase s, LayerBatch lb) {
     HS_PHASE(1);
 
     // 2. page-table probe: hits into the slot bitmap, misses into the hash.
-    //    slot-scan probe: every selected position into the hash.
+    //    slot-scan probe: every selected position into the lookup structure.
 #pragma unroll
     for (int q = 0; q < kMaxSelPerLane; ++q) {
         const int j = tid + q * kPlanThreads;
@@ -428,7 +461,14 @@ void plan_kernel(StateBase s, LayerBatch lb) {
             const int p = selv[q];
             const int slot = ptv[q];
             l.sel[j] = p;
-            if (SCAN) {
+            if constexpr (PROBE == PROBE_BITMAP) {
+                // p < L_ctx here (a lane with a bad position inserts nothing)
+                const unsigned bit = 1u << (p & 31);
+                if (atomicOr(&pbits[p >> 5], bit) & bit) {
+                    bad |= 2;
+                    bad_at = j + 1;
+                }
+            } else if constexpr (PROBE == PROBE_HASH) {
                 if (!bucket_insert(l, nbm, bucket_bits, p, j)) {
                     bad |= 2;
                     bad_at = j + 1;
@@ -465,7 +505,68 @@ void plan_kernel(StateBase s, LayerBatch lb) {
     }
     // this lane's slots that hold a selected position
     unsigned hitbits = 0;
-    if constexpr (SCAN) {
+    if constexpr (PROBE == PROBE_BITMAP) {
+        // ranks: lane tid owns the contiguous 16-byte groups of words
+        // [tid*gpl, tid*gpl + gpl), read and written whole
+        const int ng = lb.lk_half >> 2;
+        const int gpl = (ng + kPlanThreads - 1) / kPlanThreads;
+        const int g0 = tid * gpl;
+        const uint4* pb4 = reinterpret_cast<const uint4*>(pbits);
+        int cnt = 0;
+        for (int i = 0; i < gpl; ++i) {
+            if (g0 + i < ng) {
+                const uint4 v = pb4[g0 + i];
+                cnt += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
+            }
+        }
+        const int incl = wave_incl_scan(cnt);
+        if (lane == 63) l.misc[M_RANK + wave] = incl;
+        __syncthreads();
+        HS_PHASE(11);
+        int base = incl - cnt;
+#pragma unroll
+        for (int w = 0; w < kPlanWaves; ++w)
+            if (w < wave) base += l.misc[M_RANK + w];
+        for (int i = 0; i < gpl; ++i) {
+            if (g0 + i < ng) {
+                const uint4 v = pb4[g0 + i];
+                int4 rk;
+                rk.x = base;
+                rk.y = rk.x + __popc(v.x);
+                rk.z = rk.y + __popc(v.y);
+                rk.w = rk.z + __popc(v.z);
+                base = rk.w + __popc(v.w);
+                reinterpret_cast<int4*>(prank)[g0 + i] = rk;
+            }
+        }
+        __syncthreads();
+        HS_PHASE(12);
+        // selection index of each rank (the miss list's storage, not yet in use)
+#pragma unroll
+        for (int q = 0; q < kMaxSelPerLane; ++q) {
+            const int j = tid + q * kPlanThreads;
+            if (j < k) {
+                const int p = selv[q];
+                const unsigned below = (1u << (p & 31)) - 1u;
+                l.mlist[prank[p >> 5] + __popc(pbits[p >> 5] & below)] = j;
+            }
+        }
+        __syncthreads();
+        HS_PHASE(13);
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int p = spos[q];
+            if (s0 + q < B && p >= 0 && p < s.L_ctx) {
+                const unsigned word = pbits[p >> 5];
+                if ((word >> (p & 31)) & 1u) {
+                    const int j = l.mlist[prank[p >> 5] + __popc(word & ((1u << (p & 31)) - 1u))];
+                    l.sidx[j] = s0 + q;
+                    hitbits |= 1u << q;
+                }
+            }
+        }
+        __syncthreads();
+    } else if constexpr (PROBE == PROBE_HASH) {
         // the pages' probe: every cached position looked up in the hash
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
@@ -646,8 +747,10 @@ void plan_kernel(StateBase s, LayerBatch lb) {
         if (any_victim) store_run<PER, VEC, int>(spos_g, s0, B, spos);
         if (any_victim || hitbits) store_run<PER, VEC, uint32_t>(ts_g, s0, B, tsv);
         HS_PHASE(8);
+        __syncthreads();  // every miss's slot is in l.sidx
     }
-    __syncthreads();
+    // (all hit: l.sidx has not changed since the miss list's barrier, so the
+    // stamp stores need not drain before publication)
     HS_PHASE(9);
 
     // publication of every selection's slot
@@ -801,50 +904,73 @@ __global__ __launch_bounds__(kPlanThreads) void replay_meta_kernel(StateBase s, 
 
 }  // namespace
 
-size_t plan_lds_bytes(int k, int hash_bits, int B) {
+size_t plan_lds_bytes(int k, int half, int B) {
     const size_t hit_words = static_cast<size_t>(((B + 127) >> 7) << 2);
-    return sizeof(int) * (2 * (static_cast<size_t>(1) << hash_bits) + 3 * static_cast<size_t>(k) + hit_words +
-                          kHistBins + kMisc);
+    return sizeof(int) * (2 * static_cast<size_t>(half) + 3 * static_cast<size_t>(k) + hit_words + kHistBins + kMisc);
 }
 
-template <int PER, bool VEC, bool SCAN, bool WIDE>
+template <int PER, bool VEC, int PROBE, bool WIDE>
 static hipError_t launch_plan_w(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&plan_kernel<PER, VEC, SCAN, WIDE>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&plan_kernel<PER, VEC, PROBE, WIDE>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((plan_kernel<PER, VEC, SCAN, WIDE>), dim3(s.R, lb.n), dim3(kPlanThreads), lds, st, s, lb);
+    hipLaunchKernelGGL((plan_kernel<PER, VEC, PROBE, WIDE>), dim3(s.R, lb.n), dim3(kPlanThreads), lds, st, s, lb);
     return hipGetLastError();
 }
 
-template <int PER, bool VEC, bool SCAN>
-static hipError_t launch_plan_t(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
-    // enough units that two per CU matter: more than one workgroup per CU
-    return static_cast<int64_t>(s.R) * lb.n > 256 ? launch_plan_w<PER, VEC, SCAN, true>(s, lb, lds, st)
-                                                 : launch_plan_w<PER, VEC, SCAN, false>(s, lb, lds, st);
+template <int PER, bool VEC, int PROBE>
+static hipError_t launch_plan_t(const StateBase& s, const LayerBatch& lb, size_t lds, bool wide, hipStream_t st) {
+    return wide ? launch_plan_w<PER, VEC, PROBE, true>(s, lb, lds, st)
+                : launch_plan_w<PER, VEC, PROBE, false>(s, lb, lds, st);
 }
 
-template <int PER, bool SCAN>
-static hipError_t launch_plan_s(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
-    return (s.B & 3) == 0 ? launch_plan_t<PER, true, SCAN>(s, lb, lds, st)
-                          : launch_plan_t<PER, false, SCAN>(s, lb, lds, st);
+template <int PER, int PROBE>
+static hipError_t launch_plan_s(const StateBase& s, const LayerBatch& lb, size_t lds, bool wide, hipStream_t st) {
+    return (s.B & 3) == 0 ? launch_plan_t<PER, true, PROBE>(s, lb, lds, wide, st)
+                          : launch_plan_t<PER, false, PROBE>(s, lb, lds, wide, st);
 }
 
 template <int PER>
-static hipError_t launch_plan_p(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
-    return lb.probe == HS_PROBE_SLOT_SCAN ? launch_plan_s<PER, true>(s, lb, lds, st)
-                                          : launch_plan_s<PER, false>(s, lb, lds, st);
+static hipError_t launch_plan_p(const StateBase& s, const LayerBatch& lb, size_t lds, int probe, bool wide,
+                                hipStream_t st) {
+    switch (probe) {
+        case PROBE_BITMAP: return launch_plan_s<PER, PROBE_BITMAP>(s, lb, lds, wide, st);
+        case PROBE_HASH: return launch_plan_s<PER, PROBE_HASH>(s, lb, lds, wide, st);
+        default: return launch_plan_s<PER, PROBE_TABLE>(s, lb, lds, wide, st);
+    }
 }
 
-hipError_t launch_plan(const StateBase& s, const LayerBatch& lb, hipStream_t st) {
-    const size_t lds = plan_lds_bytes(lb.k, lb.hash_bits, s.B);
+hipError_t launch_plan(const StateBase& s, const LayerBatch& lb_in, hipStream_t st) {
+    LayerBatch lb = lb_in;
+    // enough units that two per CU matter: more than one workgroup per CU
+    const bool wide = static_cast<int64_t>(s.R) * lb.n > 256;
+    const int H = 1 << lb.hash_bits;
+    int probe = PROBE_TABLE;
+    lb.lk_half = H;
+    if (lb.probe == HS_PROBE_SLOT_SCAN_HASH) {
+        probe = PROBE_HASH;
+    } else if (lb.probe == HS_PROBE_SLOT_SCAN) {
+        // the bitmap over the history's positions when its two arrays fit the
+        // LDS the launch can give without losing workgroups per CU (80 KB for
+        // two per CU, 160 KB for one), or take no more than the hash's
+        probe = PROBE_HASH;
+        const int nw4 = static_cast<int>(((static_cast<int64_t>(s.L_ctx) + 127) >> 7) << 2);
+        const size_t with_bitmap = plan_lds_bytes(lb.k, nw4, s.B);
+        const size_t cap = wide ? 80 * 1024 : 160 * 1024;
+        if (with_bitmap <= cap || with_bitmap <= plan_lds_bytes(lb.k, H, s.B)) {
+            probe = PROBE_BITMAP;
+            lb.lk_half = nw4;
+        }
+    }
+    const size_t lds = plan_lds_bytes(lb.k, lb.lk_half, s.B);
     const int per = (s.B + kPlanThreads - 1) / kPlanThreads;
-    if (per <= 1) return launch_plan_p<1>(s, lb, lds, st);
-    if (per <= 2) return launch_plan_p<2>(s, lb, lds, st);
-    if (per <= 4) return launch_plan_p<4>(s, lb, lds, st);
-    if (per <= 8) return launch_plan_p<8>(s, lb, lds, st);
-    if (per <= 16) return launch_plan_p<16>(s, lb, lds, st);
+    if (per <= 1) return launch_plan_p<1>(s, lb, lds, probe, wide, st);
+    if (per <= 2) return launch_plan_p<2>(s, lb, lds, probe, wide, st);
+    if (per <= 4) return launch_plan_p<4>(s, lb, lds, probe, wide, st);
+    if (per <= 8) return launch_plan_p<8>(s, lb, lds, probe, wide, st);
+    if (per <= 16) return launch_plan_p<16>(s, lb, lds, probe, wide, st);
     return hipErrorInvalidValue;
 }
 

@@ -204,10 +204,12 @@ int hisparse_reset(hisparse_t h);
 #define HS_OPT_NT_LOADS 4       /* 1: non-temporal host loads and cache stores (default 1) */
 #define HS_OPT_PHASE_TRACE 5    /* 1: the metadata kernel stamps the end of each of its phases */
 #define HS_OPT_PROBE 6          /* how hits are found (same results either way):               */
-#define HS_PROBE_PAGE_TABLE 0   /*   one page-table load per selected position (default; lowest */
-                                /*   latency per layer)                                          */
-#define HS_PROBE_SLOT_SCAN 1    /*   every cached slot's position looked up in an LDS hash of   */
-                                /*   the selection, as the pages describe (fewest HBM bytes)     */
+#define HS_PROBE_PAGE_TABLE 0   /*   one page-table load per selected position                   */
+#define HS_PROBE_SLOT_SCAN 1    /*   (default) every cached slot's position looked up in an LDS   */
+                                /*   structure over the selection, as the pages describe (fewest  */
+                                /*   HBM bytes): a bitmap over the history's positions with       */
+                                /*   per-word ranks when it fits the LDS, else a hash             */
+#define HS_PROBE_SLOT_SCAN_HASH 2 /* the slot scan with the LDS hash whatever the history length */
 int hisparse_set_option(hisparse_t h, int key, int64_t value);
 
 /* Per-kernel times of launches issued while HS_OPT_TIMING was on, measured

@@ -102,11 +102,15 @@ SCAN_SUBSET = [w for w in RAGGED if w.name in ("ragged_b_not_mult4", "per1_small
                                               "b_equals_k", "uniform_small_ctx", "k1_b3", "hit_only")]
 
 
+@pytest.mark.parametrize("probe", ["page_table", "hash"])
 @pytest.mark.parametrize("w", SCAN_SUBSET, ids=[w.name for w in SCAN_SUBSET])
-def test_slot_scan_probe(hs, w):
-    """The pages' probe (hash over the selection, every cached slot looked up)
-    gives the same results as the page-table probe."""
-    run_parity(hs, w, options={hs.HS_OPT_PROBE: hs.HS_PROBE_SLOT_SCAN})
+def test_other_probes(hs, w, probe):
+    """The other two ways of finding hits give the same results as the default
+    (the pages' slot scan with the position bitmap, which the default takes at
+    these history lengths): one page-table load per selection, and the slot
+    scan with the LDS hash."""
+    opt = hs.HS_PROBE_PAGE_TABLE if probe == "page_table" else hs.HS_PROBE_SLOT_SCAN_HASH
+    run_parity(hs, w, options={hs.HS_OPT_PROBE: opt})
 
 
 @pytest.mark.parametrize("unroll,blocks,nt", [(1, 7, 0), (2, 64, 1), (8, 4096, 0)])
@@ -262,33 +266,41 @@ def test_victims_older_than_histogram_range(hs):
     pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
     res = make_resolver(hs, w, pool)
     scan = make_resolver(hs, w, pool)
-    scan.set_option(hs.HS_OPT_PROBE, hs.HS_PROBE_SLOT_SCAN)
+    scan.set_option(hs.HS_OPT_PROBE, hs.HS_PROBE_PAGE_TABLE)
+    hscan = make_resolver(hs, w, pool)
+    hscan.set_option(hs.HS_OPT_PROBE, hs.HS_PROBE_SLOT_SCAN_HASH)
     o = Oracle(R, 1, B, L_ctx, w.row_bytes)
     dev = torch.device("cuda:0")
     out = torch.empty((R, k), dtype=torch.int32, device=dev)
     out2 = torch.empty_like(out)
+    out3 = torch.empty_like(out)
     for t, S in enumerate(steps):
         Sd = torch.from_numpy(S).to(dev)
         res.resolve(0, Sd, out)
         scan.resolve(0, Sd, out2)
+        hscan.resolve(0, Sd, out3)
         ref = o.resolve(0, S, pool_np, w.region_rows())
         if t >= 690 or t < 6:
             got = out.cpu().numpy()
             assert np.array_equal(got, ref["slot_idx"]), f"step {t}"
-            assert np.array_equal(out2.cpu().numpy(), ref["slot_idx"]), f"slot-scan step {t}"
+            assert np.array_equal(out2.cpu().numpy(), ref["slot_idx"]), f"page-table probe step {t}"
+            assert np.array_equal(out3.cpu().numpy(), ref["slot_idx"]), f"hash slot-scan step {t}"
             st = res.state(0)
             assert np.array_equal(st["slot_pos"], o.slot_pos[0]) and np.array_equal(st["ts"], o.ts[0]), f"step {t}"
             m = int(ref["miss_count"][0])
             assert np.array_equal(st["plan"][0, :m], ref["plan"][0, :m]), f"plan step {t}"
-    assert res.error()[0] == 0 and scan.error()[0] == 0
+    assert res.error()[0] == 0 and scan.error()[0] == 0 and hscan.error()[0] == 0
     res.close()
     scan.close()
+    hscan.close()
     pool.free()
 
 
-def test_batched_launch_over_many_units(hs):
+@pytest.mark.parametrize("probe", ["page_table", "bitmap", "hash"])
+def test_batched_launch_over_many_units(hs, probe):
     """One launch over 512 (request, layer) units (the build held to two
-    workgroups per CU) against the oracle, with misses and all-hit steps."""
+    workgroups per CU) against the oracle, with misses and all-hit steps,
+    with each probe."""
     from oracle import Oracle
     w = tg.Workload("batched_wide", 64, 8, 8192, 8, 2, 256, 512, 6, tg.LOCALITY, 0.85, seed_index=95)
     tr = tg.trace(w)
@@ -296,6 +308,8 @@ def test_batched_launch_over_many_units(hs):
     pool = make_pool(hs, w)
     pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
     res = make_resolver(hs, w, pool)
+    res.set_option(hs.HS_OPT_PROBE, {"page_table": hs.HS_PROBE_PAGE_TABLE, "bitmap": hs.HS_PROBE_SLOT_SCAN,
+                                     "hash": hs.HS_PROBE_SLOT_SCAN_HASH}[probe])
     o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes)
     dev = torch.device("cuda:0")
     layers = list(range(w.num_layers))

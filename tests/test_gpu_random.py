@@ -59,7 +59,7 @@ def test_random_shapes_and_varying_k(hs, seed):
     pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
     res = make_resolver(hs, w, pool)
     other = make_resolver(hs, w, pool)   # a second live handle on the same pool, other probe
-    other.set_option(hs.HS_OPT_PROBE, hs.HS_PROBE_SLOT_SCAN)
+    other.set_option(hs.HS_OPT_PROBE, hs.HS_PROBE_PAGE_TABLE if seed % 2 == 0 else hs.HS_PROBE_SLOT_SCAN_HASH)
     o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes)
     dev = torch.device("cuda:0")
     prev = {}
