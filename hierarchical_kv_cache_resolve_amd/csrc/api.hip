@@ -306,6 +306,7 @@ static int resolve_plan_path(hisparse_t h, int n, const int* layers, const int32
     lb.k = k;
     lb.hash_bits = hash_bits_for(k);
     lb.probe = h->probe;
+    lb.nt = h->nt;
     fb.n = n;
     for (int i = 0; i < n; ++i) {
         const int l = layers[i];
@@ -327,8 +328,10 @@ static int resolve_plan_path(hisparse_t h, int n, const int* layers, const int32
         HS_TRY(hipEventRecord(h->ev_plan[layers[i]], st));
         h->plan_in_capture[layers[i]] = cap;
     }
-    rc = timed(h, K_FETCH, st, [&] { return hs::launch_fetch(h->s, fb, h->fetch_blocks, h->unroll, h->nt, st); });
-    if (rc != HS_OK) return rc;
+    if (!hs::plan_copies_misses(h->s, n)) {
+        rc = timed(h, K_FETCH, st, [&] { return hs::launch_fetch(h->s, fb, h->fetch_blocks, h->unroll, h->nt, st); });
+        if (rc != HS_OK) return rc;
+    }
     for (int i = 0; i < n; ++i) {
         const int l = layers[i];
         h->steps[l] += 1;

@@ -17,20 +17,6 @@ namespace hs {
 
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-template <bool NT>
-__device__ inline u32x4 ld16(const u32x4* p) {
-    if constexpr (NT) return __builtin_nontemporal_load(p);
-    else return *p;
-}
-
-template <bool NT>
-__device__ inline void st16(u32x4* p, u32x4 v) {
-    if constexpr (NT) __builtin_nontemporal_store(v, p);
-    else *p = v;
-}
-
 // Exclusive scan over the 256 lanes of a fetch workgroup.
 __device__ inline int block256_excl_scan(int v, int* total, int* scratch) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

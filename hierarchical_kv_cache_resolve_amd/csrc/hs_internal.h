@@ -61,6 +61,8 @@ struct LayerBatch {
     int hash_bits;
     int probe;    // HS_PROBE_PAGE_TABLE, HS_PROBE_SLOT_SCAN or HS_PROBE_SLOT_SCAN_HASH
     int lk_half;  // ints in each of the metadata kernel's two lookup arrays (set by launch_plan)
+    int nt;       // non-temporal host loads and cache stores in the metadata kernel's own copy
+    int copy;     // the metadata kernel copies the misses itself (set by launch_plan)
 };
 
 struct FetchBatch {
@@ -78,6 +80,9 @@ struct ReplayBatch {
 // Host launchers (defined in the .hip files).
 size_t plan_lds_bytes(int k, int half, int B);
 hipError_t launch_plan(const StateBase& s, const LayerBatch& lb, hipStream_t st);
+// Whether a metadata launch over n layers copies its own misses (a wide
+// launch: no fetch launch follows it).
+bool plan_copies_misses(const StateBase& s, int n);
 hipError_t launch_publish(const StateBase& s, const LayerBatch& lb, hipStream_t st);
 hipError_t launch_fetch(const StateBase& s, const FetchBatch& fb, int blocks, int unroll, bool nt, hipStream_t st);
 hipError_t launch_replay_meta(const StateBase& s, const ReplayBatch& rb, hipStream_t st);
@@ -92,6 +97,21 @@ hipError_t launch_attend_mla(const StateBase& s, int layer, const uint16_t* q, i
                              float scale, float* out, float* lse, float* workspace, int ht, int chunk,
                              hipStream_t st);
 hipError_t launch_hbm_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load / store, non-temporal (streamed past the caches) when NT.
+template <bool NT>
+__device__ inline u32x4 ld16(const u32x4* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <bool NT>
+__device__ inline void st16(u32x4* p, u32x4 v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 
 // Record the first device-side data error in the sticky word.
 __device__ inline void record_error(int32_t* err, int code, int layer, int req, int detail) {

@@ -130,13 +130,16 @@ __device__ inline int bucket_find(const PlanLds& l, unsigned nbm, int bucket_bit
     }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: four row shifts
+// scan each row of 16 lanes, then row broadcasts add lane 15's total into
+// rows 1 and 3 and lane 31's into rows 2 and 3.
 __device__ inline int wave_incl_scan(int x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
     return x;
 }
 
@@ -151,6 +154,23 @@ __device__ inline unsigned wave_max(unsigned v) {
     for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<unsigned>(__shfl_xor(static_cast<int>(v), off, 64)));
     return v;
 }
+
+// Sum of words[0 .. n) (n <= 16) of a block scan's per-wave partials, for
+// every lane: lane i < n of the wave reads word i (one LDS read), the first
+// row of 16 lanes adds up with four DPP row shifts, and lane 15 holds the sum.
+static_assert(kPlanWaves == 16, "one row of 16 lanes holds the per-wave partials");
+__device__ inline int sum_before(const int* words, int n) {
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    int v = lane < n ? words[lane & (kPlanWaves - 1)] : 0;
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    return __builtin_amdgcn_readlane(v, 15);
+}
+
+// The workgroup's wave index as a wave-uniform (scalar) value.
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6); }
 
 // Block-wide OR of a small flag word: lanes holding a non-zero value OR it
 // into one LDS word (the word must be zero before; read it after a barrier).
@@ -257,17 +277,14 @@ __device__ inline void hist_add(int* hist, int bin) {
 // the count taken from the top bin downwards first reaches `need`; `below`
 // is the count of the bins above it.  Leaves l.hist zeroed.  Barriers inside.
 __device__ inline void find_crossing_from_top(const PlanLds& l, int need, int& bin, int& below) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int my_bin = kHistBins - 1 - tid;
     const int hb = l.hist[my_bin];
     l.hist[my_bin] = 0;
     const int incl = wave_incl_scan(hb);
     if (lane == 63) l.misc[M_HIST + wave] = incl;
     __syncthreads();
-    int excl = incl - hb;
-#pragma unroll
-    for (int w = 0; w < kPlanWaves; ++w)
-        if (w < wave) excl += l.misc[M_HIST + w];
+    const int excl = incl - hb + sum_before(l.misc + M_HIST, wave);
     if (excl < need && need <= excl + hb) {
         l.misc[M_BIN] = my_bin;
         l.misc[M_BELOW] = excl;
@@ -285,7 +302,7 @@ __device__ inline void find_crossing_from_top(const PlanLds& l, int need, int& b
 template <int PER>
 __device__ inline void radix_select(const PlanLds& l, const uint32_t (&tsv)[PER], unsigned elig, int m,
                                     uint32_t& T, int& need_eq) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     unsigned mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
@@ -334,10 +351,7 @@ __device__ inline void radix_select(const PlanLds& l, const uint32_t (&tsv)[PER]
         const int incl = wave_incl_scan(hb);
         if (lane == 63) l.misc[M_HIST + wave] = incl;
         __syncthreads();
-        int bl = incl - hb;
-#pragma unroll
-        for (int w = 0; w < kPlanWaves; ++w)
-            if (w < wave) bl += l.misc[M_HIST + w];
+        const int bl = incl - hb + sum_before(l.misc + M_HIST, wave);
         if (bl < remaining && remaining <= bl + hb) {
             l.misc[M_BIN] = tid;
             l.misc[M_BELOW] = bl;
@@ -348,6 +362,39 @@ __device__ inline void radix_select(const PlanLds& l, const uint32_t (&tsv)[PER]
     }
     T = mn + static_cast<uint32_t>(prefix);
     need_eq = remaining;
+}
+
+// Copy the m missed rows of one (request, layer) from the host pool into their
+// victim slots: miss i (ascending selection index) is selection j =
+// l.mlist[i], whose position l.sel[j] goes to slot -2 - l.sidx[j].  Each lane
+// keeps four 16-byte host loads in flight.
+template <bool NT>
+__device__ inline void copy_misses(const StateBase& s, const PlanLds& l, int64_t rl, int r, int layer, int m) {
+    constexpr int U = 4;
+    const int row16 = static_cast<int>(s.row_bytes >> 4);
+    const int total = m * row16;
+    const uint8_t* src_base = s.pool + s.region_row[static_cast<int64_t>(r) * s.NL + layer] * s.row_bytes;
+    uint8_t* dst_base = s.cache + rl * s.B * s.row_bytes;
+    for (int c0 = threadIdx.x; c0 < total; c0 += kPlanThreads * U) {
+        u32x4 v[U];
+        u32x4* dst[U];
+#pragma unroll
+        for (int x = 0; x < U; ++x) {
+            const int c = c0 + x * kPlanThreads;
+            dst[x] = nullptr;
+            if (c < total) {
+                const int i = c / row16, off = c - i * row16;
+                const int j = l.mlist[i];
+                const int slot = -2 - l.sidx[j];
+                const u32x4* src = reinterpret_cast<const u32x4*>(src_base + static_cast<int64_t>(l.sel[j]) * s.row_bytes) + off;
+                dst[x] = reinterpret_cast<u32x4*>(dst_base + static_cast<int64_t>(slot) * s.row_bytes) + off;
+                v[x] = ld16<NT>(src);
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < U; ++x)
+            if (dst[x]) st16<NT>(dst[x], v[x]);
+    }
 }
 
 // The metadata half of RESOLVE for one (request, layer).
@@ -380,7 +427,7 @@ __global__ __launch_bounds__(kPlanThreads) __attribute__((amdgpu_waves_per_eu(WI
 void plan_kernel(StateBase s, LayerBatch lb) {
     constexpr bool SCAN = PROBE != PROBE_TABLE;
     extern __shared__ int lds_raw[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int r = blockIdx.x;
     const int layer = lb.layer[blockIdx.y];
     const int k = lb.k, B = s.B, H = 1 << lb.hash_bits;
@@ -523,10 +570,7 @@ void plan_kernel(StateBase s, LayerBatch lb) {
         if (lane == 63) l.misc[M_RANK + wave] = incl;
         __syncthreads();
         HS_PHASE(11);
-        int base = incl - cnt;
-#pragma unroll
-        for (int w = 0; w < kPlanWaves; ++w)
-            if (w < wave) base += l.misc[M_RANK + w];
+        int base = incl - cnt + sum_before(l.misc + M_RANK, wave);
         for (int i = 0; i < gpl; ++i) {
             if (g0 + i < ng) {
                 const uint4 v = pb4[g0 + i];
@@ -604,13 +648,8 @@ void plan_kernel(StateBase s, LayerBatch lb) {
     }
     if (lane == 0) l.misc[M_MISS + wave] = mtot;
     __syncthreads();
-    int m = 0, base = mpre;
-#pragma unroll
-    for (int w = 0; w < kPlanWaves; ++w) {
-        const int c = l.misc[M_MISS + w];
-        m += c;
-        if (w < wave) base += c;
-    }
+    const int m = sum_before(l.misc + M_MISS, kPlanWaves);
+    int base = mpre + sum_before(l.misc + M_MISS, wave);
 #pragma unroll
     for (int q = 0; q < kMaxSelPerLane; ++q)
         if ((mflags >> q) & 1u) l.mlist[base++] = j0 + q;
@@ -701,14 +740,8 @@ void plan_kernel(StateBase s, LayerBatch lb) {
             l.misc[M_TIE + wave] = ttot;
         }
         __syncthreads();
-        int sb = spre, tb = tpre;
-#pragma unroll
-        for (int w = 0; w < kPlanWaves; ++w) {
-            if (w < wave) {
-                sb += l.misc[M_STRICT + w];
-                tb += l.misc[M_TIE + w];
-            }
-        }
+        int sb = spre + sum_before(l.misc + M_STRICT, wave);
+        int tb = tpre + sum_before(l.misc + M_TIE, wave);
         HS_PHASE(7);
         // 5. assignment and metadata update
         bool any_victim = false;
@@ -768,6 +801,16 @@ void plan_kernel(StateBase s, LayerBatch lb) {
         atomicAdd(st + 1, static_cast<unsigned long long>(m));
         atomicAdd(st + 2, static_cast<unsigned long long>(m) * static_cast<unsigned long long>(s.row_bytes));
         atomicAdd(st + 3, 1ull);
+    }
+    if constexpr (WIDE) {
+        // a wide launch copies its own misses: with hundreds of workgroups
+        // copying at once the link is as busy as under the chip-wide fetch
+        // kernel, and the launch after it is saved.  Same flat (row, 16-byte
+        // piece) order as the fetch kernel; l.sidx and l.sel are final here.
+        if (lb.copy && m > 0) {
+            if (lb.nt) copy_misses<true>(s, l, rl, r, layer, m);
+            else copy_misses<false>(s, l, rl, r, layer, m);
+        }
     }
     HS_PHASE(10);
     HS_PHASE_FLUSH();
@@ -942,10 +985,20 @@ static hipError_t launch_plan_p(const StateBase& s, const LayerBatch& lb, size_t
     }
 }
 
+static bool plan_is_wide(const StateBase& s, int n) {
+    // enough units that two per CU matter: more than one workgroup per CU
+    return static_cast<int64_t>(s.R) * n > 256;
+}
+
+bool plan_copies_misses(const StateBase& s, int n) {
+    // (rows up to 8 MB keep the copy's piece index inside 32 bits)
+    return plan_is_wide(s, n) && s.row_bytes <= (static_cast<int64_t>(1) << 23);
+}
+
 hipError_t launch_plan(const StateBase& s, const LayerBatch& lb_in, hipStream_t st) {
     LayerBatch lb = lb_in;
-    // enough units that two per CU matter: more than one workgroup per CU
-    const bool wide = static_cast<int64_t>(s.R) * lb.n > 256;
+    const bool wide = plan_is_wide(s, lb.n);
+    lb.copy = plan_copies_misses(s, lb.n) ? 1 : 0;
     const int H = 1 << lb.hash_bits;
     int probe = PROBE_TABLE;
     lb.lk_half = H;

@@ -119,7 +119,10 @@ int hisparse_create(int num_req, int num_layers, int B, int W_KV, int dtype, con
 int hisparse_resolve(hisparse_t h, int layer, const int32_t* d_sel, int k, int32_t* d_slot_idx, void* stream);
 
 /* RESOLVE several independent layers in one pair of launches (async).
- * d_sel_ptrs and d_slot_idx_ptrs are host arrays of n device pointers. */
+ * d_sel_ptrs and d_slot_idx_ptrs are host arrays of n device pointers.  When
+ * num_req * n exceeds 256 the metadata kernel copies each request-layer's
+ * misses itself and no fetch launch follows (HS_OPT_FETCH_BLOCKS and
+ * HS_OPT_FETCH_UNROLL then do not apply). */
 int hisparse_resolve_layers(hisparse_t h, int n, const int* layers, const int32_t* const* d_sel_ptrs, int k,
                             int32_t* const* d_slot_idx_ptrs, void* stream);
 

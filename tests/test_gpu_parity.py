@@ -299,8 +299,8 @@ def test_victims_older_than_histogram_range(hs):
 @pytest.mark.parametrize("probe", ["page_table", "bitmap", "hash"])
 def test_batched_launch_over_many_units(hs, probe):
     """One launch over 512 (request, layer) units (the build held to two
-    workgroups per CU) against the oracle, with misses and all-hit steps,
-    with each probe."""
+    workgroups per CU, which copies its own misses) against the oracle, with
+    misses and all-hit steps, with each probe."""
     from oracle import Oracle
     w = tg.Workload("batched_wide", 64, 8, 8192, 8, 2, 256, 512, 6, tg.LOCALITY, 0.85, seed_index=95)
     tr = tg.trace(w)
@@ -324,6 +324,39 @@ def test_batched_launch_over_many_units(hs, probe):
         st = res.state(w.num_layers - 1)
         assert np.array_equal(st["ts"], o.ts[w.num_layers - 1])
         assert np.array_equal(st["slot_pos"], o.slot_pos[w.num_layers - 1])
+        for l in layers:
+            # the wide launch copies its own misses: bytes of occupied slots
+            occ = o.slot_pos[l] >= 0
+            assert np.array_equal(res.cache_layer(l)[occ], o.cache[l][occ]), f"cache bytes step {t} layer {l}"
+    assert res.error()[0] == 0
+    res.close()
+    pool.free()
+
+
+def test_wide_launch_copies_multi_piece_rows(hs):
+    """A wide launch (40 requests x 8 layers) with 1152-byte records: the
+    metadata kernel's own copy moves 72 pieces of 16 bytes per miss, bytes
+    checked against the oracle's cache model on every step."""
+    from oracle import Oracle
+    w = tg.Workload("wide_rows", 40, 8, 2048, 576, 2, 256, 512, 5, tg.LOCALITY, 0.8, seed_index=96)
+    print(f"[parity] {w.name} R={w.num_req} L={w.num_layers} B={w.B} k={w.k} row={w.row_bytes}", flush=True)
+    tr = tg.trace(w)
+    pool = make_pool(hs, w)
+    pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
+    res = make_resolver(hs, w, pool)
+    o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes)
+    dev = torch.device("cuda:0")
+    layers = list(range(w.num_layers))
+    sel = torch.from_numpy(tr).to(dev)
+    out = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
+    for t in range(w.steps):
+        res.resolve_layers(layers, [sel[t, l] for l in layers], [out[l] for l in layers])
+        torch.cuda.synchronize()
+        for l in layers:
+            ref = o.resolve(l, tr[t, l], pool_np, w.region_rows())
+            assert np.array_equal(out[l].cpu().numpy(), ref["slot_idx"]), f"step {t} layer {l}"
+            occ = o.slot_pos[l] >= 0
+            assert np.array_equal(res.cache_layer(l)[occ], o.cache[l][occ]), f"cache bytes step {t} layer {l}"
     assert res.error()[0] == 0
     res.close()
     pool.free()
