@@ -80,6 +80,8 @@ def parse():
                          "workloads get MLA attention when the records are 576-element bf16 latents, else the "
                          "gather checksum; other workloads none)")
     ap.add_argument("--heads", type=int, default=128, help="query heads of the MLA attention consumer")
+    ap.add_argument("--attn-heads-per-wg", type=int, default=0, choices=[0, 32, 64],
+                    help="heads per attention workgroup (0: the library chooses by shape)")
     ap.add_argument("--no-attention-leg", action="store_true",
                     help="skip the separate timing of the MLA attention consumer on the workload's shape")
     ap.add_argument("--hit-only-workload", default="gqa_record",
@@ -125,6 +127,8 @@ def main():
     if args.probe != "default":
         res.set_option(hs.HS_OPT_PROBE, {"page_table": hs.HS_PROBE_PAGE_TABLE, "slot_scan": hs.HS_PROBE_SLOT_SCAN,
                                          "slot_scan_hash": hs.HS_PROBE_SLOT_SCAN_HASH}[args.probe])
+    if args.attn_heads_per_wg:
+        res.set_option(hs.HS_OPT_ATTN_HEADS, args.attn_heads_per_wg)
     if args.fetch_blocks:
         res.set_option(hs.HS_OPT_FETCH_BLOCKS, args.fetch_blocks)
     if args.unroll:
@@ -315,8 +319,9 @@ def main():
             "peak": link_peak,
             "unit": "GB/s",
             "frac": achieved / link_peak,
-            "traffic": (fetch_traffic() or {}).get("total_bytes"),
-            "traffic_detail": fetch_traffic(),
+            # the counters were taken on mla_latent's launches: no figure for other workloads
+            "traffic": (fetch_traffic() or {}).get("total_bytes") if w.name == "mla_latent" else None,
+            "traffic_detail": fetch_traffic() if w.name == "mla_latent" else None,
             "peak_note": "peak = max(SDMA H2D copy, 16 B-load streaming kernel) measured in this run; "
                          f"published PCIe 5.0 x16 = {PCIE5_X16_GBPS} GB/s per direction",
             "avg_launch_ms": fetch_avg_ms,
@@ -338,7 +343,8 @@ def main():
         log(f"fetch avg {fetch_avg_ms * 1e3:.1f} us ({achieved:.1f} GB/s), plan avg {plan_avg_ms * 1e3:.1f} us")
 
     if not args.no_attention_leg and mla_records:
-        result["attention"] = attention_leg(hs, torch, res, w, out, args.heads, dev, hbm_peak)
+        result["attention"] = attention_leg(hs, torch, res, w, out, args.heads, dev, hbm_peak,
+                                            heads_per_wg=args.attn_heads_per_wg)
 
     res.close()
 
@@ -362,7 +368,7 @@ def attention_buffers(torch, w, heads, dev):
             "lse": torch.empty((w.num_req, heads), dtype=torch.float32, device=dev)}
 
 
-def attention_leg(hs, torch, res, w, out, heads, dev, hbm_peak, iters=20):
+def attention_leg(hs, torch, res, w, out, heads, dev, hbm_peak, iters=20, heads_per_wg=0):
     """The consumer alone: sparse MLA decode attention over the slots the last
     timed step published, every layer, timed with HIP events on the stream
     the kernels run on.  Algorithmic work per (request, layer): k records of
@@ -387,6 +393,7 @@ def attention_leg(hs, torch, res, w, out, heads, dev, hbm_peak, iters=20):
     gbps = io_bytes / (us * 1e-6) / 1e9
     log(f"attention: {us:.1f} us per layer ({tflops:.0f} TFLOP/s, {gbps:.0f} GB/s of records+q+out)")
     return {"kernels": "mla_partial_kernel + mla_combine_kernel", "heads": heads, "k": w.k,
+            "heads_per_workgroup": heads_per_wg or "by shape",
             "requests": w.num_req, "us_per_layer": us, "TFLOPs": tflops,
             "mfma_frac": tflops / MFMA_BF16_TFLOPS, "algorithmic_GBps": gbps,
             "hbm_frac_published": gbps / HBM_PEAK_GBPS,

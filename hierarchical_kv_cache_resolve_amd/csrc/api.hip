@@ -29,6 +29,7 @@ struct hisparse_ctx {
     bool nt = true;
     bool timing = false;
     int probe = HS_PROBE_SLOT_SCAN;
+    int attn_heads = 0;  // heads per attention workgroup: 0 = by shape, 32 or 64
     float* attn_ws = nullptr;       // consumer workspace (partials per chunk)
     size_t attn_ws_floats = 0;
     // ordering of resolve / prefetch (host-side bookkeeping only)
@@ -564,6 +565,10 @@ int hisparse_set_option(hisparse_t h, int key, int64_t value) {
         case HS_OPT_NT_LOADS:
             h->nt = value != 0;
             return HS_OK;
+        case HS_OPT_ATTN_HEADS:
+            if (value != 0 && value != 32 && value != 64) return HS_E_INVAL;
+            h->attn_heads = static_cast<int>(value);
+            return HS_OK;
         case HS_OPT_PHASE_TRACE:
             if (value && !h->s.phase) {
                 const size_t n = static_cast<size_t>(h->R) * h->NL * hs::kPhaseSlots;
@@ -681,7 +686,7 @@ int hisparse_attend_mla(hisparse_t h, int layer, const void* d_q, int num_heads,
         return HS_E_INVAL;
     if (h->dtype != HS_BF16 || h->W_KV != 576) return HS_E_INVAL;
     if (k < 1 || k > h->B) return HS_E_K;
-    const int ht = hs::attend_head_tiles(h->R, num_heads, k);
+    const int ht = h->attn_heads ? h->attn_heads / 16 : hs::attend_head_tiles(h->R, num_heads, k);
     const int chunk = hs::attend_chunk(h->R, num_heads, k, ht);
     const int nchunk = (k + chunk - 1) / chunk;
     const size_t need = hs::attend_workspace_floats(h->R, num_heads, nchunk);

@@ -440,10 +440,10 @@ int attend_chunk(int R, int H, int k, int ht) {
 int attend_head_tiles(int R, int H, int k) {
     // 64 heads per workgroup read each record into the fewest workgroups; when
     // that leaves few records per workgroup, so that the split over records is
-    // deep (eight chunks or more), the fp32 partials it writes and reads back
+    // deep (sixteen chunks or more), the fp32 partials it writes and reads back
     // cost more than the extra record reads of 32 heads per workgroup
     const int c4 = attend_chunk(R, H, k, 4);
-    return (k + c4 - 1) / c4 >= 8 ? 2 : 4;
+    return (k + c4 - 1) / c4 >= 16 ? 2 : 4;
 }
 
 hipError_t launch_attend_mla(const StateBase& s, int layer, const uint16_t* q, int H, const int32_t* slot_idx, int k,

@@ -213,6 +213,8 @@ int hisparse_reset(hisparse_t h);
                                 /*   HBM bytes): a bitmap over the history's positions with       */
                                 /*   per-word ranks when it fits the LDS, else a hash             */
 #define HS_PROBE_SLOT_SCAN_HASH 2 /* the slot scan with the LDS hash whatever the history length */
+#define HS_OPT_ATTN_HEADS 7     /* heads per workgroup of hisparse_attend_mla: 32 or 64, or 0 to */
+                                /* choose by shape (default)                                      */
 int hisparse_set_option(hisparse_t h, int key, int64_t value);
 
 /* Per-kernel times of launches issued while HS_OPT_TIMING was on, measured

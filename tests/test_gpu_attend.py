@@ -74,17 +74,17 @@ def run_attend(hs, res, layer, q_np, slot_idx, scale, dev):
     return out, lse
 
 
-def test_attend_after_resolve_ragged(hs):
-    """k from 1 to 1000 (ragged sub-chunks and chunks), 64 and 128 heads, two scales.
-
-    With three requests, k = 513, 777 and 1000 split over eight chunks or more
-    and take the 32-heads-a-workgroup kernel; the other cases take 64 heads a
-    workgroup."""
+@pytest.mark.parametrize("heads_per_wg", [0, 32, 64])
+def test_attend_after_resolve_ragged(hs, heads_per_wg):
+    """k from 1 to 1000 (ragged sub-chunks and chunks), 64 and 128 heads, two
+    scales, with the head grouping chosen by shape and forced to 32 and to 64
+    heads a workgroup."""
     w = tg.Workload("attend", 3, 2, 8192, 576, 2, 1000, 1024, 8, tg.LOCALITY, 0.8, seed_index=61)
     sel_all = tg.trace(w)
     pool = make_pool(hs, w)
     pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
     res = make_resolver(hs, w, pool)
+    res.set_option(hs.HS_OPT_ATTN_HEADS, heads_per_wg)
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(7)
     cases = [(1, 64, 0.0417), (37, 128, 0.25), (64, 64, 0.0417), (65, 128, 0.0417), (200, 64, 0.25),
@@ -96,7 +96,7 @@ def test_attend_after_resolve_ragged(hs):
             res.resolve(l, torch.from_numpy(sel).to(dev), slot_idx)
             res.check_error()
             q_np = rand_bits(rng, (w.num_req, H, D_QK))
-            print(f"attend k={k} H={H} scale={scale} layer={l}", flush=True)
+            print(f"attend k={k} H={H} scale={scale} layer={l} heads/wg={heads_per_wg}", flush=True)
             out, lse = run_attend(hs, res, l, q_np, slot_idx, scale, dev)
             check(hs, q_np, records(w, pool_np, l, sel), scale, out, lse)
 
@@ -168,15 +168,20 @@ def test_attend_rejects_bad_arguments(hs):
     out_many = torch.zeros((1, 1088, D_V), dtype=torch.float32, device=dev)
     with pytest.raises(hs.HisparseError):
         res2.attend_mla(0, q_many, idx, 0.1, out_many)  # more heads than HS_MAX_HEADS
+    with pytest.raises(hs.HisparseError):
+        res2.set_option(hs.HS_OPT_ATTN_HEADS, 48)       # 32 or 64 heads a workgroup, or 0
 
 
-def test_attend_full_size(hs):
-    """16 requests, k = 2048 of a 4096-slot cache, 128 heads: the decode shape of the MLA workload."""
+@pytest.mark.parametrize("heads_per_wg", [0, 32])
+def test_attend_full_size(hs, heads_per_wg):
+    """16 requests, k = 2048 of a 4096-slot cache, 128 heads: the decode shape
+    of the MLA workload (64 heads a workgroup by shape; also forced to 32)."""
     w = tg.Workload("attend_full", 16, 1, 32768, 576, 2, 2048, 4096, 3, tg.LOCALITY, 0.87, seed_index=66)
     sel_all = tg.trace(w)
     pool = make_pool(hs, w)
     pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
     res = make_resolver(hs, w, pool)
+    res.set_option(hs.HS_OPT_ATTN_HEADS, heads_per_wg)
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(10)
     slot_idx = torch.empty((w.num_req, w.k), dtype=torch.int32, device=dev)
