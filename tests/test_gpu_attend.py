@@ -28,6 +28,26 @@ def hs():
     return m
 
 
+_live = []
+
+
+def keep(obj):
+    """Release at the end of the test (resolvers before the pools they use)."""
+    _live.append(obj)
+    return obj
+
+
+@pytest.fixture(autouse=True)
+def _release_after_test():
+    yield
+    while _live:
+        obj = _live.pop()
+        if hasattr(obj, "close"):
+            obj.close()
+        else:
+            obj.free()
+
+
 def rand_bits(rng, shape):
     x = rng.standard_normal(shape).astype(np.float32)
     u = x.view(np.uint32)
@@ -81,9 +101,9 @@ def test_attend_after_resolve_ragged(hs, heads_per_wg):
     heads a workgroup."""
     w = tg.Workload("attend", 3, 2, 8192, 576, 2, 1000, 1024, 8, tg.LOCALITY, 0.8, seed_index=61)
     sel_all = tg.trace(w)
-    pool = make_pool(hs, w)
+    pool = keep(make_pool(hs, w))
     pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
-    res = make_resolver(hs, w, pool)
+    res = keep(make_resolver(hs, w, pool))
     res.set_option(hs.HS_OPT_ATTN_HEADS, heads_per_wg)
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(7)
@@ -105,9 +125,9 @@ def test_attend_skips_unpublished_slots(hs):
     """Slots of -1 are left out; a request with none gives zeros and -inf."""
     w = tg.Workload("attend_holes", 4, 1, 4096, 576, 2, 300, 512, 1, tg.UNIFORM, 0.0, seed_index=62)
     sel = np.ascontiguousarray(tg.trace(w)[0, 0])
-    pool = make_pool(hs, w)
+    pool = keep(make_pool(hs, w))
     pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
-    res = make_resolver(hs, w, pool)
+    res = keep(make_resolver(hs, w, pool))
     dev = torch.device("cuda:0")
     slot_idx = torch.empty((w.num_req, w.k), dtype=torch.int32, device=dev)
     res.resolve(0, torch.from_numpy(sel).to(dev), slot_idx)
@@ -130,9 +150,9 @@ def test_attend_rejected_request(hs):
     w = tg.Workload("attend_rej", 2, 1, 4096, 576, 2, 128, 256, 1, tg.UNIFORM, 0.0, seed_index=63)
     sel = np.ascontiguousarray(tg.trace(w)[0, 0])
     sel[1, 5] = sel[1, 9]
-    pool = make_pool(hs, w)
+    pool = keep(make_pool(hs, w))
     pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
-    res = make_resolver(hs, w, pool)
+    res = keep(make_resolver(hs, w, pool))
     dev = torch.device("cuda:0")
     slot_idx = torch.empty((w.num_req, w.k), dtype=torch.int32, device=dev)
     res.resolve(0, torch.from_numpy(sel).to(dev), slot_idx)
@@ -149,8 +169,8 @@ def test_attend_rejected_request(hs):
 
 def test_attend_rejects_bad_arguments(hs):
     w = tg.Workload("attend_args", 1, 1, 1024, 64, 2, 16, 32, 1, seed_index=64)
-    pool = make_pool(hs, w)
-    res = make_resolver(hs, w, pool)
+    pool = keep(make_pool(hs, w))
+    res = keep(make_resolver(hs, w, pool))
     dev = torch.device("cuda:0")
     q = torch.zeros((1, 64, D_QK), dtype=torch.int16, device=dev)
     idx = torch.zeros((1, 16), dtype=torch.int32, device=dev)
@@ -158,8 +178,8 @@ def test_attend_rejects_bad_arguments(hs):
     with pytest.raises(hs.HisparseError):
         res.attend_mla(0, q, idx, 0.1, out)     # records of 64 elements are not MLA records
     w2 = tg.Workload("attend_args2", 1, 1, 1024, 576, 2, 16, 32, 1, seed_index=65)
-    pool2 = make_pool(hs, w2)
-    res2 = make_resolver(hs, w2, pool2)
+    pool2 = keep(make_pool(hs, w2))
+    res2 = keep(make_resolver(hs, w2, pool2))
     with pytest.raises(hs.HisparseError):
         res2.attend_mla(0, q[:, :32].contiguous(), idx, 0.1, out)   # heads not a multiple of 64
     with pytest.raises(hs.HisparseError):
@@ -178,9 +198,9 @@ def test_attend_full_size(hs, heads_per_wg):
     of the MLA workload (64 heads a workgroup by shape; also forced to 32)."""
     w = tg.Workload("attend_full", 16, 1, 32768, 576, 2, 2048, 4096, 3, tg.LOCALITY, 0.87, seed_index=66)
     sel_all = tg.trace(w)
-    pool = make_pool(hs, w)
+    pool = keep(make_pool(hs, w))
     pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
-    res = make_resolver(hs, w, pool)
+    res = keep(make_resolver(hs, w, pool))
     res.set_option(hs.HS_OPT_ATTN_HEADS, heads_per_wg)
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(10)
@@ -239,8 +259,8 @@ def test_attend_in_a_captured_graph(hs):
         res.check_error()
         return outs
 
-    pool = make_pool(hs, w)
-    eager = run(make_resolver(hs, w, pool), False)
-    graph = run(make_resolver(hs, w, pool), True)
+    pool = keep(make_pool(hs, w))
+    eager = run(keep(make_resolver(hs, w, pool)), False)
+    graph = run(keep(make_resolver(hs, w, pool)), True)
     for t, ((oe, le), (og, lg)) in enumerate(zip(eager, graph)):
         assert torch.equal(oe, og) and torch.equal(le, lg), f"step {t}"

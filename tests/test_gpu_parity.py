@@ -90,6 +90,10 @@ RAGGED = [
     wl("gqa_row", W_KV=2048, B=600, k=300, L_ctx=3000, steps=8),
     wl("many_requests", num_req=64, num_layers=1, B=256, k=128, L_ctx=4000, W_KV=8, steps=10),
     wl("hit_only", mode=tg.HITONLY, p_keep=1.0, steps=6),
+    # a history too long for the position bitmap in LDS: the slot scan falls back to the hash
+    wl("long_ctx_hash_fallback", L_ctx=1_000_000, B=300, k=150, W_KV=8, num_req=2, num_layers=1, steps=8),
+    # a history length that is not a multiple of the bitmap's 128-position groups
+    wl("ctx_not_mult128", L_ctx=4101, B=700, k=300, W_KV=8, steps=10),
 ]
 
 
