@@ -42,7 +42,7 @@ enum : int {
     M_HIST = 82,     // [16] histogram-scan wave totals
     M_BIN = 98,      // crossing bin of the current radix pass
     M_BELOW = 99,    // candidates below the crossing bin
-    M_RANK = 100,    // [16] selected positions per wave's run of bitmap words
+    M_RANK = 100,    // first rank not yet handed to a wave (bitmap probe)
 };
 
 // How the slot-scan probe maps a cached position to its selection index.
@@ -244,7 +244,7 @@ __device__ inline void reject(const StateBase& s, int32_t* out, int k, int64_t r
 // global store that a later barrier would have to wait for.  Slots: 0 start,
 // 1 global reads issued and LDS cleared, 2 selection inserted, 3 probe done,
 // 4 miss list, 5-8 victim stages, 9 metadata written, 10 published; the
-// bitmap probe also stamps 11 word counts, 12 ranks, 13 rank -> selection map.
+// bitmap probe also stamps 11 word counts and 12 ranks.
 #define HS_PHASE(i)                                          \
     do {                                                     \
         if (s.phase != nullptr) stamp[(i)] = wall_clock64(); \
@@ -252,7 +252,7 @@ __device__ inline void reject(const StateBase& s, int32_t* out, int k, int64_t r
 #define HS_PHASE_FLUSH()                                                                \
     do {                                                                                \
         if (s.phase != nullptr && tid == 0)                                             \
-            for (int i_ = 0; i_ < 14; ++i_) s.phase[rl * kPhaseSlots + i_] = stamp[i_]; \
+            for (int i_ = 0; i_ < 13; ++i_) s.phase[rl * kPhaseSlots + i_] = stamp[i_]; \
     } while (0)
 
 constexpr int kMaxSelPerLane = HS_MAX_K / kPlanThreads;  // 4
@@ -444,7 +444,7 @@ void plan_kernel(StateBase s, LayerBatch lb) {
     unsigned* const pbits = reinterpret_cast<unsigned*>(l.bkey);
     int* const prank = l.bval;
     const unsigned long long lt = lanemask_lt();
-    unsigned long long stamp[14] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    unsigned long long stamp[13] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     HS_PHASE(0);
 
     // 1. global reads
@@ -489,7 +489,9 @@ void plan_kernel(StateBase s, LayerBatch lb) {
     } else {
         for (int i = tid; i < H; i += kPlanThreads) l.bkey[i] = kEmpty;
     }
-    if constexpr (SCAN) {
+    if constexpr (PROBE == PROBE_BITMAP) {
+        for (int j = tid; j < k; j += kPlanThreads) l.mlist[j] = -1;  // slot by rank
+    } else if constexpr (PROBE == PROBE_HASH) {
         for (int j = tid; j < k; j += kPlanThreads) l.sidx[j] = -1;
     } else {
         for (int i = tid; i < hitmap_words(B); i += kPlanThreads) l.hitmap[i] = 0u;
@@ -567,10 +569,14 @@ void plan_kernel(StateBase s, LayerBatch lb) {
             }
         }
         const int incl = wave_incl_scan(cnt);
-        if (lane == 63) l.misc[M_RANK + wave] = incl;
-        __syncthreads();
+        // each wave takes a run of ranks with one LDS atomic: whatever order
+        // the waves' adds land in, the k selected positions map one to one
+        // onto [0, k) (ascending within a wave's words), and no barrier is
+        // needed before the ranks are written
+        int wbase = 0;
+        if (lane == 63) wbase = atomicAdd(&l.misc[M_RANK], incl);
+        int base = __builtin_amdgcn_readlane(wbase, 63) + incl - cnt;
         HS_PHASE(11);
-        int base = incl - cnt + sum_before(l.misc + M_RANK, wave);
         for (int i = 0; i < gpl; ++i) {
             if (g0 + i < ng) {
                 const uint4 v = pb4[g0 + i];
@@ -585,26 +591,16 @@ void plan_kernel(StateBase s, LayerBatch lb) {
         }
         __syncthreads();
         HS_PHASE(12);
-        // selection index of each rank (the miss list's storage, not yet in use)
-#pragma unroll
-        for (int q = 0; q < kMaxSelPerLane; ++q) {
-            const int j = tid + q * kPlanThreads;
-            if (j < k) {
-                const int p = selv[q];
-                const unsigned below = (1u << (p & 31)) - 1u;
-                l.mlist[prank[p >> 5] + __popc(pbits[p >> 5] & below)] = j;
-            }
-        }
-        __syncthreads();
-        HS_PHASE(13);
+        // each cached slot holding a selected position records itself at the
+        // position's rank (slot by rank, in the miss list's storage, cleared
+        // to -1 at the start); the miss list maps ranks back to selections
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
             const int p = spos[q];
             if (s0 + q < B && p >= 0 && p < s.L_ctx) {
                 const unsigned word = pbits[p >> 5];
                 if ((word >> (p & 31)) & 1u) {
-                    const int j = l.mlist[prank[p >> 5] + __popc(word & ((1u << (p & 31)) - 1u))];
-                    l.sidx[j] = s0 + q;
+                    l.mlist[prank[p >> 5] + __popc(word & ((1u << (p & 31)) - 1u))] = s0 + q;
                     hitbits |= 1u << q;
                 }
             }
@@ -639,7 +635,21 @@ void plan_kernel(StateBase s, LayerBatch lb) {
     for (int q = 0; q < kMaxSelPerLane; ++q) {
         if (q < kper) {
             const int j = j0 + q;
-            const bool f = j < k && l.sidx[j] < 0;
+            bool f;
+            if constexpr (PROBE == PROBE_BITMAP) {
+                // the slot recorded at this selection's rank, or -1 (a miss);
+                // the slot-by-rank array is overwritten by the miss list only
+                // after the barrier below
+                f = false;
+                if (j < k) {
+                    const int p = l.sel[j];
+                    const int v = l.mlist[prank[p >> 5] + __popc(pbits[p >> 5] & ((1u << (p & 31)) - 1u))];
+                    l.sidx[j] = v;
+                    f = v < 0;
+                }
+            } else {
+                f = j < k && l.sidx[j] < 0;
+            }
             mflags |= static_cast<unsigned>(f) << q;
             const unsigned long long bm = __ballot(f);
             mpre += __popcll(bm & lt);
