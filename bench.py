@@ -353,6 +353,8 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(tg, w, tr, pool, W, args.cpu_seconds)
+        result["cpu_baseline_threads"] = cpu_baseline_threads(tg, w, tr, pool, W,
+                                                              result["cpu_baseline"]["steps"])
 
     pool.free()
     print(json.dumps(result), flush=True)
@@ -519,7 +521,51 @@ def cpu_baseline(tg, w, tr, pool, warm_steps, seconds):
     return {"value": sels / spent, "unit": "selections/s", "cores": 1, "kind": "oracle",
             "sample": f"steps {warm_steps}..{warm_steps + n_steps - 1} of {w.name} (all {w.num_req} requests x "
                       f"{w.num_layers} layers, miss rows copied from the same pinned pool), after "
-                      f"{warm_steps} untimed warm steps; single thread"}
+                      f"{warm_steps} untimed warm steps; single thread",
+            "steps": n_steps, "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline_threads(tg, w, tr, pool, warm_steps, n_steps):
+    """The same oracle sample with one thread per layer (layers are independent
+    and the oracle keeps no state shared between them; its calls release the
+    interpreter lock), wall clock around all threads."""
+    import threading
+    from oracle import Oracle
+    pool_np = pool.numpy_view()
+    rr = w.region_rows()
+    o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes, model_bytes=True)
+
+    def run_layer(l, t0, t1):
+        for t in range(t0, t1):
+            o.resolve(l, tr[t, l], pool_np, rr)
+
+    def run_all(t0, t1):
+        th = [threading.Thread(target=run_layer, args=(l, t0, t1)) for l in range(w.num_layers)]
+        for x in th:
+            x.start()
+        for x in th:
+            x.join()
+
+    run_all(0, warm_steps)
+    t0 = time.perf_counter()
+    run_all(warm_steps, warm_steps + n_steps)
+    spent = time.perf_counter() - t0
+    o.close()
+    sels = n_steps * w.num_layers * w.num_req * w.k
+    log(f"cpu oracle, {w.num_layers} threads: {n_steps} steps in {spent:.1f}s -> {sels / spent / 1e6:.2f} M sel/s")
+    return {"value": sels / spent, "unit": "selections/s", "cores": w.num_layers, "kind": "oracle",
+            "sample": f"the single-thread sample, one thread per layer", "cpu_model": cpu_model(),
+            "host_cpus": os.cpu_count()}
 
 
 if __name__ == "__main__":
