@@ -3,6 +3,8 @@ import ctypes
 import os
 import re
 
+import pytest
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
@@ -80,3 +82,18 @@ def test_binding_refuses_tensors_the_kernels_would_overrun():
         hs._dev_arg(FakeDev(50, 2), 100, 4, "x")        # wrong element size
     with pytest.raises(ValueError):
         hs._dev_arg(FakeDev(25, 4, contiguous=False), 100, 4, "x")
+
+
+def test_binding_constants_match_the_header():
+    """Every numeric HS_* constant of include/hisparse.h that the binding
+    names has the header's value, and every option and probe constant is named."""
+    import re
+    hs = pytest.importorskip("hierarchical_kv_cache_resolve_amd")
+    text = open(os.path.join(ROOT, "include", "hisparse.h")).read()
+    defs = dict(re.findall(r"#define\s+(HS_[A-Z0-9_]+)\s+\(?(-?\d+)\)?", text))
+    assert defs, "no constants parsed"
+    for name, val in defs.items():
+        if name.startswith(("HS_OPT_", "HS_PROBE_")):
+            assert hasattr(hs, name), f"binding lacks {name}"
+        if hasattr(hs, name):
+            assert getattr(hs, name) == int(val), f"{name}: binding {getattr(hs, name)} != header {val}"
