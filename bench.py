@@ -93,7 +93,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the RESOLVE path shards by "
-              "(request, layer) with no exchange, and this build measures one GPU's share.", flush=True)
+              "(request, layer) with no exchange, and this benchmark measures one GPU's share.", flush=True)
         sys.exit(2)
     import torch
 
