@@ -418,10 +418,12 @@ def hit_only_leg(hs, tg, torch, w, dev, sptr, hbm_peak, steps=64):
     out = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
     for l in range(w.num_layers):
         res.resolve(l, tr[0, l], out[l], sptr)
-    # algorithmic bytes per (request, layer) of an all-hit resolve: read the
-    # selection (4k), the page-table entries it names (4k) and the slot map
-    # (4B); write the hit stamps (4k) and the published slots (4k)
-    per_rl = 4 * w.k + 4 * w.k + 4 * w.B + 4 * w.k + 4 * w.k
+    # algorithmic bytes per (request, layer) of an all-hit resolve with the
+    # slot scan (the default probe): read the selection (4k) and the slot map
+    # (4B); write the hit stamps (4k) and the published slots (4k).  The
+    # page-table probe also reads the k page-table entries the selection names.
+    per_rl = 4 * w.k + 4 * w.B + 4 * w.k + 4 * w.k
+    per_rl_pt = per_rl + 4 * w.k
     layers = list(range(w.num_layers))
     nb = max(1, min(len(layers), 8192 // w.num_req, 32))  # layers per batched launch
     batches = [layers[i:i + nb] for i in range(0, len(layers), nb)]
@@ -470,14 +472,16 @@ def hit_only_leg(hs, tg, torch, w, dev, sptr, hbm_peak, steps=64):
     res.close()
     pool.free()
     total = per_rl * w.num_req * w.num_layers * steps
+    total_pt = per_rl_pt * w.num_req * w.num_layers * steps
     r = {
         "workload": f"{w.name} shapes: {w.num_req} requests x {w.num_layers} layers, k={w.k}, B={w.B}",
         "bytes_per_request_layer": per_rl,
+        "bytes_per_request_layer_page_table_probe": per_rl_pt,
         "per_layer_launch_GBps": total / per_layer / 1e9,
         "per_layer_resolve_us": per_layer / (steps * w.num_layers) * 1e6,
         "batched_all_layers_GBps": total / batched / 1e9,
         "batched_step_us": batched / steps * 1e6,
-        "batched_page_table_GBps": total / batched_pt / 1e9,
+        "batched_page_table_GBps": total_pt / batched_pt / 1e9,
         "batched_page_table_step_us": batched_pt / steps * 1e6,
         "batched_launches_per_step": len(batches),
         "hbm_peak_GBps": hbm_peak,
