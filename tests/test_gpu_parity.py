@@ -337,12 +337,21 @@ def test_batched_launch_over_many_units(hs, probe):
     pool.free()
 
 
-def test_wide_launch_copies_multi_piece_rows(hs):
-    """A wide launch (40 requests x 8 layers) with 1152-byte records: the
-    metadata kernel's own copy moves 72 pieces of 16 bytes per miss, bytes
-    checked against the oracle's cache model on every step."""
+WIDE_SHAPES = [
+    tg.Workload("wide_rows", 40, 8, 2048, 576, 2, 256, 512, 5, tg.LOCALITY, 0.8, seed_index=96),
+    # B not a multiple of 4 (scalar slot runs), one slot a lane, ragged history length
+    tg.Workload("wide_ragged", 40, 8, 2001, 72, 2, 150, 301, 5, tg.LOCALITY, 0.8, seed_index=97),
+]
+
+
+@pytest.mark.parametrize("w", WIDE_SHAPES, ids=[w.name for w in WIDE_SHAPES])
+def test_wide_launch_copies_multi_piece_rows(hs, w):
+    """Wide launches (40 requests x 8 layers): the metadata kernel's own copy
+    moves every piece of each missed record, bytes checked against the
+    oracle's cache model on every step.  On step 2 two request-layers are
+    rejected (a repeated position, a position past the history); they copy
+    nothing and keep their state, the others resolve as usual."""
     from oracle import Oracle
-    w = tg.Workload("wide_rows", 40, 8, 2048, 576, 2, 256, 512, 5, tg.LOCALITY, 0.8, seed_index=96)
     print(f"[parity] {w.name} R={w.num_req} L={w.num_layers} B={w.B} k={w.k} row={w.row_bytes}", flush=True)
     tr = tg.trace(w)
     pool = make_pool(hs, w)
@@ -351,8 +360,11 @@ def test_wide_launch_copies_multi_piece_rows(hs):
     o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes)
     dev = torch.device("cuda:0")
     layers = list(range(w.num_layers))
-    sel = torch.from_numpy(tr).to(dev)
     out = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
+    tr = tr.copy()
+    tr[2, 3, 7, 5] = tr[2, 3, 7, 9]        # layer 3, request 7: repeated position
+    tr[2, 6, 30, 0] = w.L_ctx              # layer 6, request 30: outside the history
+    sel = torch.from_numpy(tr).to(dev)
     for t in range(w.steps):
         res.resolve_layers(layers, [sel[t, l] for l in layers], [out[l] for l in layers])
         torch.cuda.synchronize()
@@ -361,6 +373,11 @@ def test_wide_launch_copies_multi_piece_rows(hs):
             assert np.array_equal(out[l].cpu().numpy(), ref["slot_idx"]), f"step {t} layer {l}"
             occ = o.slot_pos[l] >= 0
             assert np.array_equal(res.cache_layer(l)[occ], o.cache[l][occ]), f"cache bytes step {t} layer {l}"
+            st = res.state(l)
+            assert np.array_equal(st["slot_pos"], o.slot_pos[l]) and np.array_equal(st["ts"], o.ts[l])
+        if t == 2:
+            assert res.error()[0] in (hs.HS_DEV_DUP, hs.HS_DEV_RANGE)
+            res.clear_error()
     assert res.error()[0] == 0
     res.close()
     pool.free()
