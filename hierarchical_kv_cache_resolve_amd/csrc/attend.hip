@@ -10,7 +10,7 @@
 // with whole records and the values are the records' first 512 elements.
 //
 // Work split (flash-decoding): workgroup = (request, 32 or 64 heads, a chunk
-// of records); 4 wave64s.  Records move HBM -> LDS with
+// of records); 4 wave64s at 32 heads, 8 at 64.  Records move HBM -> LDS with
 // global_load_lds (16 bytes a lane, no registers), 64 records per sub-chunk
 // into one of two LDS buffers, so the loads of sub-chunk i+1 are in flight
 // while sub-chunk i is computed.
@@ -19,17 +19,17 @@
 // record is its bytes 128L..128L+127 (one HBM cache line) and slot j holds
 // piece 8L + (j ^ swz(rec)).  One global_load_lds moves whole lines of 8
 // records (8 lanes a line, so every access is a full coalesced line), a lane
-// loads the same two records for the whole sub-chunk, and the XOR swizzle
+// loads the same record(s) for the whole sub-chunk, and the XOR swizzle
 // keeps both operand reads below free of bank conflicts:
-//   scores  wave w: S^T = K Q^T for one tile of 16 heads over all 64 records
-//           of the sub-chunk (64 heads a workgroup) or over 32 of them (32
-//           heads: two waves share a tile) (v_mfma_f32_16x16x32_bf16, K from
+//   scores  wave w: S^T = K Q^T for one tile of 16 heads over 32 of the
+//           sub-chunk's 64 records (two waves share a tile)
+//           (v_mfma_f32_16x16x32_bf16, K from
 //           LDS, Q fragments in registers); online softmax; the
 //           probabilities go to LDS as bf16 MFMA fragments;
-//   output  wave w: O^T = V^T P^T for output dimensions 128w..128w+127 of all
+//   output  wave w: O^T = V^T P^T for output dimensions 512w/W.. (W waves) of all
 //           the workgroup's heads; V^T comes from the gfx950 transposing LDS read
 //           (ds_read_b64_tr_b16, the costliest LDS access here, so each wave
-//           reads only its quarter of the values), P^T fragments from LDS.
+//           reads only its share of the values), P^T fragments from LDS.
 // The record order inside each 32-wide k-step is permuted identically on
 // both operands of O^T = V^T P^T, so the probability fragments are written
 // exactly as the score registers hold them.  A lane of the score phase owns
@@ -49,8 +49,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kAttnThreads = 256;
-constexpr int kAttnWaves = kAttnThreads / 64;
 constexpr int kMaxHeadTiles = 4;               // a workgroup takes 2 or 4 tiles of 16 heads
 constexpr int kSub = 64;                       // records per LDS sub-chunk
 constexpr int kDqk = 576, kDv = 512;
@@ -65,8 +63,6 @@ constexpr int kPBytes = kMaxHeadTiles * 2 * 1024;   // P fragments: [head tile][
 constexpr int kXBytes = 2 * 16 * kMaxHeadTiles * 4;  // [record half][head] partial maxima / sums
 constexpr size_t kAttnLds =
     2 * static_cast<size_t>(kBufBytes) + kPBytes + 16 * kMaxHeadTiles * sizeof(float) + kXBytes;
-constexpr int kDimsPerWave = kDv / kAttnWaves; // 128 output dimensions a wave
-constexpr int kWaveDTiles = kDimsPerWave / 16; // 8
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt == 0 only:
 // vmcnt 0 (bits 3:0, 15:14), expcnt 7 (bits 6:4), lgkmcnt 15 (bits 11:8)
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -91,46 +87,53 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // land on distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int rec) { return (rec & 6) | ((rec >> 3) & 1); }
 
-// This wave's share of one sub-chunk, HBM -> LDS: records 16w..16w+15, all 9
-// lines (18 instructions of 1 KB).  `src_a` / `src_b` point at this lane's
-// piece of line 0 of record 16w + lane/8 and 16w + 8 + lane/8.  The loads are
-// issued as inline assembly on purpose: the compiler would otherwise guard
-// the transposing LDS reads of the other buffer with a full vmcnt wait (it
-// cannot tell the buffers apart), serialising loads and compute.  Their
-// completion is waited for explicitly before the barrier that publishes a
-// buffer.
-__device__ __forceinline__ void issue_records(uint8_t* buf, const uint8_t* src_a, const uint8_t* src_b, int wave) {
+// This wave's share of one sub-chunk, HBM -> LDS: NR groups of 8 records
+// (records 8NR·w .. 8NR·w + 8NR - 1; NR = 2 with 4 waves, 1 with 8), all 9
+// lines (9·NR instructions of 1 KB).  src[h] points at this lane's piece of
+// line 0 of record 8NR·w + 8h + lane/8.  The loads are issued as inline
+// assembly on purpose: the compiler would otherwise guard the transposing LDS
+// reads of the other buffer with a full vmcnt wait (it cannot tell the
+// buffers apart), serialising loads and compute.  Their completion is waited
+// for explicitly before the barrier that publishes a buffer.
+template <int NR>
+__device__ __forceinline__ void issue_records(uint8_t* buf, const uint8_t* const (&src)[NR], int wave) {
 #pragma unroll
     for (int L = 0; L < kLines; ++L) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint8_t* dst = buf + L * kLineBlock + (2 * wave + h) * 1024;
+        for (int h = 0; h < NR; ++h) {
+            const uint8_t* dst = buf + L * kLineBlock + (NR * wave + h) * 1024;
             const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)dst));
             // M0 carries the LDS destination; its previous value is restored
             uint32_t m0_saved;
             asm volatile(
                 "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
                 : "=&s"(m0_saved)
-                : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"((h ? src_b : src_a) + 128 * L)
+                : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src[h] + 128 * L)
                 : "memory");
         }
     }
 }
 
-// HT: head tiles of 16 per workgroup.  The score phase spreads the HT tiles
-// over the 4 waves: RS = 4 / HT waves share a tile, each taking 64 / RS of
-// the sub-chunk's records (HT score tiles of 16 records) and exchanging its
-// partial maximum through LDS; the value phase is split by output dimensions
-// as always.  HT = 2 halves the partial outputs per record read, which pays
-// when the split over records is deep (few requests); HT = 4 reads each
-// record into fewer workgroups.
-template <int HT>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// HT: head tiles of 16 per workgroup; W: waves per workgroup (4 or 8, one
+// workgroup per CU either way).  The score phase spreads the HT tiles over
+// the W waves: RS = W / HT waves share a tile, each taking 64 / RS of the
+// sub-chunk's records (TPW score tiles of 16 records) and exchanging its
+// partial maximum through LDS; the value phase gives each wave 512 / W output
+// dimensions of every head.  HT = 2 halves the partial outputs per record
+// read, which pays when the split over records is deep (few requests); HT = 4
+// reads each record into fewer workgroups and runs 8 waves, so that two
+// waves share each SIMD and hide each other's LDS and memory waits.
+template <int HT, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W / 4)))
 void mla_partial_kernel(StateBase s, int layer, const uint16_t* q, int H, const int32_t* slot_idx, int k, int chunk,
                         int nchunk, float scale_log2, float* part_o, float* part_ml) {
     constexpr int HPW = 16 * HT;         // heads per workgroup
-    constexpr int RS = kAttnWaves / HT;  // waves sharing a head tile in the score phase
+    constexpr int RS = W / HT;           // waves sharing a head tile in the score phase
     constexpr int TPW = 4 / RS;          // score tiles (of 16 records) per wave
+    constexpr int NR = 8 / W;            // groups of 8 records each lane loads
+    constexpr int kDimsPerWave = kDv / W;
+    constexpr int kWaveDTiles = kDimsPerWave / 16;
+    static_assert((W == 4 || W == 8) && TPW >= 2 && TPW % 2 == 0, "each wave owns whole k-steps of P");
     extern __shared__ __align__(16) uint8_t attn_lds[];
     uint8_t* pfrag = attn_lds + 2 * kBufBytes;                          // [HT][2][64][16 B]
     float* alpha_lds = reinterpret_cast<float*>(pfrag + kPBytes);       // [HPW] rescale of each head
@@ -164,18 +167,28 @@ void mla_partial_kernel(StateBase s, int layer, const uint16_t* q, int H, const 
         return (j_begin + sub * kSub + i < j_end && v >= 0 && v < s.B) ? v : -1;
     };
     // the two records this lane loads, and its piece slot inside each line
-    const int rec_a = 16 * wave + (lane >> 3), rec_b = rec_a + 8;
-    const int pa = 16 * ((lane & 7) ^ swz(rec_a)), pb = 16 * ((lane & 7) ^ swz(rec_b));
+    int rec[NR], poff[NR];
+#pragma unroll
+    for (int h = 0; h < NR; ++h) {
+        rec[h] = 8 * NR * wave + 8 * h + (lane >> 3);
+        poff[h] = 16 * ((lane & 7) ^ swz(rec[h]));
+    }
     auto record_src = [&](int slot, int piece_off) -> const uint8_t* {
         return (slot >= 0 ? cache + static_cast<int64_t>(slot) * kRecBytes
                           : reinterpret_cast<const uint8_t*>(g_zero_record)) + piece_off;
     };
-    issue_records(attn_lds, record_src(checked(0, rec_a, raw_slot(0, rec_a)), pa),
-                  record_src(checked(0, rec_b, raw_slot(0, rec_b)), pb), wave);
+    {
+        const uint8_t* src[NR];
+#pragma unroll
+        for (int h = 0; h < NR; ++h) src[h] = record_src(checked(0, rec[h], raw_slot(0, rec[h])), poff[h]);
+        issue_records<NR>(attn_lds, src, wave);
+    }
     // slots are read one sub-chunk ahead of their use: `mk_*` names record
     // `lane` (validity mask), `la_*` / `lb_*` the records this lane loads
     int mk_cur = raw_slot(0, lane);
-    int la_nxt = raw_slot(1, rec_a), lb_nxt = raw_slot(1, rec_b);
+    int slot_nxt[NR];
+#pragma unroll
+    for (int h = 0; h < NR; ++h) slot_nxt[h] = raw_slot(1, rec[h]);
     int mk_nxt = raw_slot(1, lane);
 
     // query fragments of this wave's 16 heads (B operand of S^T = K Q^T)
@@ -185,7 +198,7 @@ void mla_partial_kernel(StateBase s, int layer, const uint16_t* q, int H, const 
 #pragma unroll
         for (int st = 0; st < kQSteps; ++st) aq[st] = *reinterpret_cast<const bf16x8*>(qrow + 32 * st);
     }
-    // output accumulators: dimension tile dt (dims 128w + 16dt ..) x head tile ht;
+    // output accumulators: dimension tile dt (dims kDimsPerWave·w + 16dt ..) x head tile ht;
     // lane (grp, n) holds dims +4grp+i of head 16ht + n
     f32x4 acc_o[kWaveDTiles][HT];
 #pragma unroll
@@ -204,7 +217,7 @@ void mla_partial_kernel(StateBase s, int layer, const uint16_t* q, int H, const 
     //   (2(t&3) + (qq>>1)) ^ swz = 2(t&3) ^ gv, half qq & 1
     const int e = n >> 2, qq = n & 3;
     const int gv = (qq >> 1) ^ swz(4 * grp + e);
-    // (this wave's dimension tiles are t = 8w + dt, so t & 3 = dt & 3)
+    // (this wave's dimension tiles are t = kWaveDTiles·w + dt, so t & 3 = dt & 3)
     const int v_base = 128 * (4 * grp + e) + 8 * (qq & 1);
     const int v_off[4] = {v_base + 16 * (0 ^ gv), v_base + 16 * (2 ^ gv), v_base + 16 * (4 ^ gv),
                           v_base + 16 * (6 ^ gv)};
@@ -216,12 +229,15 @@ void mla_partial_kernel(StateBase s, int layer, const uint16_t* q, int H, const 
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();                          // sub-chunk `sub` is in LDS
         const uint64_t valid = __ballot(checked(sub, lane, mk_cur) >= 0);
-        if (sub + 1 < nsub)
-            issue_records(attn_lds + ((sub + 1) & 1) * kBufBytes, record_src(checked(sub + 1, rec_a, la_nxt), pa),
-                          record_src(checked(sub + 1, rec_b, lb_nxt), pb), wave);
+        if (sub + 1 < nsub) {
+            const uint8_t* src[NR];
+#pragma unroll
+            for (int h = 0; h < NR; ++h) src[h] = record_src(checked(sub + 1, rec[h], slot_nxt[h]), poff[h]);
+            issue_records<NR>(attn_lds + ((sub + 1) & 1) * kBufBytes, src, wave);
+        }
         mk_cur = mk_nxt;
-        la_nxt = raw_slot(sub + 2, rec_a);
-        lb_nxt = raw_slot(sub + 2, rec_b);
+#pragma unroll
+        for (int h = 0; h < NR; ++h) slot_nxt[h] = raw_slot(sub + 2, rec[h]);
         mk_nxt = raw_slot(sub + 2, lane);
 
         // S^T = K Q^T: tile nt covers records 16nt..16nt+15; this lane ends with
@@ -330,7 +346,7 @@ void mla_partial_kernel(StateBase s, int layer, const uint16_t* q, int H, const 
                 for (int ht = 0; ht < HT; ++ht) acc_o[dt][ht] *= a_ht[ht];
         }
 
-        // O^T += V^T P^T for dims 128w.. of the workgroup's heads
+        // O^T += V^T P^T for dims kDimsPerWave·w.. of the workgroup's heads
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             bf16x8 pf[HT];
@@ -362,7 +378,7 @@ void mla_partial_kernel(StateBase s, int layer, const uint16_t* q, int H, const 
     }
 
     // partials: unnormalised O, running maximum and sum (log2 units); lane
-    // (grp, n) holds dims 128w + 16dt + 4grp + i of head 16ht + n, and the
+    // (grp, n) holds dims kDimsPerWave·w + 16dt + 4grp + i of head 16ht + n, and the
     // score-phase statistics of head h0 + n
     const int64_t hbase = (static_cast<int64_t>(r) * nchunk + c) * H + g * HPW;
 #pragma unroll
@@ -455,8 +471,8 @@ hipError_t launch_attend_mla(const StateBase& s, int layer, const uint16_t* q, i
     float* part_ml = workspace + static_cast<size_t>(s.R) * nchunk * H * kDv;
     // the attribute belongs to each kernel instance: set it once per process
     static bool lds_attr_set[2] = {false, false};
-    const void* fn = ht == 2 ? reinterpret_cast<const void*>(&mla_partial_kernel<2>)
-                             : reinterpret_cast<const void*>(&mla_partial_kernel<4>);
+    const void* fn = ht == 2 ? reinterpret_cast<const void*>(&mla_partial_kernel<2, 4>)
+                             : reinterpret_cast<const void*>(&mla_partial_kernel<4, 8>);
     if (!lds_attr_set[ht / 4]) {
         const hipError_t e =
             hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kAttnLds));
@@ -466,11 +482,11 @@ hipError_t launch_attend_mla(const StateBase& s, int layer, const uint16_t* q, i
     const float scale_log2 = scale * 1.44269504088896340736f;
     const int nwg = nchunk * (H / (16 * ht)) * s.R;
     if (ht == 2)
-        hipLaunchKernelGGL(mla_partial_kernel<2>, dim3(nwg), dim3(kAttnThreads), kAttnLds, st, s, layer, q, H,
-                           slot_idx, k, chunk, nchunk, scale_log2, part_o, part_ml);
+        hipLaunchKernelGGL((mla_partial_kernel<2, 4>), dim3(nwg), dim3(256), kAttnLds, st, s, layer, q, H, slot_idx, k,
+                           chunk, nchunk, scale_log2, part_o, part_ml);
     else
-        hipLaunchKernelGGL(mla_partial_kernel<4>, dim3(nwg), dim3(kAttnThreads), kAttnLds, st, s, layer, q, H,
-                           slot_idx, k, chunk, nchunk, scale_log2, part_o, part_ml);
+        hipLaunchKernelGGL((mla_partial_kernel<4, 8>), dim3(nwg), dim3(512), kAttnLds, st, s, layer, q, H, slot_idx, k,
+                           chunk, nchunk, scale_log2, part_o, part_ml);
     hipLaunchKernelGGL(mla_combine_kernel, dim3(H, s.R), dim3(kCombineThreads), 0, st, part_o, part_ml, H, nchunk, out,
                        lse);
     return hipGetLastError();
