@@ -469,16 +469,11 @@ hipError_t launch_attend_mla(const StateBase& s, int layer, const uint16_t* q, i
     const int nchunk = (k + chunk - 1) / chunk;
     float* part_o = workspace;
     float* part_ml = workspace + static_cast<size_t>(s.R) * nchunk * H * kDv;
-    // the attribute belongs to each kernel instance: set it once per process
-    static bool lds_attr_set[2] = {false, false};
     const void* fn = ht == 2 ? reinterpret_cast<const void*>(&mla_partial_kernel<2, 4>)
                              : reinterpret_cast<const void*>(&mla_partial_kernel<4, 8>);
-    if (!lds_attr_set[ht / 4]) {
-        const hipError_t e =
-            hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kAttnLds));
-        if (e != hipSuccess) return e;
-        lds_attr_set[ht / 4] = true;
-    }
+    static LdsGrants granted[2];  // one per kernel instance
+    const hipError_t e = ensure_lds_limit(fn, kAttnLds, granted[ht / 4]);
+    if (e != hipSuccess) return e;
     const float scale_log2 = scale * 1.44269504088896340736f;
     const int nwg = nchunk * (H / (16 * ht)) * s.R;
     if (ht == 2)

@@ -98,6 +98,27 @@ hipError_t launch_attend_mla(const StateBase& s, int layer, const uint16_t* q, i
                              hipStream_t st);
 hipError_t launch_hbm_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 
+// Largest dynamic-LDS limit already granted to one kernel, per device.
+struct LdsGrants {
+    static constexpr int kDevices = 64;
+    size_t bytes[kDevices] = {};
+};
+
+// Raise a kernel's dynamic-LDS limit when a launch needs more than the default
+// 64 KB.  The limit is set once per kernel and device (and again only for a
+// larger need), so steady-state launches make no attribute call.  A handle is
+// not thread-safe, and neither is this bookkeeping.
+inline hipError_t ensure_lds_limit(const void* fn, size_t lds, LdsGrants& g) {
+    if (lds <= 65536) return hipSuccess;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    const bool tracked = dev >= 0 && dev < LdsGrants::kDevices;
+    if (tracked && lds <= g.bytes[dev]) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e == hipSuccess && tracked) g.bytes[dev] = lds;
+    return e;
+}
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte load / store, non-temporal (streamed past the caches) when NT.

@@ -964,11 +964,10 @@ size_t plan_lds_bytes(int k, int half, int B) {
 
 template <int PER, bool VEC, int PROBE, bool WIDE>
 static hipError_t launch_plan_w(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&plan_kernel<PER, VEC, PROBE, WIDE>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess) return e;
-    }
+    static LdsGrants granted;  // per instantiation
+    const hipError_t e =
+        ensure_lds_limit(reinterpret_cast<const void*>(&plan_kernel<PER, VEC, PROBE, WIDE>), lds, granted);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((plan_kernel<PER, VEC, PROBE, WIDE>), dim3(s.R, lb.n), dim3(kPlanThreads), lds, st, s, lb);
     return hipGetLastError();
 }
@@ -1045,11 +1044,9 @@ hipError_t launch_publish(const StateBase& s, const LayerBatch& lb, hipStream_t 
 
 hipError_t launch_replay_meta(const StateBase& s, const ReplayBatch& rb, hipStream_t st) {
     const size_t lds = sizeof(int) * static_cast<size_t>(s.B);
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&replay_meta_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess) return e;
-    }
+    static LdsGrants granted;
+    const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(&replay_meta_kernel), lds, granted);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(replay_meta_kernel, dim3(s.R, rb.n), dim3(kPlanThreads), lds, st, s, rb);
     return hipGetLastError();
 }
