@@ -300,13 +300,24 @@ def test_victims_older_than_histogram_range(hs):
     pool.free()
 
 
+BATCHED_SHAPES = [
+    # 512 units: one per workgroup of the two-per-CU build
+    tg.Workload("batched_wide", 64, 8, 8192, 8, 2, 256, 512, 6, tg.LOCALITY, 0.85, seed_index=95),
+    # more units than the chip keeps resident at once (two rounds of workgroups)
+    tg.Workload("batched_2x", 64, 16, 8192, 8, 2, 256, 512, 5, tg.LOCALITY, 0.85, seed_index=98),
+    # 600 units at B = 4096, k = 2048 (a ragged second round)
+    tg.Workload("batched_ragged_b4096", 40, 15, 16384, 8, 2, 2048, 4096, 4, tg.LOCALITY, 0.87, seed_index=99),
+]
+
+
+@pytest.mark.parametrize("w", BATCHED_SHAPES, ids=[w.name for w in BATCHED_SHAPES])
 @pytest.mark.parametrize("probe", ["page_table", "bitmap", "hash"])
-def test_batched_launch_over_many_units(hs, probe):
-    """One launch over 512 (request, layer) units (the build held to two
-    workgroups per CU, which copies its own misses) against the oracle, with
-    misses and all-hit steps, with each probe."""
+def test_batched_launch_over_many_units(hs, probe, w):
+    """One launch over 512 or more (request, layer) units (the build held to
+    two workgroups per CU, which copies its own misses) against the oracle,
+    with misses and all-hit steps, with each probe."""
     from oracle import Oracle
-    w = tg.Workload("batched_wide", 64, 8, 8192, 8, 2, 256, 512, 6, tg.LOCALITY, 0.85, seed_index=95)
+    print(f"[parity] {w.name} R={w.num_req} L={w.num_layers} B={w.B} k={w.k} probe={probe}", flush=True)
     tr = tg.trace(w)
     tr[3] = tr[2]                         # an all-hit step
     pool = make_pool(hs, w)
