@@ -58,7 +58,6 @@ constexpr int kLines = kRecBytes / 128;        // 9 lines of 128 bytes a record
 constexpr int kLineBlock = kSub * 128;         // 8 KB: one line of every record
 constexpr int kBufBytes = kLines * kLineBlock; // 73728 per buffer
 constexpr int kQSteps = kDqk / 32;             // 18 MFMA k-steps for the scores
-constexpr int kDTiles = kDv / 16;              // 32 output tiles of 16 dimensions
 constexpr int kPBytes = kMaxHeadTiles * 2 * 1024;   // P fragments: [head tile][k-step][64 lanes][16 B]
 constexpr int kXBytes = 2 * 16 * kMaxHeadTiles * 4;  // [record half][head] partial maxima / sums
 constexpr size_t kAttnLds =

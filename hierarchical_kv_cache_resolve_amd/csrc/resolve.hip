@@ -255,7 +255,6 @@ __device__ inline void reject(const StateBase& s, int32_t* out, int k, int64_t r
             for (int i_ = 0; i_ < 13; ++i_) s.phase[rl * kPhaseSlots + i_] = stamp[i_]; \
     } while (0)
 
-constexpr int kMaxSelPerLane = HS_MAX_K / kPlanThreads;  // 4
 
 // Histogram increment for this lane's bin (-1: none).  When every active
 // lane of the wave has the same bin (an empty cache, or one stamp shared by
@@ -418,11 +417,13 @@ __device__ inline void copy_misses(const StateBase& s, const PlanLds& l, int64_t
 //   5. the i-th miss takes the i-th victim in slot order; slot map, stamps
 //      (2t+1 for misses, 2t+2 for hits), page table and plan are written and
 //      every selection's slot is published.
+// SPL: selections a lane holds at most (k <= SPL * 1024); 2 covers k up to
+// 2048 without carrying the empty iterations of the 4096 build.
 // WIDE: the instantiation for launches over many (request, layer) units.  Up
 // to B = 4096 (PER <= 4) it is held to 8 waves per SIMD, so two workgroups
 // share a CU; per-layer launches (a few units) use the unconstrained build,
 // whose scalar registers need not spill.
-template <int PER, bool VEC, int PROBE, bool WIDE>
+template <int PER, bool VEC, int PROBE, bool WIDE, int SPL>
 __global__ __launch_bounds__(kPlanThreads) __attribute__((amdgpu_waves_per_eu(WIDE && PER <= 4 ? 8 : 1)))
 void plan_kernel(StateBase s, LayerBatch lb) {
     constexpr bool SCAN = PROBE != PROBE_TABLE;
@@ -450,9 +451,9 @@ void plan_kernel(StateBase s, LayerBatch lb) {
     // 1. global reads
     const uint32_t t = s.clock[rl];
     const int64_t hist_len = s.length[rl];
-    int selv[kMaxSelPerLane];
+    int selv[SPL];
 #pragma unroll
-    for (int q = 0; q < kMaxSelPerLane; ++q) {
+    for (int q = 0; q < SPL; ++q) {
         const int j = tid + q * kPlanThreads;
         selv[q] = j < k ? sel[j] : 0;
     }
@@ -462,9 +463,9 @@ void plan_kernel(StateBase s, LayerBatch lb) {
     load_run<PER, VEC, int>(spos_g, s0, B, spos, kEmpty);
     if constexpr (!SCAN) load_run<PER, VEC, uint32_t>(ts_g, s0, B, tsv, 0xFFFFFFFFu);
     int bad = 0, bad_at = 0;
-    int ptv[kMaxSelPerLane];
+    int ptv[SPL];
 #pragma unroll
-    for (int q = 0; q < kMaxSelPerLane; ++q) {
+    for (int q = 0; q < SPL; ++q) {
         const int j = tid + q * kPlanThreads;
         ptv[q] = -1;
         if (j < k) {
@@ -504,7 +505,7 @@ void plan_kernel(StateBase s, LayerBatch lb) {
     // 2. page-table probe: hits into the slot bitmap, misses into the hash.
     //    slot-scan probe: every selected position into the lookup structure.
 #pragma unroll
-    for (int q = 0; q < kMaxSelPerLane; ++q) {
+    for (int q = 0; q < SPL; ++q) {
         const int j = tid + q * kPlanThreads;
         if (j < k && !(bad & 1)) {
             const int p = selv[q];
@@ -632,7 +633,7 @@ void plan_kernel(StateBase s, LayerBatch lb) {
     unsigned mflags = 0;
     int mpre = 0, mtot = 0;
 #pragma unroll
-    for (int q = 0; q < kMaxSelPerLane; ++q) {
+    for (int q = 0; q < SPL; ++q) {
         if (q < kper) {
             const int j = j0 + q;
             bool f;
@@ -661,7 +662,7 @@ void plan_kernel(StateBase s, LayerBatch lb) {
     const int m = sum_before(l.misc + M_MISS, kPlanWaves);
     int base = mpre + sum_before(l.misc + M_MISS, wave);
 #pragma unroll
-    for (int q = 0; q < kMaxSelPerLane; ++q)
+    for (int q = 0; q < SPL; ++q)
         if ((mflags >> q) & 1u) l.mlist[base++] = j0 + q;
     HS_PHASE(4);
     const int h = k - m;
@@ -962,14 +963,22 @@ size_t plan_lds_bytes(int k, int half, int B) {
     return sizeof(int) * (2 * static_cast<size_t>(half) + 3 * static_cast<size_t>(k) + hit_words + kHistBins + kMisc);
 }
 
-template <int PER, bool VEC, int PROBE, bool WIDE>
-static hipError_t launch_plan_w(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
+template <int PER, bool VEC, int PROBE, bool WIDE, int SPL>
+static hipError_t launch_plan_k(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
     static LdsGrants granted;  // per instantiation
     const hipError_t e =
-        ensure_lds_limit(reinterpret_cast<const void*>(&plan_kernel<PER, VEC, PROBE, WIDE>), lds, granted);
+        ensure_lds_limit(reinterpret_cast<const void*>(&plan_kernel<PER, VEC, PROBE, WIDE, SPL>), lds, granted);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((plan_kernel<PER, VEC, PROBE, WIDE>), dim3(s.R, lb.n), dim3(kPlanThreads), lds, st, s, lb);
+    hipLaunchKernelGGL((plan_kernel<PER, VEC, PROBE, WIDE, SPL>), dim3(s.R, lb.n), dim3(kPlanThreads), lds, st, s,
+                       lb);
     return hipGetLastError();
+}
+
+template <int PER, bool VEC, int PROBE, bool WIDE>
+static hipError_t launch_plan_w(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
+    static_assert(HS_MAX_K <= 4 * kPlanThreads, "a lane holds at most four selections");
+    return lb.k <= 2 * kPlanThreads ? launch_plan_k<PER, VEC, PROBE, WIDE, 2>(s, lb, lds, st)
+                                    : launch_plan_k<PER, VEC, PROBE, WIDE, 4>(s, lb, lds, st);
 }
 
 template <int PER, bool VEC, int PROBE>
