@@ -82,6 +82,9 @@ RAGGED = [
     wl("per2", B=2047, k=1023),
     wl("per4_mla", B=4096, k=2048, L_ctx=40000, W_KV=576, num_req=2, num_layers=2, steps=10),
     wl("per8", B=8000, k=3000, L_ctx=60000, W_KV=24, num_req=2, steps=8),
+    # the smallest k that needs more than two selections per lane, and the largest that does not
+    wl("k2049_three_per_lane", B=2100, k=2049, L_ctx=30000, W_KV=8, num_req=2, steps=8),
+    wl("k2048_b2049", B=2049, k=2048, L_ctx=30000, W_KV=8, num_req=2, steps=8),
     wl("per16_maxb", B=16384, k=4096, L_ctx=90000, W_KV=8, num_req=1, num_layers=1, steps=6),
     wl("b_equals_k", B=900, k=900, p_keep=0.6),
     wl("uniform_small_ctx", mode=tg.UNIFORM, L_ctx=2000, B=1200, k=500),
