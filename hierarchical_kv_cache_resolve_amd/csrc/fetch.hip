@@ -237,7 +237,9 @@ hipError_t launch_link_read(const void* src, void* dst, size_t bytes, hipStream_
 }
 
 hipError_t launch_hbm_copy(const void* src, void* dst, size_t bytes, hipStream_t st) {
-    hipLaunchKernelGGL(hbm_copy_kernel<4>, dim3(4096), dim3(kFetchThreads), 0, st,
+    // 65536 workgroups: measured on MI355X over 4 GiB, 5.2 TB/s against 4.7 TB/s with 4096
+    // (and 4.6 TB/s for a device-to-device hipMemcpy), so the reported peak is not understated
+    hipLaunchKernelGGL(hbm_copy_kernel<4>, dim3(65536), dim3(kFetchThreads), 0, st,
                        static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), static_cast<int64_t>(bytes / 16));
     return hipGetLastError();
 }
