@@ -74,7 +74,7 @@ typedef struct hisparse_ctx* hisparse_t;
 #define HS_E_ORDER (-10)  /* prefetch / shared-layer resolve issued out of order */
 
 /* ---- device error codes (sticky word) -------------------------------------- */
-#define HS_DEV_RANGE 1        /* a position outside [0, L_ctx) */
+#define HS_DEV_RANGE 1        /* a position outside [0, length) of its history (length <= L_ctx) */
 #define HS_DEV_DUP 2          /* a position repeated within one request's selection */
 #define HS_DEV_NOT_RESIDENT 3 /* shared layer: a selected position is not where the anchor's plan put it */
 #define HS_DEV_DIVERGED 4     /* shared layer: its cache state no longer mirrors its anchor's */
