@@ -8,9 +8,13 @@
 // HBM cache).  The misses of all requests of the launched layers form one
 // flat index space of (row, 16-byte piece) pairs, so consecutive lanes of a
 // wave read consecutive bytes of one record and the whole chip shares the
-// transfer however unevenly the misses fall on requests.  Each lane keeps U
-// independent loads in flight before storing, which is what hides the
-// microsecond-scale latency of reads that cross the host link.
+// transfer however unevenly the misses fall on requests.  Each lane takes U
+// pieces a round; a piece's host address needs its plan entry and its
+// history's first row, and the in-order vector-memory counter makes those
+// loads wait for the previous piece's host load, so about one host load per
+// lane is in flight -- with 262144 lanes, megabytes in flight, which is what
+// hides the microsecond-scale latency of reads that cross the host link
+// (keeping all U in flight per lane measured slower).
 #include "hs_internal.h"
 
 namespace hs {
