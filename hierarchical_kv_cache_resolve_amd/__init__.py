@@ -335,6 +335,8 @@ class Resolver:
         _check("hisparse_resolve", hisparse_resolve(self.h, layer, _ptr(sel), k, _ptr(out), _stream(stream)))
 
     def resolve_layers(self, layers, sels, outs, stream=None):
+        if not (len(layers) == len(sels) == len(outs)) or len(layers) == 0:
+            raise ValueError(f"resolve_layers: {len(layers)} layers, {len(sels)} selections, {len(outs)} outputs")
         k = int(sels[0].shape[-1])
         for s_, o_ in zip(sels, outs):
             _dev_arg(s_, 4 * self.num_req * k, 4, "sel")

@@ -220,6 +220,14 @@ def test_synchronous_argument_errors(hs):
     assert e.value.rc == hs.HS_E_POOL
     with pytest.raises(hs.HisparseError):
         hs.hisparse_create(2, 2, 0, 8, hs.BF16, hs.hs_host_pool(pool.ptr, w.pool_rows, w.L_ctx, None))
+    # batched resolve: a null selection pointer, a repeated layer, lists of different lengths
+    sel8, out8 = sel[:, :8].contiguous(), out[:, :8].contiguous()
+    assert hs.hisparse_resolve_layers(res.h, [0, 1], [sel8.data_ptr(), 0], 8,
+                                      [out8.data_ptr(), out8.data_ptr()], s) == hs.HS_E_INVAL
+    assert hs.hisparse_resolve_layers(res.h, [1, 1], [sel8.data_ptr()] * 2, 8, [out8.data_ptr()] * 2,
+                                      s) == hs.HS_E_INVAL
+    with pytest.raises(ValueError):
+        res.resolve_layers([0, 1], [sel8], [out8, out8])
     assert res.hbm_bytes() == hs.hisparse_kv_bytes(2, 2, 32, 8, hs.BF16) == 2 * 2 * 32 * 16
     res.close()
     pool.free()
