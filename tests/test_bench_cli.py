@@ -22,3 +22,42 @@ def test_traffic_is_tied_to_the_measured_source():
     # source, or the bench reports no traffic at all
     if t is not None:
         assert t["total_bytes"] == t["read_bytes"] + t["write_bytes"] > 0
+
+
+def _bench_tree(tmp_path, sha_override=None):
+    """A copy of the two files fetch_traffic reads, optionally with the
+    summary stamped for a different source."""
+    prof = open(os.path.join(ROOT, "profiles", "fetch_kernel_traffic_mla_latent.md")).read()
+    if sha_override is not None:
+        import re
+        prof = re.sub(r"sha256 prefix [0-9a-f]{16}", f"sha256 prefix {sha_override}", prof)
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "fetch_kernel_traffic_mla_latent.md").write_text(prof)
+    src = tmp_path / "hierarchical_kv_cache_resolve_amd" / "csrc"
+    src.mkdir(parents=True)
+    src_text = open(os.path.join(ROOT, "hierarchical_kv_cache_resolve_amd", "csrc", "fetch.hip"), "rb").read()
+    (src / "fetch.hip").write_bytes(src_text)
+    return tmp_path
+
+
+def test_traffic_is_dropped_for_another_source(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    monkeypatch.setattr(bench, "ROOT", str(_bench_tree(tmp_path, sha_override="0" * 16)))
+    assert bench.fetch_traffic() is None
+
+
+def test_traffic_values_come_from_the_summary_table(tmp_path, monkeypatch):
+    import hashlib
+    import re
+    sys.path.insert(0, ROOT)
+    import bench
+    src = open(os.path.join(ROOT, "hierarchical_kv_cache_resolve_amd", "csrc", "fetch.hip"), "rb").read()
+    tree = _bench_tree(tmp_path, sha_override=hashlib.sha256(src).hexdigest()[:16])
+    monkeypatch.setattr(bench, "ROOT", str(tree))
+    t = bench.fetch_traffic()
+    text = (tree / "profiles" / "fetch_kernel_traffic_mla_latent.md").read_text()
+    rd = int(re.search(r"\| read \(scaled FETCH_SIZE\) \| (\d+) \|", text).group(1))
+    wr = int(re.search(r"\| written \(scaled WRITE_SIZE\) \| (\d+) \|", text).group(1))
+    assert t == {"read_bytes": rd, "write_bytes": wr, "total_bytes": rd + wr,
+                 "source": "profiles/fetch_kernel_traffic_mla_latent.md"}
