@@ -80,3 +80,52 @@ def test_graph_replay_equals_eager(hs, prefetch):
     graphed.close()
     eager.close()
     pool.free()
+
+
+def test_graph_replay_of_wide_batched_launches(hs):
+    """A batched launch over 40 requests x 8 layers (320 request-layers: the
+    two-per-CU build, which copies its own misses, no fetch launch) captured
+    once and replayed step after step equals the oracle on every replay."""
+    from oracle import Oracle
+    w = tg.Workload("graph_wide", 40, 8, 8192, 64, 2, 256, 512, 8, tg.LOCALITY, 0.85, seed_index=120)
+    print(f"[graph] {w.name} R={w.num_req} L={w.num_layers} B={w.B} k={w.k}", flush=True)
+    tr = tg.trace(w)
+    pool = make_pool(hs, w)
+    pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
+    res = make_resolver(hs, w, pool)
+    o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes)
+    dev = torch.device("cuda:0")
+    layers = list(range(w.num_layers))
+    sel = torch.from_numpy(tr).to(dev)
+    sel_buf = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
+    out_buf = torch.empty_like(sel_buf)
+
+    def check(t):
+        for l in layers:
+            ref = o.resolve(l, tr[t, l], pool_np, w.region_rows())
+            assert np.array_equal(out_buf[l].cpu().numpy(), ref["slot_idx"]), f"step {t} layer {l}"
+            st = res.state(l)
+            assert np.array_equal(st["slot_pos"], o.slot_pos[l]) and np.array_equal(st["ts"], o.ts[l])
+            occ = o.slot_pos[l] >= 0
+            assert np.array_equal(res.cache_layer(l)[occ], o.cache[l][occ]), f"cache step {t} layer {l}"
+
+    # one eager step first, then the capture
+    sel_buf.copy_(sel[0])
+    res.resolve_layers(layers, [sel_buf[l] for l in layers], [out_buf[l] for l in layers])
+    torch.cuda.synchronize()
+    check(0)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cur = torch.cuda.current_stream()
+        res.resolve_layers(layers, [sel_buf[l] for l in layers], [out_buf[l] for l in layers], cur)
+    for t in range(1, w.steps):
+        sel_buf.copy_(sel[t])
+        g.replay()
+        junk = torch.randn(1 << 20, device=dev).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+        check(t)
+    assert res.error()[0] == 0
+    del g
+    res.close()
+    pool.free()
