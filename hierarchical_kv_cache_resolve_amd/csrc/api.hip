@@ -12,7 +12,9 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
+#include <unordered_set>
 #include <vector>
 
 #include "hs_internal.h"
@@ -124,7 +126,23 @@ int init_state(hisparse_ctx* h, hipStream_t st) {
     return HS_OK;
 }
 
-bool valid(hisparse_t h) { return h != nullptr && h->s.cache != nullptr; }
+// Live handles.  A destroyed handle is freed, so its pointer is checked
+// against this set before anything reads through it: a call with a null or
+// destroyed handle returns HS_E_HANDLE instead of touching freed memory.
+std::mutex& handles_mutex() {
+    static std::mutex m;
+    return m;
+}
+std::unordered_set<const hisparse_ctx*>& live_handles() {
+    static std::unordered_set<const hisparse_ctx*> set;
+    return set;
+}
+
+bool valid(hisparse_t h) {
+    if (h == nullptr) return false;
+    std::lock_guard<std::mutex> g(handles_mutex());
+    return live_handles().count(h) != 0 && h->s.cache != nullptr;
+}
 
 bool capturing(hipStream_t st) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -286,12 +304,20 @@ int hisparse_create(int num_req, int num_layers, int B, int W_KV, int dtype, con
         delete h;
         return rc;
     }
+    {
+        std::lock_guard<std::mutex> g(handles_mutex());
+        live_handles().insert(h);
+    }
     *out = h;
     return HS_OK;
 }
 
 int hisparse_destroy(hisparse_t h) {
     if (!valid(h)) return HS_E_HANDLE;
+    {
+        std::lock_guard<std::mutex> g(handles_mutex());
+        live_handles().erase(h);
+    }
     (void)hipDeviceSynchronize();
     free_all(h);
     h->s.cache = nullptr;

@@ -228,6 +228,12 @@ def test_synchronous_argument_errors(hs):
                                       s) == hs.HS_E_INVAL
     with pytest.raises(ValueError):
         res.resolve_layers([0, 1], [sel8], [out8, out8])
+    # a destroyed handle is refused, not read
+    h2 = hs.hisparse_create(2, 2, 32, 8, hs.BF16, hs.hs_host_pool(pool.ptr, w.pool_rows, w.L_ctx, None))
+    assert hs.hisparse_destroy(h2) == hs.HS_OK
+    assert hs.hisparse_destroy(h2) == hs.HS_E_HANDLE
+    assert hs.hisparse_resolve(h2, 0, sel8.data_ptr(), 8, out8.data_ptr(), s) == hs.HS_E_HANDLE
+    assert hs.hisparse_hbm_bytes(h2) == 0
     assert res.hbm_bytes() == hs.hisparse_kv_bytes(2, 2, 32, 8, hs.BF16) == 2 * 2 * 32 * 16
     res.close()
     pool.free()
