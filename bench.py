@@ -332,7 +332,6 @@ def main():
                                         "replay_launches": tim.replay_launches,
                                         "publish_avg_ms": tim.publish_ms / max(1, tim.publish_launches),
                                         "replay_GBps": (miss_bytes - fetch_bytes) / (tim.replay_ms * 1e-3) / 1e9}
-        meta_bytes_per_layer_step = w.num_req * (4 * w.k + 4 * w.B + 4 * w.B + 4 * w.k)
         result["kernels"] = {
             "fetch_avg_ms": fetch_avg_ms, "fetch_launches": tim.fetch_launches,
             "plan_avg_ms": plan_avg_ms, "plan_launches": tim.plan_launches,

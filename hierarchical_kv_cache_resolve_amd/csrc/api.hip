@@ -505,7 +505,8 @@ size_t hisparse_meta_bytes(hisparse_t h) {
     if (!valid(h)) return 0;
     const size_t nrl = static_cast<size_t>(h->R) * h->NL;
     return nrl * h->B * (sizeof(int32_t) + sizeof(uint32_t) + sizeof(int4) + 1) +
-           nrl * static_cast<size_t>(h->L_ctx) * sizeof(int32_t) + nrl * (3 * sizeof(int32_t) + sizeof(int64_t)) +
+           nrl * static_cast<size_t>(h->L_ctx) * sizeof(int32_t) +
+           nrl * (4 * sizeof(int32_t) + sizeof(int64_t)) +  // clock, miss count, status, length; region row
            static_cast<size_t>(h->NL) * 4 * sizeof(unsigned long long) + 4 * sizeof(int32_t);
 }
 

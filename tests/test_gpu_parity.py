@@ -235,6 +235,12 @@ def test_synchronous_argument_errors(hs):
     assert hs.hisparse_resolve(h2, 0, sel8.data_ptr(), 8, out8.data_ptr(), s) == hs.HS_E_HANDLE
     assert hs.hisparse_hbm_bytes(h2) == 0
     assert res.hbm_bytes() == hs.hisparse_kv_bytes(2, 2, 32, 8, hs.BF16) == 2 * 2 * 32 * 16
+    # metadata: per slot a position, a stamp, a plan entry and a hit-mask byte; per history a
+    # page table of L_ctx entries, four 32-bit words and the 64-bit region row; per layer four
+    # counters; the error word
+    nrl = 2 * 2
+    assert hs.hisparse_meta_bytes(res.h) == (nrl * 32 * (4 + 4 + 16 + 1) + nrl * w.L_ctx * 4 + nrl * (4 * 4 + 8)
+                                             + 2 * 4 * 8 + 16)
     res.close()
     pool.free()
 
