@@ -736,9 +736,12 @@ int hisparse_attend_mla(hisparse_t h, int layer, const void* d_q, int num_heads,
 static int probe(int kind, const void* src, void* dst, size_t bytes, int iters, void* stream, double* gbps) {
     if (!src || !dst || !gbps || bytes < 16 || (bytes % 16) != 0 || iters < 1) return HS_E_INVAL;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipEvent_t a, b;
+    hipEvent_t a = nullptr, b = nullptr;
     HS_TRY(hipEventCreate(&a));
-    HS_TRY(hipEventCreate(&b));
+    if (hipEventCreate(&b) != hipSuccess) {
+        (void)hipEventDestroy(a);
+        return HS_E_HIP;
+    }
     auto one = [&]() -> hipError_t {
         if (kind == 0) return hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, st);
         if (kind == 1) return hs::launch_link_read(src, dst, bytes, st);
