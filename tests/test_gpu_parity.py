@@ -415,3 +415,43 @@ def test_wide_launch_copies_multi_piece_rows(hs, w):
     assert res.error()[0] == 0
     res.close()
     pool.free()
+
+
+def test_instrumentation_changes_nothing(hs):
+    """Per-launch timing and phase stamps on: results still equal the oracle
+    bit for bit, every launch is counted, and each request-layer's stamps
+    (taken by its first wave in program order) never go backwards."""
+    from oracle import Oracle
+    w = wl("instrumented", num_req=4, num_layers=2, B=1024, k=512, L_ctx=20000, W_KV=8, steps=6)
+    tr = tg.trace(w)
+    pool = make_pool(hs, w)
+    pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
+    res = make_resolver(hs, w, pool)
+    res.set_option(hs.HS_OPT_TIMING, 1)
+    res.set_option(hs.HS_OPT_PHASE_TRACE, 1)
+    o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes)
+    dev = torch.device("cuda:0")
+    sel = torch.from_numpy(tr).to(dev)
+    out = torch.empty((w.num_req, w.k), dtype=torch.int32, device=dev)
+    order = [0, 1, 2, 11, 12, 3, 4, 5, 6, 7, 8, 9, 10]   # the bitmap probe's phases in program order
+    for t in range(w.steps):
+        for l in range(w.num_layers):
+            res.resolve(l, sel[t, l], out)
+            ref = o.resolve(l, tr[t, l], pool_np, w.region_rows())
+            assert np.array_equal(out.cpu().numpy(), ref["slot_idx"]), f"step {t} layer {l}"
+            stamps, ns = hs.hisparse_phase_trace(res.h, l, w.num_req)
+            assert ns > 0
+            for r in range(w.num_req):
+                seq = [int(stamps[r, i]) for i in order if stamps[r, i] != 0]
+                assert stamps[r, 0] != 0 and stamps[r, 10] != 0
+                assert seq == sorted(seq), f"stamps out of order, step {t} layer {l} request {r}"
+    tim = res.timing(clear=True)
+    assert tim.plan_launches == w.steps * w.num_layers == tim.fetch_launches
+    assert tim.dropped == 0 and tim.plan_ms > 0 and tim.fetch_ms > 0
+    st = res.state(w.num_layers - 1)
+    assert np.array_equal(st["slot_pos"], o.slot_pos[w.num_layers - 1])
+    assert res.error()[0] == 0
+    res.set_option(hs.HS_OPT_PHASE_TRACE, 0)
+    res.set_option(hs.HS_OPT_TIMING, 0)
+    res.close()
+    pool.free()
