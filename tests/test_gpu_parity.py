@@ -455,3 +455,28 @@ def test_instrumentation_changes_nothing(hs):
     res.set_option(hs.HS_OPT_TIMING, 0)
     res.close()
     pool.free()
+
+
+def test_fine_grained_pool(hs):
+    """A pool in fine-grained (coherent) pinned memory gives the same slots and
+    the same cached bytes as the oracle (the default pool is coarse-grained)."""
+    from oracle import Oracle
+    w = wl("coherent_pool", num_req=3, num_layers=2, B=600, k=300, L_ctx=5000, W_KV=72, steps=6)
+    tr = tg.trace(w)
+    pool = make_pool(hs, w, coherent=True)
+    pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
+    res = make_resolver(hs, w, pool)
+    o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes)
+    dev = torch.device("cuda:0")
+    sel = torch.from_numpy(tr).to(dev)
+    out = torch.empty((w.num_req, w.k), dtype=torch.int32, device=dev)
+    for t in range(w.steps):
+        for l in range(w.num_layers):
+            res.resolve(l, sel[t, l], out)
+            ref = o.resolve(l, tr[t, l], pool_np, w.region_rows())
+            assert np.array_equal(out.cpu().numpy(), ref["slot_idx"]), f"step {t} layer {l}"
+            occ = o.slot_pos[l] >= 0
+            assert np.array_equal(res.cache_layer(l)[occ], o.cache[l][occ]), f"cache step {t} layer {l}"
+    assert res.error()[0] == 0
+    res.close()
+    pool.free()
