@@ -480,3 +480,36 @@ def test_fine_grained_pool(hs):
     assert res.error()[0] == 0
     res.close()
     pool.free()
+
+
+@pytest.mark.parametrize("dtype,elem", [("FP8", 1), ("FP16", 2), ("FP32", 4)])
+def test_other_element_types(hs, dtype, elem):
+    """The element type only sets the record size (bytes are copied verbatim):
+    64-byte records of fp8, fp16 and fp32 elements resolve like bf16 ones,
+    slots and cached bytes equal to the oracle's, footprint identity exact."""
+    from oracle import Oracle
+    W_KV = 64 // elem
+    w = tg.Workload(f"elem_{dtype}", 3, 2, 4000, W_KV, elem, 200, 400, 5, tg.LOCALITY, 0.8, seed_index=130 + elem)
+    assert w.row_bytes == 64
+    tr = tg.trace(w)
+    pool = hs.HostPool.allocate(w.pool_rows * w.row_bytes)
+    pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
+    pool_np[:] = np.random.default_rng(elem).integers(0, 256, pool_np.shape, dtype=np.uint8)
+    res = hs.Resolver(w.num_req, w.num_layers, w.B, W_KV, getattr(hs, dtype), pool, w.L_ctx, w.pool_rows,
+                      region_row=w.region_rows())
+    assert res.hbm_bytes() == hs.hisparse_kv_bytes(w.num_req, w.num_layers, w.B, W_KV, getattr(hs, dtype)) \
+        == w.num_req * w.num_layers * w.B * 64
+    o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes)
+    dev = torch.device("cuda:0")
+    sel = torch.from_numpy(tr).to(dev)
+    out = torch.empty((w.num_req, w.k), dtype=torch.int32, device=dev)
+    for t in range(w.steps):
+        for l in range(w.num_layers):
+            res.resolve(l, sel[t, l], out)
+            ref = o.resolve(l, tr[t, l], pool_np, w.region_rows())
+            assert np.array_equal(out.cpu().numpy(), ref["slot_idx"]), f"step {t} layer {l}"
+            occ = o.slot_pos[l] >= 0
+            assert np.array_equal(res.cache_layer(l)[occ], o.cache[l][occ]), f"cache step {t} layer {l}"
+    assert res.error()[0] == 0
+    res.close()
+    pool.free()
