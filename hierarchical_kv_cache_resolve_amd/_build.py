@@ -6,7 +6,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["csrc/api.hip", "csrc/resolve.hip", "csrc/fetch.hip", "csrc/attend.hip"]
+SOURCES = ["csrc/api.hip", "csrc/resolve.hip", "csrc/resolve_bitmap.hip", "csrc/fetch.hip", "csrc/attend.hip"]
 LIB = os.path.join(HERE, "libhisparse.so")
 
 HIPCC_FLAGS = [
@@ -23,15 +23,23 @@ def hipcc() -> str:
 
 
 def build_library(verbose: bool = False) -> str:
-    objs = []
+    """Compile every HIP source (in parallel, one hipcc per file) and link."""
+    import concurrent.futures as cf
+    jobs = []
     for src in SOURCES:
         obj = os.path.join(HERE, os.path.basename(src) + ".o")
         cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(HERE, src), "-o", obj]
         cmd.remove("-shared")
-        if verbose:
-            print("+", " ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
-        objs.append(obj)
+        jobs.append((cmd, obj))
+    with cf.ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
+        futs = []
+        for cmd, _ in jobs:
+            if verbose:
+                print("+", " ".join(cmd), flush=True)
+            futs.append(ex.submit(subprocess.run, cmd, check=True))
+        for f in futs:
+            f.result()
+    objs = [o for _, o in jobs]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

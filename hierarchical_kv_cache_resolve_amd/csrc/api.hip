@@ -42,6 +42,7 @@ struct hisparse_ctx {
     std::vector<char> last_was_plan;
     std::vector<int64_t> steps;
     std::vector<int> last_k;
+    std::vector<const int32_t*> last_sel;  // selection of each layer's last planned resolve
     // timing ring
     struct Timed { hipEvent_t a, b; int kind; };
     std::vector<Timed> ring;
@@ -116,7 +117,7 @@ int init_state(hisparse_ctx* h, hipStream_t st) {
     HS_TRY(hipMemsetAsync(s.hit_mask, 0, nrl * h->B, st));
     HS_TRY(hipMemsetAsync(s.status, 0, nrl * sizeof(int32_t), st));
     HS_TRY(hipMemsetAsync(s.err, 0, 4 * sizeof(int32_t), st));
-    HS_TRY(hipMemsetAsync(s.stats, 0, static_cast<size_t>(h->NL) * 4 * sizeof(unsigned long long), st));
+    HS_TRY(hipMemsetAsync(s.stats, 0, nrl * 4 * sizeof(unsigned long long), st));
     HS_TRY(hipStreamSynchronize(st));
     std::fill(h->pending_anchor.begin(), h->pending_anchor.end(), -1);
     std::fill(h->join_outstanding.begin(), h->join_outstanding.end(), 0);
@@ -154,8 +155,12 @@ bool capturing(hipStream_t st) {
 }
 
 // Make `st` wait for `ev`.  Inside a graph capture, an event recorded before
-// the capture began cannot be waited on; such an event has completed (a
-// capture starts from an idle device), so the wait is dropped.
+// the capture began cannot be waited on, queried (a query invalidates a
+// global-mode capture) or waited on as an external event (the runtime of this
+// image crashes on it), so such a wait is dropped: the header makes it the
+// caller's contract that a capture begins after the library's earlier work on
+// the prefetch side stream has finished (a device synchronise, as
+// torch.cuda.graph does on entry).
 int wait_event(hipStream_t st, hipEvent_t ev, bool ev_in_capture) {
     if (capturing(st) && !ev_in_capture) return HS_OK;
     HS_TRY(hipStreamWaitEvent(st, ev, 0));
@@ -257,7 +262,7 @@ int hisparse_create(int num_req, int num_layers, int B, int W_KV, int dtype, con
     HS_ALLOC(hit_mask, uint8_t, nB)
     HS_ALLOC(status, int32_t, static_cast<size_t>(nrl))
     HS_ALLOC(err, int32_t, 4)
-    HS_ALLOC(stats, unsigned long long, static_cast<size_t>(num_layers) * 4)
+    HS_ALLOC(stats, unsigned long long, static_cast<size_t>(nrl) * 4)
     HS_ALLOC(length, int32_t, static_cast<size_t>(nrl))
 #undef HS_ALLOC
     if ((rc = alloc_dev(&p, sizeof(int64_t) * static_cast<size_t>(nrl))) != HS_OK) {
@@ -290,6 +295,7 @@ int hisparse_create(int num_req, int num_layers, int B, int W_KV, int dtype, con
     h->last_was_plan.assign(num_layers, 0);
     h->steps.assign(num_layers, 0);
     h->last_k.assign(num_layers, 0);
+    h->last_sel.assign(num_layers, nullptr);
     const std::vector<int32_t> full(static_cast<size_t>(nrl), static_cast<int32_t>(pool->L_ctx));
     if (hipMemcpy(h->d_region_row, region.data(), sizeof(int64_t) * region.size(), hipMemcpyHostToDevice) !=
             hipSuccess ||
@@ -364,6 +370,7 @@ static int resolve_plan_path(hisparse_t h, int n, const int* layers, const int32
         h->steps[l] += 1;
         h->last_was_plan[l] = 1;
         h->last_k[l] = k;
+        h->last_sel[l] = sel[i];
     }
     return HS_OK;
 }
@@ -386,6 +393,7 @@ int hisparse_resolve(hisparse_t h, int layer, const int32_t* d_sel, int k, int32
         lb.sel[0] = d_sel;
         lb.out[0] = d_slot_idx;
         lb.layer[0] = layer;
+        lb.anchor_sel[0] = h->last_sel[anchor];
         rc = timed(h, K_PUBLISH, st, [&] { return hs::launch_publish(h->s, lb, st); });
         if (rc != HS_OK) return rc;
         h->pending_anchor[layer] = -1;
@@ -480,6 +488,10 @@ int hisparse_set_lengths(hisparse_t h, const int64_t* lengths) {
     }
     HS_TRY(hipDeviceSynchronize());
     HS_TRY(hipMemcpy(h->s.length, dev.data(), sizeof(int32_t) * nrl, hipMemcpyHostToDevice));
+    // positions at or past a new length leave the cache (their records may be
+    // rewritten by later appends)
+    HS_TRY(hs::launch_trim(h->s, nullptr));
+    HS_TRY(hipDeviceSynchronize());
     return HS_OK;
 }
 
@@ -507,7 +519,7 @@ size_t hisparse_meta_bytes(hisparse_t h) {
     return nrl * h->B * (sizeof(int32_t) + sizeof(uint32_t) + sizeof(int4) + 1) +
            nrl * static_cast<size_t>(h->L_ctx) * sizeof(int32_t) +
            nrl * (4 * sizeof(int32_t) + sizeof(int64_t)) +  // clock, miss count, status, length; region row
-           static_cast<size_t>(h->NL) * 4 * sizeof(unsigned long long) + 4 * sizeof(int32_t);
+           nrl * 4 * sizeof(unsigned long long) + 4 * sizeof(int32_t);  // counters; error word
 }
 
 int hisparse_layer_state(hisparse_t h, int layer, hs_layer_state* out) {
@@ -553,16 +565,19 @@ int hisparse_clear_error(hisparse_t h) {
 int hisparse_stats(hisparse_t h, int layer, hs_stats* out) {
     if (!valid(h)) return HS_E_HANDLE;
     if (!out || layer < -1 || layer >= h->NL) return layer >= h->NL ? HS_E_LAYER : HS_E_INVAL;
-    std::vector<unsigned long long> st(static_cast<size_t>(h->NL) * 4);
+    std::vector<unsigned long long> st(static_cast<size_t>(h->NL) * h->R * 4);
     HS_TRY(hipDeviceSynchronize());
     HS_TRY(hipMemcpy(st.data(), h->s.stats, sizeof(unsigned long long) * st.size(), hipMemcpyDeviceToHost));
     std::memset(out, 0, sizeof *out);
     for (int l = 0; l < h->NL; ++l) {
         if (layer != -1 && l != layer) continue;
-        out->hits += st[4 * l];
-        out->misses += st[4 * l + 1];
-        out->miss_bytes += st[4 * l + 2];
-        out->resolves += st[4 * l + 3];
+        for (int r = 0; r < h->R; ++r) {
+            const unsigned long long* c = st.data() + 4 * (static_cast<size_t>(l) * h->R + r);
+            out->hits += c[0];
+            out->misses += c[1];
+            out->miss_bytes += c[2];
+            out->resolves += c[3];
+        }
     }
     return HS_OK;
 }

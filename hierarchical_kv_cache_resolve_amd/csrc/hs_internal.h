@@ -15,6 +15,8 @@
 //   hit_mask   uint8  [layer][req][B]
 //   status     int32  [layer][req]       0, or the device error code of the last step
 //   length     int32  [layer][req]       positions of the history written so far (<= L_ctx)
+//   stats      uint64 [layer][req][4]    hits, misses, miss bytes, resolves (each unit adds to
+//                                        its own counters only, so no two units contend)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,7 +44,7 @@ struct StateBase {
     uint8_t* hit_mask;
     int32_t* status;
     int32_t* err;                   // sticky {code, layer, req, detail}
-    unsigned long long* stats;      // [layer][4]: hits, misses, miss bytes, resolves
+    unsigned long long* stats;      // [layer][req][4]: hits, misses, miss bytes, resolves
     unsigned long long* phase;      // [layer][req][kPhaseSlots] wall-clock stamps, or null (off)
     uint8_t* pool;                  // device-visible pointer to the host pool
     int32_t* length;                // [layer][req] positions written so far in each history
@@ -55,14 +57,18 @@ struct StateBase {
 struct LayerBatch {
     const int32_t* sel[kMaxBatch];  // [R][k] per entry
     int32_t* out[kMaxBatch];        // [R][k] per entry
+    const int32_t* anchor_sel[kMaxBatch];  // publish only: the anchor's selection [R][k]
     int layer[kMaxBatch];
     int n;
     int k;
     int hash_bits;
     int probe;    // HS_PROBE_PAGE_TABLE, HS_PROBE_SLOT_SCAN or HS_PROBE_SLOT_SCAN_HASH
-    int lk_half;  // ints in each of the metadata kernel's two lookup arrays (set by launch_plan)
+    int lk_half;  // ints in each of the hash kernel's two lookup arrays (set by launch_plan)
+    int ngroups;  // bitmap kernel: 16-byte groups of position bits, ceil(L_ctx / 128)
+    int r1_ints;  // bitmap kernel: ints of its first LDS region
     int nt;       // non-temporal host loads and cache stores in the metadata kernel's own copy
     int copy;     // the metadata kernel copies the misses itself (set by launch_plan)
+    int trace;    // phase stamps on (s.phase is set)
 };
 
 struct FetchBatch {
@@ -80,6 +86,12 @@ struct ReplayBatch {
 // Host launchers (defined in the .hip files).
 size_t plan_lds_bytes(int k, int half, int B);
 hipError_t launch_plan(const StateBase& s, const LayerBatch& lb, hipStream_t st);
+// The bitmap metadata kernel (resolve_bitmap.hip): its LDS need, its lanes a
+// unit, and its launch (vec: k and B multiples of 4, arrays 16-byte aligned).
+size_t bitmap_lds_bytes(int k, int64_t L_ctx, bool wide);
+int bitmap_lanes(int B, int k, bool wide);
+hipError_t launch_bitmap_resolve(const StateBase& s, const LayerBatch& lb, bool wide, bool vec, hipStream_t st);
+hipError_t launch_trim(const StateBase& s, hipStream_t st);
 // Whether a metadata launch over n layers copies its own misses (a wide
 // launch: no fetch launch follows it).
 bool plan_copies_misses(const StateBase& s, int n);

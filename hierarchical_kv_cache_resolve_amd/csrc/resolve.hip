@@ -1,16 +1,19 @@
-// resolve.hip -- metadata half of RESOLVE on gfx950: hash build, cache probe,
-// miss compaction, LRU victim choice, metadata update and publication.
+// resolve.hip -- the metadata half of RESOLVE on gfx950 for histories whose
+// positions do not fit the LDS as a bitmap (or when a probe is forced): hash
+// build, cache probe, miss compaction, LRU victim choice, metadata update and
+// publication; also the shared layers' publish-only resolve, the replay of an
+// anchor's plan, and the trim of cached positions past a history's length.
 //
 // One 1024-lane workgroup (16 wave64s) per (request, layer); a batched launch
 // covers several independent layers with grid.y.  The five stages follow the
 // pith review's "Core claim" / "What carries the argument" (shared-memory hash
 // table over the selected positions, a parallel probe and scan to mark hits and
-// choose victims, page-table publication); where the history's positions fit,
-// the shared-memory structure is a bitmap over them with per-word ranks rather
-// than a hash, which gives each probe one lookup and no chains.  The host
-// fetch of the misses is the separate streaming kernel in fetch.hip, launched
-// right after on the same stream, because the miss rows of all requests are
-// best spread over the whole chip rather than over one workgroup per request.
+// choose victims, page-table publication).  The default lookup structure, a
+// bitmap over the history's positions, lives in resolve_bitmap.hip; launch_plan
+// picks it whenever it fits the LDS.  The host fetch of the misses is the
+// separate streaming kernel in fetch.hip, launched right after on the same
+// stream, because the miss rows of all requests are best spread over the whole
+// chip rather than over one workgroup per request.
 //
 // Determinism: victims are the m candidate slots with the smallest
 // (stamp, slot) keys, assigned in ascending slot order to the misses in
@@ -20,7 +23,7 @@
 // together, so the result does not depend on wave scheduling.
 #include <climits>
 
-#include "hs_internal.h"
+#include "hs_device.h"
 
 namespace hs {
 
@@ -42,24 +45,17 @@ enum : int {
     M_HIST = 82,     // [16] histogram-scan wave totals
     M_BIN = 98,      // crossing bin of the current radix pass
     M_BELOW = 99,    // candidates below the crossing bin
-    M_RANK = 100,    // first rank not yet handed to a wave (bitmap probe)
 };
 
 // How the slot-scan probe maps a cached position to its selection index.
 enum : int {
     PROBE_TABLE = 0,   // no slot scan: page-table lookups
     PROBE_HASH = 1,    // bucketed LDS hash of the selection
-    PROBE_BITMAP = 2,  // LDS bitmap of the selected positions with per-word ranks
 };
 
 __device__ inline unsigned hash_bucket(int p, int bucket_bits) {
     // multiplicative hashing with the golden-ratio constant (Knuth, TAOCP 6.4)
     return bucket_bits > 0 ? (static_cast<unsigned>(p) * 0x9E3779B1u) >> (32 - bucket_bits) : 0u;
-}
-
-__device__ inline unsigned long long lanemask_lt() {
-    const int lane = threadIdx.x & 63;
-    return lane ? (~0ull >> (64 - lane)) : 0ull;
 }
 
 // LDS carve-up of the metadata kernel (ints): the lookup structure's two
@@ -128,54 +124,6 @@ __device__ inline int bucket_find(const PlanLds& l, unsigned nbm, int bucket_bit
         if (kk.w == kEmpty) return -1;  // entries fill in order: a bucket with room ends the chain
         b = (b + 1) & nbm;
     }
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave with DPP: four row shifts
-// scan each row of 16 lanes, then row broadcasts add lane 15's total into
-// rows 1 and 3 and lane 31's into rows 2 and 3.
-__device__ inline int wave_incl_scan(int x) {
-    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-    return x;
-}
-
-__device__ inline unsigned wave_min(unsigned v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = min(v, static_cast<unsigned>(__shfl_xor(static_cast<int>(v), off, 64)));
-    return v;
-}
-
-__device__ inline unsigned wave_max(unsigned v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<unsigned>(__shfl_xor(static_cast<int>(v), off, 64)));
-    return v;
-}
-
-// Sum of words[0 .. n) (n <= 16) of a block scan's per-wave partials, for
-// every lane: lane i < n of the wave reads word i (one LDS read), the first
-// row of 16 lanes adds up with four DPP row shifts, and lane 15 holds the sum.
-static_assert(kPlanWaves == 16, "one row of 16 lanes holds the per-wave partials");
-__device__ inline int sum_before(const int* words, int n) {
-    const int lane = static_cast<int>(threadIdx.x) & 63;
-    int v = lane < n ? words[lane & (kPlanWaves - 1)] : 0;
-    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
-    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
-    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
-    return __builtin_amdgcn_readlane(v, 15);
-}
-
-// The workgroup's wave index as a wave-uniform (scalar) value.
-__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6); }
-
-// Block-wide OR of a small flag word: lanes holding a non-zero value OR it
-// into one LDS word (the word must be zero before; read it after a barrier).
-__device__ inline void block_or_into(int* word, int v) {
-    if (__ballot(v != 0) != 0ull && v != 0) atomicOr(word, v);
 }
 
 // Per-lane contiguous slot range [tid*PER, tid*PER + PER), moved as 16-byte
@@ -255,22 +203,6 @@ __device__ inline void reject(const StateBase& s, int32_t* out, int k, int64_t r
             for (int i_ = 0; i_ < 13; ++i_) s.phase[rl * kPhaseSlots + i_] = stamp[i_]; \
     } while (0)
 
-
-// Histogram increment for this lane's bin (-1: none).  When every active
-// lane of the wave has the same bin (an empty cache, or one stamp shared by
-// the whole wave) a single atomic adds the count; otherwise one atomic per
-// lane.  Called by all lanes of the wave.
-__device__ inline void hist_add(int* hist, int bin) {
-    const unsigned long long act = __ballot(bin >= 0);
-    if (act == 0ull) return;
-    const int lead = __ffsll(static_cast<long long>(act)) - 1;
-    const int b0 = __shfl(bin, lead, 64);
-    if (__ballot(bin == b0) == act) {
-        if ((threadIdx.x & 63) == lead) atomicAdd(&hist[b0], __popcll(act));
-    } else if (bin >= 0) {
-        atomicAdd(&hist[bin], 1);
-    }
-}
 
 // With l.hist holding counts per bin (bin b at index b), find the bin where
 // the count taken from the top bin downwards first reaches `need`; `below`
@@ -404,13 +336,9 @@ __device__ inline void copy_misses(const StateBase& s, const PlanLds& l, int64_t
 //   2. page-table probe: hits are marked in an LDS bitmap over the slots (a
 //      slot claimed twice means a repeated position); the positions that
 //      missed go into an LDS hash table, which catches repeats among them.
-//      Slot-scan probe: every selected position goes into an LDS lookup
-//      structure (a repeat is caught on insertion) and every cached slot's
-//      position is looked up in it.  The structure is the hash table, or,
-//      when the history's positions fit, a bitmap over them with the rank
-//      of each word (selected positions in the words before it): the rank of
-//      a position is then its index among the selected positions in
-//      ascending order, which maps it to its selection index in O(1);
+//      Slot-scan probe: every selected position goes into the LDS hash (a
+//      repeat is caught on insertion) and every cached slot's position is
+//      looked up in it;
 //   3. misses are compacted in ascending j with wave ballots;
 //   4. the m victims are the non-hit slots with the smallest (stamp, slot)
 //      keys (radix select on the stamps, then one ballot-counted pass);
@@ -441,9 +369,6 @@ void plan_kernel(StateBase s, LayerBatch lb) {
     uint32_t* ts_g = s.ts + rl * B;
     int32_t* pt = s.page_table + rl * s.L_ctx;
     const PlanLds l = carve(lds_raw, lb.lk_half, k, B);
-    // bitmap probe: word w of the position bitmap, and the rank of word w
-    unsigned* const pbits = reinterpret_cast<unsigned*>(l.bkey);
-    int* const prank = l.bval;
     const unsigned long long lt = lanemask_lt();
     unsigned long long stamp[13] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     HS_PHASE(0);
@@ -483,16 +408,8 @@ void plan_kernel(StateBase s, LayerBatch lb) {
         }
     }
 
-    if constexpr (PROBE == PROBE_BITMAP) {
-        // the whole region, padding words included (ranks read 16-byte groups)
-        for (int i = tid; i < (lb.lk_half >> 2); i += kPlanThreads)
-            reinterpret_cast<uint4*>(pbits)[i] = make_uint4(0u, 0u, 0u, 0u);
-    } else {
-        for (int i = tid; i < H; i += kPlanThreads) l.bkey[i] = kEmpty;
-    }
-    if constexpr (PROBE == PROBE_BITMAP) {
-        for (int j = tid; j < k; j += kPlanThreads) l.mlist[j] = -1;  // slot by rank
-    } else if constexpr (PROBE == PROBE_HASH) {
+    for (int i = tid; i < H; i += kPlanThreads) l.bkey[i] = kEmpty;
+    if constexpr (PROBE == PROBE_HASH) {
         for (int j = tid; j < k; j += kPlanThreads) l.sidx[j] = -1;
     } else {
         for (int i = tid; i < hitmap_words(B); i += kPlanThreads) l.hitmap[i] = 0u;
@@ -511,14 +428,7 @@ void plan_kernel(StateBase s, LayerBatch lb) {
             const int p = selv[q];
             const int slot = ptv[q];
             l.sel[j] = p;
-            if constexpr (PROBE == PROBE_BITMAP) {
-                // p < L_ctx here (a lane with a bad position inserts nothing)
-                const unsigned bit = 1u << (p & 31);
-                if (atomicOr(&pbits[p >> 5], bit) & bit) {
-                    bad |= 2;
-                    bad_at = j + 1;
-                }
-            } else if constexpr (PROBE == PROBE_HASH) {
+            if constexpr (PROBE == PROBE_HASH) {
                 if (!bucket_insert(l, nbm, bucket_bits, p, j)) {
                     bad |= 2;
                     bad_at = j + 1;
@@ -555,59 +465,7 @@ void plan_kernel(StateBase s, LayerBatch lb) {
     }
     // this lane's slots that hold a selected position
     unsigned hitbits = 0;
-    if constexpr (PROBE == PROBE_BITMAP) {
-        // ranks: lane tid owns the contiguous 16-byte groups of words
-        // [tid*gpl, tid*gpl + gpl), read and written whole
-        const int ng = lb.lk_half >> 2;
-        const int gpl = (ng + kPlanThreads - 1) / kPlanThreads;
-        const int g0 = tid * gpl;
-        const uint4* pb4 = reinterpret_cast<const uint4*>(pbits);
-        int cnt = 0;
-        for (int i = 0; i < gpl; ++i) {
-            if (g0 + i < ng) {
-                const uint4 v = pb4[g0 + i];
-                cnt += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
-            }
-        }
-        const int incl = wave_incl_scan(cnt);
-        // each wave takes a run of ranks with one LDS atomic: whatever order
-        // the waves' adds land in, the k selected positions map one to one
-        // onto [0, k) (ascending within a wave's words), and no barrier is
-        // needed before the ranks are written
-        int wbase = 0;
-        if (lane == 63) wbase = atomicAdd(&l.misc[M_RANK], incl);
-        int base = __builtin_amdgcn_readlane(wbase, 63) + incl - cnt;
-        HS_PHASE(11);
-        for (int i = 0; i < gpl; ++i) {
-            if (g0 + i < ng) {
-                const uint4 v = pb4[g0 + i];
-                int4 rk;
-                rk.x = base;
-                rk.y = rk.x + __popc(v.x);
-                rk.z = rk.y + __popc(v.y);
-                rk.w = rk.z + __popc(v.z);
-                base = rk.w + __popc(v.w);
-                reinterpret_cast<int4*>(prank)[g0 + i] = rk;
-            }
-        }
-        __syncthreads();
-        HS_PHASE(12);
-        // each cached slot holding a selected position records itself at the
-        // position's rank (slot by rank, in the miss list's storage, cleared
-        // to -1 at the start); the miss list maps ranks back to selections
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            const int p = spos[q];
-            if (s0 + q < B && p >= 0 && p < s.L_ctx) {
-                const unsigned word = pbits[p >> 5];
-                if ((word >> (p & 31)) & 1u) {
-                    l.mlist[prank[p >> 5] + __popc(word & ((1u << (p & 31)) - 1u))] = s0 + q;
-                    hitbits |= 1u << q;
-                }
-            }
-        }
-        __syncthreads();
-    } else if constexpr (PROBE == PROBE_HASH) {
+    if constexpr (PROBE == PROBE_HASH) {
         // the pages' probe: every cached position looked up in the hash
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
@@ -636,21 +494,7 @@ void plan_kernel(StateBase s, LayerBatch lb) {
     for (int q = 0; q < SPL; ++q) {
         if (q < kper) {
             const int j = j0 + q;
-            bool f;
-            if constexpr (PROBE == PROBE_BITMAP) {
-                // the slot recorded at this selection's rank, or -1 (a miss);
-                // the slot-by-rank array is overwritten by the miss list only
-                // after the barrier below
-                f = false;
-                if (j < k) {
-                    const int p = l.sel[j];
-                    const int v = l.mlist[prank[p >> 5] + __popc(pbits[p >> 5] & ((1u << (p & 31)) - 1u))];
-                    l.sidx[j] = v;
-                    f = v < 0;
-                }
-            } else {
-                f = j < k && l.sidx[j] < 0;
-            }
+            const bool f = j < k && l.sidx[j] < 0;
             mflags |= static_cast<unsigned>(f) << q;
             const unsigned long long bm = __ballot(f);
             mpre += __popcll(bm & lt);
@@ -807,7 +651,7 @@ void plan_kernel(StateBase s, LayerBatch lb) {
         s.miss_count[rl] = m;
         s.status[rl] = 0;
         s.clock[rl] = t + 1u;
-        unsigned long long* st = s.stats + 4 * layer;
+        unsigned long long* st = s.stats + 4 * rl;
         atomicAdd(st + 0, static_cast<unsigned long long>(h));
         atomicAdd(st + 1, static_cast<unsigned long long>(m));
         atomicAdd(st + 2, static_cast<unsigned long long>(m) * static_cast<unsigned long long>(s.row_bytes));
@@ -844,10 +688,17 @@ __global__ __launch_bounds__(kPlanThreads) void publish_kernel(StateBase s, Laye
     for (int i = tid; i < (B + 31) / 32; i += kPlanThreads) pub_bits[i] = 0u;
     if (tid == 0) pub_flags = 0;
     __syncthreads();
-    int bad_range = 0, bad_dup = 0, bad_res = 0, bad_at = -1;
+    int bad_range = 0, bad_dup = 0, bad_res = 0, bad_div = 0, bad_at = -1;
     const int64_t hist_len = s.length[rl];
+    const int32_t* asel = lb.anchor_sel[blockIdx.y] + static_cast<int64_t>(r) * k;
     for (int j = tid; j < k; j += kPlanThreads) {
         const int p = sel[j];
+        if (p != asel[j]) {
+            // not the selection the anchor resolved (another order or another
+            // set): its hit mask and stamps would not be this layer's own
+            bad_div = 1;
+            bad_at = j;
+        }
         if (p < 0 || static_cast<int64_t>(p) >= s.L_ctx) {
             bad_range = 1;
             bad_at = j;
@@ -870,11 +721,14 @@ __global__ __launch_bounds__(kPlanThreads) void publish_kernel(StateBase s, Laye
             bad_at = j;
         }
     }
-    block_or_into(&pub_flags, bad_range | (bad_dup << 1) | (bad_res << 2));
+    block_or_into(&pub_flags, bad_range | (bad_dup << 1) | (bad_res << 2) | (bad_div << 3));
     __syncthreads();
     const int fl = pub_flags;
     if (fl) {
-        const int code = (fl & 1) ? HS_DEV_RANGE : ((fl & 2) ? HS_DEV_DUP : HS_DEV_NOT_RESIDENT);
+        const int code = (fl & 1)   ? HS_DEV_RANGE
+                         : (fl & 2) ? HS_DEV_DUP
+                         : (fl & 8) ? HS_DEV_DIVERGED
+                                    : HS_DEV_NOT_RESIDENT;
         for (int j = tid; j < k; j += kPlanThreads) out[j] = -1;
         if (tid == 0) record_error(s.err, code, layer, r, bad_at);
         return;
@@ -948,11 +802,33 @@ __global__ __launch_bounds__(kPlanThreads) void replay_meta_kernel(StateBase s, 
         s.miss_count[rs] = m;
         s.status[rs] = 0;
         s.clock[rs] = s.clock[ra];
-        unsigned long long* st = s.stats + 4 * L2;
+        unsigned long long* st = s.stats + 4 * rs;
         atomicAdd(st + 0, static_cast<unsigned long long>(rb.k - m));
         atomicAdd(st + 1, static_cast<unsigned long long>(m));
         atomicAdd(st + 2, static_cast<unsigned long long>(m) * static_cast<unsigned long long>(s.row_bytes));
         atomicAdd(st + 3, 1ull);
+    }
+}
+
+// Drop every cached position at or past its history's length (after the
+// lengths were lowered): the slot becomes empty (stamp 0) and the position
+// host-only, so a record later rewritten at that position is fetched again
+// rather than served from the old copy -- the host pool is the authoritative
+// copy (blog section 2, item 1).  One workgroup per (request, layer).
+__global__ __launch_bounds__(256) void trim_kernel(StateBase s) {
+    const int r = blockIdx.x, layer = blockIdx.y;
+    const int64_t rl = static_cast<int64_t>(layer) * s.R + r;
+    const int len = s.length[rl];
+    int32_t* spos = s.slot_pos + rl * s.B;
+    uint32_t* ts = s.ts + rl * s.B;
+    int32_t* pt = s.page_table + rl * s.L_ctx;
+    for (int i = threadIdx.x; i < s.B; i += 256) {
+        const int p = spos[i];
+        if (p >= len) {
+            pt[p] = -1;
+            spos[i] = kEmpty;
+            ts[i] = 0u;
+        }
     }
 }
 
@@ -997,7 +873,6 @@ template <int PER>
 static hipError_t launch_plan_p(const StateBase& s, const LayerBatch& lb, size_t lds, int probe, bool wide,
                                 hipStream_t st) {
     switch (probe) {
-        case PROBE_BITMAP: return launch_plan_s<PER, PROBE_BITMAP>(s, lb, lds, wide, st);
         case PROBE_HASH: return launch_plan_s<PER, PROBE_HASH>(s, lb, lds, wide, st);
         default: return launch_plan_s<PER, PROBE_TABLE>(s, lb, lds, wide, st);
     }
@@ -1017,24 +892,19 @@ hipError_t launch_plan(const StateBase& s, const LayerBatch& lb_in, hipStream_t 
     LayerBatch lb = lb_in;
     const bool wide = plan_is_wide(s, lb.n);
     lb.copy = plan_copies_misses(s, lb.n) ? 1 : 0;
-    const int H = 1 << lb.hash_bits;
-    int probe = PROBE_TABLE;
-    lb.lk_half = H;
-    if (lb.probe == HS_PROBE_SLOT_SCAN_HASH) {
-        probe = PROBE_HASH;
-    } else if (lb.probe == HS_PROBE_SLOT_SCAN) {
-        // the bitmap over the history's positions when its two arrays fit the
-        // LDS the launch can give without losing workgroups per CU (80 KB for
-        // two per CU, 160 KB for one), or take no more than the hash's
-        probe = PROBE_HASH;
-        const int nw4 = static_cast<int>(((static_cast<int64_t>(s.L_ctx) + 127) >> 7) << 2);
-        const size_t with_bitmap = plan_lds_bytes(lb.k, nw4, s.B);
-        const size_t cap = wide ? 80 * 1024 : 160 * 1024;
-        if (with_bitmap <= cap || with_bitmap <= plan_lds_bytes(lb.k, H, s.B)) {
-            probe = PROBE_BITMAP;
-            lb.lk_half = nw4;
-        }
+    lb.trace = s.phase != nullptr ? 1 : 0;
+    if (lb.probe == HS_PROBE_SLOT_SCAN && bitmap_lds_bytes(lb.k, s.L_ctx, wide) <= 160 * 1024) {
+        // the default: a bitmap over the history's positions, whenever it
+        // fits the LDS of one CU.  Runs move as 16-byte vectors when k and B
+        // are multiples of 4 and the caller's arrays are 16-byte aligned.
+        bool vec = (lb.k & 3) == 0 && (s.B & 3) == 0;
+        for (int i = 0; i < lb.n && vec; ++i)
+            vec = (reinterpret_cast<uintptr_t>(lb.sel[i]) & 15u) == 0 && (reinterpret_cast<uintptr_t>(lb.out[i]) & 15u) == 0;
+        return launch_bitmap_resolve(s, lb, wide, vec, st);
     }
+    const int H = 1 << lb.hash_bits;
+    const int probe = lb.probe == HS_PROBE_PAGE_TABLE ? PROBE_TABLE : PROBE_HASH;
+    lb.lk_half = H;
     const size_t lds = plan_lds_bytes(lb.k, lb.lk_half, s.B);
     const int per = (s.B + kPlanThreads - 1) / kPlanThreads;
     if (per <= 1) return launch_plan_p<1>(s, lb, lds, probe, wide, st);
@@ -1057,6 +927,11 @@ hipError_t launch_replay_meta(const StateBase& s, const ReplayBatch& rb, hipStre
     const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(&replay_meta_kernel), lds, granted);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(replay_meta_kernel, dim3(s.R, rb.n), dim3(kPlanThreads), lds, st, s, rb);
+    return hipGetLastError();
+}
+
+hipError_t launch_trim(const StateBase& s, hipStream_t st) {
+    hipLaunchKernelGGL(trim_kernel, dim3(s.R, s.NL), dim3(256), 0, st, s);
     return hipGetLastError();
 }
 

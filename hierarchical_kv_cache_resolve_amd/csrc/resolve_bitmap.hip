@@ -1,0 +1,746 @@
+// resolve_bitmap.hip -- the metadata half of RESOLVE on gfx950 when the
+// history's positions fit the LDS as a bitmap (every workload here).
+//
+// One workgroup of NT lanes (512 or 1024) per (request, layer); a batched
+// launch covers several independent layers with grid.y.  The stages follow
+// the pith review's "Core claim" and "What carries the argument" and the
+// blog's section 3 ("RESOLVE: Five Stages in One Launch"): a lookup
+// structure over the selected positions in shared memory, every cached slot
+// probed against it to mark hits, LRU victims for the misses (hits ranked
+// above newly fetched misses), then metadata update and publication.  The
+// lookup structure is a bitmap over the history's positions plus the rank of
+// each 16-byte group of bitmap words: the rank of a selected position is its
+// index among the selected positions, so a position maps to its selection in
+// O(1) with no probe chains.
+//
+// The kernel is laid out for the all-hit case, which decides the cost of a
+// layer whose selection barely moves: five barriers, every hit published as
+// soon as the selection side finds it, each lane's run of hit stamps written
+// back as whole 16-byte pieces.  Only a unit with misses goes on to the
+// victim search (age histogram, threshold, slot-order ranking), and there
+// the lane that takes a victim slot publishes the miss itself.
+//
+// Determinism: victims are the m candidate slots with the smallest
+// (stamp, slot) keys, assigned in ascending slot order to the misses in
+// ascending selection order, whatever the order in which waves run.
+#include "hs_device.h"
+
+namespace hs {
+
+namespace {
+
+constexpr int kEmpty = -1;
+constexpr int kHistQ = kHistBins / 64;  // histogram bins per lane of a wave that scans all of them
+
+// Words of the misc block (each scan owns its own words, so one scan's
+// partials never have to be drained before the next scan writes its own).
+enum : int {
+    X_FLAGS = 0,    // bit 0: a position outside the history, bit 1: a repeated position
+    X_BADAT = 1,    // largest offending selection index + 1
+    X_RANK = 2,     // first group rank not yet handed to a wave
+    X_BIN = 3,      // radix select: crossing bin of the current pass
+    X_BELOW = 4,    // radix select: candidates below it
+    X_MISS = 16,    // [16] per-wave inclusive miss counts
+    X_VICT = 32,    // [16] per-wave packed (strict | tie << 16) victim counts
+    X_HIST = 48,    // [16] radix-scan partials
+    X_MIN = 64,     // [16] per-wave minimum candidate stamp
+    X_MAX = 80,     // [16] per-wave maximum candidate stamp
+    X_STAMP = 96,   // [2 * 11] phase stamps of wave 0 while tracing
+    kMiscWords = 128,
+};
+
+// A lane's contiguous run v[0..N) of elements i0 .. i0+N-1 of g, in pieces of
+// W = min(N, 4) elements when VEC (the caller guarantees n % 4 == 0 and
+// 16-byte alignment, so each piece lies wholly inside or outside [0, n));
+// element by element otherwise.  Elements outside [0, n) read as `fill`.
+// The loads are unconditional, from an address clamped into [0, n), so no
+// loaded value is merged across a branch (which would make the wave wait for
+// it on the spot instead of where it is used).
+template <int N, bool VEC, typename T>
+__device__ inline void load_run(const T* g, int i0, int n, T (&v)[N], T fill) {
+    constexpr int W = N < 4 ? N : 4;
+    if constexpr (VEC && W == 4) {
+#pragma unroll
+        for (int q = 0; q < N; q += 4) {
+            const bool in = i0 + q < n;
+            const uint4 w = *reinterpret_cast<const uint4*>(g + (in ? i0 + q : n - 4));
+            v[q] = in ? static_cast<T>(w.x) : fill;
+            v[q + 1] = in ? static_cast<T>(w.y) : fill;
+            v[q + 2] = in ? static_cast<T>(w.z) : fill;
+            v[q + 3] = in ? static_cast<T>(w.w) : fill;
+        }
+    } else if constexpr (VEC && W == 2) {
+        const bool in = i0 < n;
+        const uint2 w = *reinterpret_cast<const uint2*>(g + (in ? i0 : n - 2));
+        v[0] = in ? static_cast<T>(w.x) : fill;
+        v[1] = in ? static_cast<T>(w.y) : fill;
+    } else {
+#pragma unroll
+        for (int q = 0; q < N; ++q) {
+            const bool in = i0 + q < n;
+            const T w = g[in ? i0 + q : n - 1];
+            v[q] = in ? w : fill;
+        }
+    }
+}
+
+// Store the pieces of a run that hold at least one element flagged in
+// `mask` (bit q: element q); same piece layout as load_run.
+template <int N, bool VEC, typename T>
+__device__ inline void store_run_masked(T* g, int i0, int n, const T (&v)[N], unsigned mask) {
+    constexpr int W = N < 4 ? N : 4;
+    if constexpr (VEC && W == 4) {
+#pragma unroll
+        for (int q = 0; q < N; q += 4) {
+            if ((mask >> q) & 0xFu) {
+                *reinterpret_cast<uint4*>(g + i0 + q) =
+                    make_uint4(static_cast<unsigned>(v[q]), static_cast<unsigned>(v[q + 1]),
+                               static_cast<unsigned>(v[q + 2]), static_cast<unsigned>(v[q + 3]));
+            }
+        }
+    } else if constexpr (VEC && W == 2) {
+        if (mask & 3u)
+            *reinterpret_cast<uint2*>(g + i0) = make_uint2(static_cast<unsigned>(v[0]), static_cast<unsigned>(v[1]));
+    } else {
+#pragma unroll
+        for (int q = 0; q < N; ++q)
+            if (((mask >> q) & 1u) && i0 + q < n) g[i0 + q] = v[q];
+    }
+}
+
+// Rank of position p among the selected positions (its bit must be set):
+// the rank of its 16-byte group plus the set bits before it in the group.
+__device__ inline bool bitmap_rank(const uint4* bits4, const int* grank, int p, int& rank) {
+    const uint4 g = bits4[p >> 7];
+    const int base = grank[p >> 7];
+    const int wi = (p >> 5) & 3;
+    const unsigned w = wi == 0 ? g.x : (wi == 1 ? g.y : (wi == 2 ? g.z : g.w));
+    const unsigned bit = 1u << (p & 31);
+    rank = base + __popc(w & (bit - 1u)) + (wi > 0 ? __popc(g.x) : 0) + (wi > 1 ? __popc(g.y) : 0) +
+           (wi > 2 ? __popc(g.z) : 0);
+    return (w & bit) != 0u;
+}
+
+// The age bin where the count taken from the oldest bin downwards first
+// reaches `need`, and the count of the bins above it.  Every wave computes it
+// on its own from the finished histogram (no barrier, no broadcast): lane i
+// covers the 16 bins [1008 - 16i, 1023 - 16i].
+__device__ inline void crossing_from_top(const int* hist, int need, int& bin, int& below) {
+    const int lane = threadIdx.x & 63;
+    const int lo = kHistBins - kHistQ * (lane + 1);
+    int h[kHistQ];
+#pragma unroll
+    for (int i = 0; i < kHistQ; i += 4) {
+        const int4 v = *reinterpret_cast<const int4*>(hist + lo + i);
+        h[i] = v.x;
+        h[i + 1] = v.y;
+        h[i + 2] = v.z;
+        h[i + 3] = v.w;
+    }
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < kHistQ; ++i) c += h[i];
+    const int incl = wave_incl_scan(c);
+    int acc = incl - c, my_bin = -1, my_below = 0;
+#pragma unroll
+    for (int i = kHistQ - 1; i >= 0; --i) {
+        if (my_bin < 0 && acc < need && need <= acc + h[i]) {
+            my_bin = lo + i;
+            my_below = acc;
+        }
+        acc += h[i];
+    }
+    const unsigned long long found = __ballot(my_bin >= 0);
+    const int L = __ffsll(static_cast<long long>(found)) - 1;
+    bin = __builtin_amdgcn_readlane(my_bin, L);
+    below = __builtin_amdgcn_readlane(my_below, L);
+}
+
+// Fallback threshold search among the slots flagged in `elig` (this lane's
+// run): the m-th smallest stamp T and how many slots stamped exactly T are
+// taken.  Min/max reduction, then a radix select over stamps relative to the
+// minimum in 10-bit digits from the top.  Expects hist zeroed; leaves it
+// zeroed.  Barriers inside; every lane of the workgroup must call it.
+template <int NT, int PER>
+__device__ inline void radix_select(int* hist, int* misc, const uint32_t (&tsv)[PER], unsigned elig, int m,
+                                    uint32_t& T, int& need_eq) {
+    constexpr int NW = NT / 64, BPL = kHistBins / NT;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    unsigned mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        if ((elig >> q) & 1u) {
+            mn = min(mn, tsv[q]);
+            mx = max(mx, tsv[q]);
+        }
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) {
+        misc[X_MIN + wave] = static_cast<int>(mn);
+        misc[X_MAX + wave] = static_cast<int>(mx);
+    }
+    __syncthreads();
+    mn = 0xFFFFFFFFu;
+    mx = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        mn = min(mn, static_cast<unsigned>(misc[X_MIN + w]));
+        mx = max(mx, static_cast<unsigned>(misc[X_MAX + w]));
+    }
+    if (mn == mx) {
+        T = mn;
+        need_eq = m;
+        return;
+    }
+    const int nbits = 32 - __clz(static_cast<int>(mx - mn));
+    uint64_t prefix = 0;
+    int remaining = m, pos = nbits;
+    while (pos > 0) {
+        const int d = pos < 10 ? pos : 10;
+        pos -= d;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            int bin = -1;
+            if ((elig >> q) & 1u) {
+                const uint64_t rel = static_cast<uint64_t>(tsv[q] - mn);
+                if ((rel >> (pos + d)) == prefix) bin = static_cast<int>((rel >> pos) & ((1u << d) - 1u));
+            }
+            hist_add(hist, bin);
+        }
+        __syncthreads();
+        // lane tid owns bins [tid*BPL, tid*BPL + BPL): read and zero them, then
+        // a block scan finds the bin where the count from the bottom reaches
+        // `remaining`
+        int hb[BPL], c = 0;
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+            hb[i] = hist[tid * BPL + i];
+            hist[tid * BPL + i] = 0;
+            c += hb[i];
+        }
+        const int incl = wave_incl_scan(c);
+        if (lane == 63) misc[X_HIST + wave] = incl;
+        __syncthreads();
+        int acc = incl - c + sum_before(misc + X_HIST, wave);
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+            if (acc < remaining && remaining <= acc + hb[i]) {
+                misc[X_BIN] = tid * BPL + i;
+                misc[X_BELOW] = acc;
+            }
+            acc += hb[i];
+        }
+        __syncthreads();
+        prefix = (prefix << d) | static_cast<uint64_t>(misc[X_BIN]);
+        remaining -= misc[X_BELOW];
+    }
+    T = mn + static_cast<uint32_t>(prefix);
+    need_eq = remaining;
+}
+
+// Phase stamps (constant-rate clock) while tracing is on: lane 0 of wave 0
+// keeps them in the misc block (no long-lived scalar registers) and writes
+// them out at the end.  Slots in program order: 0 start, 1 reads issued and
+// LDS cleared, 2 selection inserted, 3 ranks, 4 slot side, 5 selection side,
+// 6 miss list and histogram, 7 threshold, 8 victim ranks, 9 metadata
+// written, 10 end.
+#define HB_PHASE(i)                                                                      \
+    do {                                                                                 \
+        if (lb.trace && tid == 0)                                                        \
+            reinterpret_cast<unsigned long long*>(misc + X_STAMP)[(i)] = wall_clock64(); \
+    } while (0)
+#define HB_PHASE_FLUSH()                                                                                 \
+    do {                                                                                                 \
+        if (lb.trace && tid == 0) {                                                                      \
+            const unsigned long long* st_ = reinterpret_cast<const unsigned long long*>(misc + X_STAMP); \
+            for (int i_ = 0; i_ < 11; ++i_) s.phase[rl * kPhaseSlots + i_] = st_[i_];                    \
+        }                                                                                                \
+    } while (0)
+
+// Per-unit counters and the end of a step: miss count, status, clock.  The
+// status and counter arrays are read from the arguments here, at the end, so
+// they hold no registers before.
+__device__ inline void finish_unit(const StateBase& s, uint32_t* clock_u, int32_t* mc_u, int64_t rl, uint32_t t,
+                                   int k, int m) {
+    *mc_u = m;
+    s.status[rl] = 0;
+    *clock_u = t + 1u;
+    unsigned long long* st = s.stats + 4 * rl;
+    atomicAdd(st + 0, static_cast<unsigned long long>(k - m));
+    if (m > 0) {
+        atomicAdd(st + 1, static_cast<unsigned long long>(m));
+        atomicAdd(st + 2, static_cast<unsigned long long>(m) * static_cast<unsigned long long>(s.row_bytes));
+    }
+    atomicAdd(st + 3, 1ull);
+}
+
+// Copy the m missed rows of one (request, layer) from the host pool into
+// their victim slots (launches over many request-layers, where no separate
+// fetch launch follows): miss i reads position mpos[i] into slot msl[i].
+// Same flat (row, 16-byte piece) order and 16-byte loads as the fetch kernel.
+template <int NT, bool NTL>
+__device__ inline void copy_misses(const StateBase& s, const int* mpos, const int* msl, int64_t rl, int r, int layer,
+                                   int m) {
+    constexpr int U = 4;
+    const int row16 = static_cast<int>(s.row_bytes >> 4);
+    const int total = m * row16;
+    const uint8_t* src_base = s.pool + s.region_row[static_cast<int64_t>(r) * s.NL + layer] * s.row_bytes;
+    uint8_t* dst_base = s.cache + rl * s.B * s.row_bytes;
+    for (int c0 = threadIdx.x; c0 < total; c0 += NT * U) {
+        u32x4 v[U];
+        u32x4* dst[U];
+#pragma unroll
+        for (int x = 0; x < U; ++x) {
+            const int c = c0 + x * NT;
+            dst[x] = nullptr;
+            if (c < total) {
+                const int i = c / row16, off = c - i * row16;
+                const u32x4* src = reinterpret_cast<const u32x4*>(src_base + static_cast<int64_t>(mpos[i]) * s.row_bytes) + off;
+                dst[x] = reinterpret_cast<u32x4*>(dst_base + static_cast<int64_t>(msl[i]) * s.row_bytes) + off;
+                v[x] = ld16<NTL>(src);
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < U; ++x)
+            if (dst[x]) st16<NTL>(dst[x], v[x]);
+    }
+}
+
+// LDS layout (ints): region 1 holds the lookup structure -- bitmap
+// [4*NG words as NG 16-byte groups], group ranks [NG], slot by rank [k] and
+// a spare word per lane [64] --
+// and, once the selection side is done with it, the miss lists: selection
+// index [k], position [k] and (wide launches) victim slot [k] of each miss.
+// Then the histogram [kHistBins] and the misc block [kMiscWords].
+//
+// Template parameters: NT lanes a unit; SPL selections and PER slots a lane
+// (contiguous runs j0 = tid*SPL, s0 = tid*PER); VEC: k and B multiples of 4
+// and 16-byte aligned selection / output arrays, so runs move as vectors;
+// WIDE: a launch over many units (held to two or four workgroups a CU, and
+// it copies its own misses).
+template <int NT, int SPL, int PER, bool VEC, bool WIDE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WIDE ? 8 : 1)))
+void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
+    constexpr int NW = NT / 64;
+    static_assert(NW <= 16, "per-wave partials fit one row of 16 lanes");
+    extern __shared__ int lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int r = blockIdx.x;
+    const int layer = lb.layer[blockIdx.y];
+    const int k = lb.k, B = s.B, NG = lb.ngroups;
+    const int64_t rl = static_cast<int64_t>(layer) * s.R + r;
+    const int32_t* sel = lb.sel[blockIdx.y] + static_cast<int64_t>(r) * k;
+    int32_t* out = lb.out[blockIdx.y] + static_cast<int64_t>(r) * k;
+    int32_t* spos_g = s.slot_pos + rl * B;
+    uint32_t* ts_g = s.ts + rl * B;
+    uint32_t* clock_u = s.clock + rl;
+    int32_t* mc_u = s.miss_count + rl;
+    uint4* const bits4 = reinterpret_cast<uint4*>(lds);
+    unsigned* const bits = reinterpret_cast<unsigned*>(lds);
+    int* const grank = lds + 4 * NG;
+    int* const byrank = grank + NG;
+    int* const mj = lds;          // overlays, valid after the selection side
+    int* const mpos = lds + k;
+    int* const msl = lds + 2 * k;
+    int* const hist = lds + lb.r1_ints;
+    int* const misc = hist + kHistBins;
+    if (lb.trace && tid == 0) {
+        // the stamp words lie outside the part of the misc block cleared below
+        unsigned long long* st0 = reinterpret_cast<unsigned long long*>(misc + X_STAMP);
+        st0[0] = wall_clock64();
+        for (int i = 1; i < 11; ++i) st0[i] = 0ull;
+    }
+
+    // 1. every global read up front: clock, history length, last step's miss
+    // count, this lane's runs of the selection, the slot map and the stamps
+    const uint32_t t = *clock_u;
+    const int hist_len = s.length[rl];
+    const bool spec = *mc_u > 0;  // expect misses: build the age histogram early
+    const int j0 = tid * SPL, s0 = tid * PER;
+    int selv[SPL];
+    load_run<SPL, VEC, int>(sel, j0, k, selv, kEmpty);
+    int spos[PER];
+    load_run<PER, VEC, int>(spos_g, s0, B, spos, kEmpty);
+    uint32_t tsv[PER];
+    load_run<PER, VEC, uint32_t>(ts_g, s0, B, tsv, 0u);
+    for (int g = tid; g < NG; g += NT) bits4[g] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tid; i < k; i += NT) byrank[i] = kEmpty;
+    for (int i = tid; i < kHistBins; i += NT) hist[i] = 0;
+    if (tid < X_STAMP) misc[tid] = 0;
+    __syncthreads();
+    HB_PHASE(1);
+
+    // 2. every selected position sets its bit; a bit already set is a
+    // repeated position, a position outside the history rejects the request
+    // (straight-line: a lane without a valid selection ORs nothing into word 0)
+    int bad = 0, bad_at = 0;
+#pragma unroll
+    for (int q = 0; q < SPL; ++q) {
+        const int j = j0 + q;
+        const int p = selv[q];
+        const bool live = j < k;
+        const bool inr = live && static_cast<unsigned>(p) < static_cast<unsigned>(hist_len);
+        const unsigned bit = inr ? 1u << (p & 31) : 0u;
+        const unsigned old = atomicOr(&bits[inr ? p >> 5 : 0], bit);
+        const int b = ((live && !inr) ? 1 : 0) | ((old & bit) ? 2 : 0);
+        bad |= b;
+        bad_at = b ? j + 1 : bad_at;
+    }
+    block_or_into(&misc[X_FLAGS], bad);
+    if (bad) atomicMax(&misc[X_BADAT], bad_at);
+    __syncthreads();
+    HB_PHASE(2);
+    const int flags = misc[X_FLAGS];
+    if (flags) {
+        // reject: -1 everywhere, state unchanged
+        for (int j = tid; j < k; j += NT) {
+            out[j] = -1;
+            s.hit_mask[rl * B + j] = 0;
+        }
+        if (tid == 0) {
+            *mc_u = 0;
+            s.status[rl] = (flags & 1) ? HS_DEV_RANGE : HS_DEV_DUP;
+            record_error(s.err, (flags & 1) ? HS_DEV_RANGE : HS_DEV_DUP, layer, r, misc[X_BADAT] - 1);
+        }
+        return;
+    }
+
+    // 3. group ranks: lane tid owns the 16-byte groups [tid*gpl, tid*gpl + gpl);
+    // each wave takes its run of ranks with one LDS atomic, so ranks map the
+    // selected positions one to one onto [0, k) whatever order the waves'
+    // atomics land in, with no barrier between counting and ranking
+    {
+        const int gpl = (NG + NT - 1) / NT;
+        const int g0 = tid * gpl;
+        int cnt = 0;
+        for (int i = 0; i < gpl; ++i) {
+            if (g0 + i < NG) {
+                const uint4 v = bits4[g0 + i];
+                cnt += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
+            }
+        }
+        const int incl = wave_incl_scan(cnt);
+        int wb = 0;
+        if (lane == 63) wb = atomicAdd(&misc[X_RANK], incl);
+        int base = __builtin_amdgcn_readlane(wb, 63) + incl - cnt;
+        for (int i = 0; i < gpl; ++i) {
+            if (g0 + i < NG) {
+                const uint4 v = bits4[g0 + i];
+                grank[g0 + i] = base;
+                base += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
+            }
+        }
+    }
+    __syncthreads();
+    HB_PHASE(3);
+
+    // 4. slot side: each cached slot whose position is selected records
+    // itself at that position's rank and takes the hit stamp 2t+2; the run of
+    // stamps goes back as whole pieces
+    const uint32_t ts_hit = 2u * t + 2u, ts_miss = 2u * t + 1u;
+    // (straight-line: a slot that is not a hit writes its lane's spare word
+    // byrank[k + lane] instead)
+    unsigned hitbits = 0;
+    const int nbits_pos = NG * 128;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int p = spos[q];
+        const bool live = s0 + q < B && p >= 0 && p < nbits_pos;
+        int rank;
+        const bool hit = bitmap_rank(bits4, grank, live ? p : 0, rank) && live;
+        byrank[hit ? rank : k + lane] = s0 + q;
+        hitbits |= static_cast<unsigned>(hit) << q;
+        // at most four lookups in flight: bounds the registers they hold
+        if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+    if (hitbits) {
+        uint32_t tsn[PER];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) tsn[q] = ((hitbits >> q) & 1u) ? ts_hit : tsv[q];
+        store_run_masked<PER, VEC, uint32_t>(ts_g, s0, B, tsn, hitbits);
+    }
+    if (spec) {
+        // candidate ages (2t - stamp; no stamp exceeds 2t before step t);
+        // ages of 1023 and more share the top bin
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            int bin = -1;
+            if (s0 + q < B && !((hitbits >> q) & 1u)) {
+                const uint32_t age = 2u * t - tsv[q];
+                bin = age < kHistBins - 1 ? static_cast<int>(age) : kHistBins - 1;
+            }
+            hist_add(hist, bin);
+        }
+    }
+    __syncthreads();
+    HB_PHASE(4);
+
+    // 5. selection side: the slot recorded at each selection's rank is its
+    // hit (published now), or nothing (a miss, published by its victim lane)
+    int slv[SPL];
+    unsigned mf = 0;
+#pragma unroll
+    for (int q = 0; q < SPL; ++q) {
+        // (a lane past the end looks up position 0; its rank stays within
+        // [0, k], so the read stays inside byrank and is discarded)
+        const bool live = j0 + q < k;
+        int rank;
+        bitmap_rank(bits4, grank, live ? selv[q] : 0, rank);
+        const int v = byrank[rank];
+        slv[q] = live ? v : kEmpty;
+        mf |= static_cast<unsigned>(live && v < 0) << q;
+    }
+    {
+        constexpr int W = SPL < 4 ? SPL : 4;
+        constexpr unsigned PM = (1u << W) - 1u;
+        uint8_t* hm = s.hit_mask + rl * B;
+        if constexpr (VEC && W >= 2) {
+#pragma unroll
+            for (int q = 0; q < SPL; q += W) {
+                if (j0 + q < k) {
+                    if (((mf >> q) & PM) == 0u) {
+                        if constexpr (W == 4)
+                            *reinterpret_cast<int4*>(out + j0 + q) = make_int4(slv[q], slv[q + 1], slv[q + 2], slv[q + 3]);
+                        else
+                            *reinterpret_cast<int2*>(out + j0 + q) = make_int2(slv[q], slv[q + 1]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < W; ++e)
+                            if (!((mf >> (q + e)) & 1u)) out[j0 + q + e] = slv[q + e];
+                    }
+                    unsigned hw = 0;
+#pragma unroll
+                    for (int e = 0; e < W; ++e) hw |= static_cast<unsigned>(!((mf >> (q + e)) & 1u)) << (8 * e);
+                    if constexpr (W == 4) *reinterpret_cast<uint32_t*>(hm + j0 + q) = hw;
+                    else *reinterpret_cast<uint16_t*>(hm + j0 + q) = static_cast<uint16_t>(hw);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < SPL; ++q) {
+                const int j = j0 + q;
+                if (j < k) {
+                    if (!((mf >> q) & 1u)) out[j] = slv[q];
+                    hm[j] = ((mf >> q) & 1u) ? 0 : 1;
+                }
+            }
+        }
+    }
+    const int mc = __popc(mf);
+    const int mincl = wave_incl_scan(mc);
+    if (lane == 63) misc[X_MISS + wave] = mincl;
+    __syncthreads();
+    HB_PHASE(5);
+    const int m = sum_before(misc + X_MISS, NW);
+    if (m == 0) {
+        // every selection hit: the hit stamps are written, nothing else changes
+        if (tid == 0) finish_unit(s, clock_u, mc_u, rl, t, k, 0);
+        HB_PHASE(10);
+        HB_PHASE_FLUSH();
+        return;
+    }
+
+    // 6. misses in ascending selection order (region 1 is free now), and the
+    // age histogram of the candidate slots unless it was built early
+    {
+        int mb = mincl - mc + sum_before(misc + X_MISS, wave);
+#pragma unroll
+        for (int q = 0; q < SPL; ++q) {
+            if ((mf >> q) & 1u) {
+                mj[mb] = j0 + q;
+                mpos[mb] = selv[q];
+                ++mb;
+            }
+        }
+    }
+    if (!spec) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            int bin = -1;
+            if (s0 + q < B && !((hitbits >> q) & 1u)) {
+                const uint32_t age = 2u * t - tsv[q];
+                bin = age < kHistBins - 1 ? static_cast<int>(age) : kHistBins - 1;
+            }
+            hist_add(hist, bin);
+        }
+    }
+    __syncthreads();
+    HB_PHASE(6);
+
+    // 7. threshold stamp T and how many candidates stamped exactly T go
+    // (lowest slots first); every other victim is older than T
+    const int h = k - m;
+    const int ncand = B - h;
+    uint32_t T;
+    int need_eq;
+    if (m == ncand) {
+        T = 0xFFFFFFFFu;  // every candidate is a victim (stamps never reach this value)
+        need_eq = 0;
+    } else {
+        int bin, below;
+        crossing_from_top(hist, m, bin, below);
+        if (bin < kHistBins - 1) {
+            T = 2u * t - static_cast<uint32_t>(bin);
+            need_eq = m - below;
+        } else {
+            // All m victims are at least 1023 ages old: select among those
+            // with a radix select on their stamps (hist must start at zero).
+            __syncthreads();
+            for (int i = tid; i < kHistBins; i += NT) hist[i] = 0;
+            unsigned old_bits = 0;
+#pragma unroll
+            for (int q = 0; q < PER; ++q)
+                if (s0 + q < B && !((hitbits >> q) & 1u) && 2u * t - tsv[q] >= static_cast<uint32_t>(kHistBins - 1))
+                    old_bits |= 1u << q;
+            __syncthreads();
+            radix_select<NT, PER>(hist, misc, tsv, old_bits, m, T, need_eq);
+        }
+    }
+    HB_PHASE(7);
+
+    // 8. victim ranks in slot order: strictly older candidates and tied
+    // candidates are counted together in one packed scan (strict in the low
+    // 16 bits, tied in the high; both at most B <= 16384)
+    unsigned strict_bits = 0, tie_bits = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const bool cand = s0 + q < B && !((hitbits >> q) & 1u);
+        strict_bits |= static_cast<unsigned>(cand && tsv[q] < T) << q;
+        tie_bits |= static_cast<unsigned>(cand && tsv[q] == T) << q;
+    }
+    const int packed = __popc(strict_bits) | (__popc(tie_bits) << 16);
+    const int vincl = wave_incl_scan(packed);
+    if (lane == 63) misc[X_VICT + wave] = vincl;
+    __syncthreads();
+    HB_PHASE(8);
+    const int vpre = vincl - packed + sum_before(misc + X_VICT, wave);
+    int sb = vpre & 0xFFFF, tb = vpre >> 16;
+
+    // 9. the rank-th miss (ascending j) takes the rank-th victim (ascending
+    // slot); the evicted position goes back to host-only (no write-back: the
+    // host copy is authoritative); the victim lane publishes the miss
+    int32_t* pt = s.page_table + rl * s.L_ctx;
+    int4* plan = s.plan + rl * B;
+    unsigned vbits = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        int rank = -1;
+        if ((strict_bits >> q) & 1u) {
+            rank = sb + min(tb, need_eq);
+            ++sb;
+        } else if ((tie_bits >> q) & 1u) {
+            if (tb < need_eq) rank = sb + tb;
+            ++tb;
+        }
+        if (rank >= 0 && rank < m) {
+            const int slot = s0 + q;
+            const int j = mj[rank];
+            const int newp = mpos[rank];
+            const int old = spos[q];
+            plan[rank] = make_int4(j, slot, old, newp);
+            if (old >= 0) pt[old] = -1;
+            pt[newp] = slot;
+            out[j] = slot;
+            if constexpr (WIDE) msl[rank] = slot;
+            spos[q] = newp;
+            vbits |= 1u << q;
+        }
+    }
+    if (vbits) {
+        // the pieces holding a victim are written again whole: victims get
+        // 2t+1, hits keep the 2t+2 written above, the rest their stamps
+        uint32_t tsn[PER];
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+            tsn[q] = ((vbits >> q) & 1u) ? ts_miss : (((hitbits >> q) & 1u) ? ts_hit : tsv[q]);
+        store_run_masked<PER, VEC, int>(spos_g, s0, B, spos, vbits);
+        store_run_masked<PER, VEC, uint32_t>(ts_g, s0, B, tsn, vbits);
+    }
+    HB_PHASE(9);
+    if (tid == 0) finish_unit(s, clock_u, mc_u, rl, t, k, m);
+    if constexpr (WIDE) {
+        // a wide launch copies its own misses: with hundreds of workgroups
+        // copying at once the link is as busy as under the chip-wide fetch
+        // kernel, and the launch after it is saved
+        if (lb.copy) {
+            __syncthreads();  // every victim slot is in msl
+            if (lb.nt) copy_misses<NT, true>(s, mpos, msl, rl, r, layer, m);
+            else copy_misses<NT, false>(s, mpos, msl, rl, r, layer, m);
+        }
+    }
+    HB_PHASE(10);
+    HB_PHASE_FLUSH();
+}
+
+template <int NT, int SPL, int PER, bool VEC, bool WIDE>
+hipError_t launch_b(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
+    static LdsGrants granted;  // per instantiation
+    const void* fn = reinterpret_cast<const void*>(&bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE>);
+    const hipError_t e = ensure_lds_limit(fn, lds, granted);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE>), dim3(s.R, lb.n), dim3(NT), lds, st, s, lb);
+    return hipGetLastError();
+}
+
+template <int NT, int SPL, int PER, bool WIDE>
+hipError_t launch_v(const StateBase& s, const LayerBatch& lb, size_t lds, bool vec, hipStream_t st) {
+    return vec ? launch_b<NT, SPL, PER, true, WIDE>(s, lb, lds, st) : launch_b<NT, SPL, PER, false, WIDE>(s, lb, lds, st);
+}
+
+template <int NT, int SPL, bool WIDE>
+hipError_t launch_p(const StateBase& s, const LayerBatch& lb, size_t lds, bool vec, hipStream_t st) {
+    const int per = (s.B + NT - 1) / NT;
+    if (per <= 1) return launch_v<NT, SPL, 1, WIDE>(s, lb, lds, vec, st);
+    if (per <= 2) return launch_v<NT, SPL, 2, WIDE>(s, lb, lds, vec, st);
+    if (per <= 4) return launch_v<NT, SPL, 4, WIDE>(s, lb, lds, vec, st);
+    if (per <= 8) return launch_v<NT, SPL, 8, WIDE>(s, lb, lds, vec, st);
+    if constexpr (NT == 1024) {
+        if (per <= 16) return launch_v<NT, SPL, 16, WIDE>(s, lb, lds, vec, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int NT, bool WIDE>
+hipError_t launch_s(const StateBase& s, const LayerBatch& lb, size_t lds, bool vec, hipStream_t st) {
+    const int spl = (lb.k + NT - 1) / NT;
+    if (spl <= 1) return launch_p<NT, 1, WIDE>(s, lb, lds, vec, st);
+    if (spl <= 2) return launch_p<NT, 2, WIDE>(s, lb, lds, vec, st);
+    if (spl <= 4) return launch_p<NT, 4, WIDE>(s, lb, lds, vec, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+// Ints of region 1 of the bitmap kernel's LDS, rounded to 16 bytes.
+static size_t bitmap_r1_ints(int k, int ngroups, bool wide) {
+    // bitmap, group ranks, slot by rank (k) and one spare word per lane (64)
+    const size_t look = 5 * static_cast<size_t>(ngroups) + static_cast<size_t>(k) + 64;
+    const size_t miss = (wide ? 3 : 2) * static_cast<size_t>(k);
+    const size_t r1 = look > miss ? look : miss;
+    return (r1 + 3) & ~static_cast<size_t>(3);
+}
+
+size_t bitmap_lds_bytes(int k, int64_t L_ctx, bool wide) {
+    const int ng = static_cast<int>((L_ctx + 127) >> 7);
+    return sizeof(int) * (bitmap_r1_ints(k, ng, wide) + kHistBins + kMiscWords);
+}
+
+int bitmap_lanes(int B, int k, bool wide) {
+    // 512 lanes let four units share a CU in wide launches (fewer lanes per
+    // unit, more units in flight); a few units per launch take 1024 lanes
+    return (wide && B <= 8 * 512 && k <= 4 * 512) ? 512 : 1024;
+}
+
+hipError_t launch_bitmap_resolve(const StateBase& s, const LayerBatch& lb_in, bool wide, bool vec, hipStream_t st) {
+    LayerBatch lb = lb_in;
+    lb.ngroups = static_cast<int>((s.L_ctx + 127) >> 7);
+    lb.r1_ints = static_cast<int>(bitmap_r1_ints(lb.k, lb.ngroups, wide));
+    const size_t lds = bitmap_lds_bytes(lb.k, s.L_ctx, wide);
+    if (bitmap_lanes(s.B, lb.k, wide) == 512) {
+        return wide ? launch_s<512, true>(s, lb, lds, vec, st) : launch_s<512, false>(s, lb, lds, vec, st);
+    }
+    return wide ? launch_s<1024, true>(s, lb, lds, vec, st) : launch_s<1024, false>(s, lb, lds, vec, st);
+}
+
+}  // namespace hs

@@ -34,8 +34,12 @@
  *     decode-step order on one stream (or be ordered by the caller's events).
  *   - Graph capture: resolve and prefetch may be captured (the prefetch side
  *     stream must join the capture, e.g. by waiting on the capturing stream).
- *     A capture must begin with the device idle: inside a capture the library
- *     drops its waits on its own events that were recorded before the capture.
+ *     Contract: a capture must begin after the library's earlier (eager) work
+ *     has finished, e.g. after a device synchronise (torch.cuda.graph does one
+ *     on entry).  Inside a capture the library cannot wait on, or query, its
+ *     own events recorded before the capture began, so it drops those waits;
+ *     a capture begun while an eager prefetch replay still runs would not be
+ *     ordered after it.
  *
  * Layouts (all row-major, C order)
  *   host pool      rows of W_KV*s bytes; the history of (request r, layer l)
@@ -77,7 +81,8 @@ typedef struct hisparse_ctx* hisparse_t;
 #define HS_DEV_RANGE 1        /* a position outside [0, length) of its history (length <= L_ctx) */
 #define HS_DEV_DUP 2          /* a position repeated within one request's selection */
 #define HS_DEV_NOT_RESIDENT 3 /* shared layer: a selected position is not where the anchor's plan put it */
-#define HS_DEV_DIVERGED 4     /* shared layer: its cache state no longer mirrors its anchor's */
+#define HS_DEV_DIVERGED 4     /* shared layer: its cache state no longer mirrors its anchor's, or its
+                                 selection is not the anchor's (positions or order) */
 #define HS_DEV_FULL 5         /* append: the history already holds L_ctx positions */
 
 /* ---- limits --------------------------------------------------------------- */
@@ -132,7 +137,11 @@ int hisparse_resolve_layers(hisparse_t h, int n, const int* layers, const int32_
  * replays that plan into each shared layer (the same slots, records read from
  * the shared layer's own host rows) and mirrors the anchor's cache state into
  * it.  The next hisparse_resolve of each shared layer waits for the replay and
- * only publishes; its selection must equal the anchor's.  Async on both
+ * only publishes; its selection must equal the anchor's element by element
+ * (same positions, same order), which that resolve checks against the
+ * anchor's d_sel buffer -- so the anchor's selection buffer must stay
+ * unchanged until the shared layers' resolves have run.  A shared layer whose
+ * selection differs publishes -1 and sets HS_DEV_DIVERGED.  Async on both
  * streams.  Errors: HS_E_HANDLE, HS_E_LAYER, HS_E_INVAL, HS_E_ORDER, HS_E_HIP. */
 int hisparse_prefetch(hisparse_t h, int anchor_layer, const int* shared_layers, int n_shared, void* side_stream);
 
@@ -149,7 +158,11 @@ int hisparse_append(hisparse_t h, int layer, const void* d_rows, void* stream);
 /* Set the number of positions already written in every history (e.g. the
  * prefill lengths): lengths [num_req*num_layers], index r*num_layers + l,
  * each in [0, L_ctx].  Selections must name positions below the length.
- * At create every history has length L_ctx.  Synchronises the device. */
+ * At create every history has length L_ctx.  A cached position at or past
+ * its history's new length leaves the cache (its slot becomes empty, stamp 0,
+ * the position host-only): a record appended there later is fetched from the
+ * pool, the authoritative copy (blog section 2, item 1), never served from
+ * the old copy.  Synchronises the device. */
 int hisparse_set_lengths(hisparse_t h, const int64_t* lengths);
 /* Read the history lengths into lengths [num_req*num_layers] (synchronises). */
 int hisparse_get_lengths(hisparse_t h, int64_t* lengths);

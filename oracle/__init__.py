@@ -44,6 +44,8 @@ def _load():
         getattr(lib, name).argtypes = [vp]
     lib.oracle_length.restype = vp
     lib.oracle_length.argtypes = [vp]
+    lib.oracle_set_length.restype = ctypes.c_int
+    lib.oracle_set_length.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int64]
     lib.oracle_append.restype = ctypes.c_int
     lib.oracle_append.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp]
     lib.oracle_resolve.restype = ctypes.c_int
@@ -92,6 +94,15 @@ class Oracle:
 
     def reset(self):
         self.lib.oracle_reset(self.h)
+
+    def set_lengths(self, lengths):
+        """lengths [num_req][num_layers]: set every history's length (cached
+        positions at or past a lowered length leave the cache)."""
+        lengths = np.asarray(lengths, dtype=np.int64).reshape(self.num_req, self.num_layers)
+        for r in range(self.num_req):
+            for l in range(self.num_layers):
+                if self.lib.oracle_set_length(self.h, l, r, int(lengths[r, l])) != E_OK:
+                    raise ValueError(f"length {lengths[r, l]} outside [0, {self.L_ctx}]")
 
     def append(self, layer, rows, pool, region_row=None):
         """rows: uint8 [num_req][row_bytes]; pool: writable uint8 array holding the host pool."""

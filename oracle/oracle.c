@@ -44,6 +44,9 @@
  *     pool, the authoritative copy, like prefill records (blog section 2,
  *     item 1); positions at or beyond a history's length are out of range;
  *     the record enters the GPU cache only when a later selection names it.
+ *   - lowering a history's length drops the cached copies of the positions
+ *     it cuts off (their slots become empty), so a record appended again at
+ *     such a position is fetched from the pool, never served stale.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -104,6 +107,30 @@ int32_t* oracle_page_table(oracle_t* o) { return o->page_table; }
 uint32_t* oracle_clock(oracle_t* o) { return o->clock; }
 uint8_t* oracle_cache(oracle_t* o) { return o->cache; }
 int64_t* oracle_length(oracle_t* o) { return o->length; }
+
+/* Set the length of the (request, layer) history to n (0 <= n <= L_ctx).
+ * A record at a position at or beyond n is no longer part of the history,
+ * and a later append may write a different record there; since the host
+ * pool is the authoritative copy (blog section 2, item 1), a cached copy of
+ * such a position leaves the cache: its slot becomes empty (position -1,
+ * stamp 0, as at creation) and the position host-only.  Returns OR_E_RANGE
+ * for n outside [0, L_ctx], else OR_OK. */
+int oracle_set_length(oracle_t* o, int layer, int req, int64_t n) {
+    if (n < 0 || n > o->L_ctx) return OR_E_RANGE;
+    const int64_t rl = (int64_t)layer * o->num_req + req;
+    int32_t* spos = o->slot_pos + rl * o->B;
+    uint32_t* ts = o->ts + rl * o->B;
+    int32_t* pt = o->page_table + rl * o->L_ctx;
+    for (int s = 0; s < o->B; ++s) {
+        if (spos[s] >= 0 && (int64_t)spos[s] >= n) {
+            pt[spos[s]] = -1;
+            spos[s] = -1;
+            ts[s] = 0;
+        }
+    }
+    o->length[rl] = n;
+    return OR_OK;
+}
 
 /* Decode-time append: rows [num_req][row_bytes] go to position length of
  * each (request, layer) history in `pool`; err[r] = OR_E_FULL for a history

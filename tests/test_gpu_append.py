@@ -37,7 +37,7 @@ def test_append_then_select(hs):
     o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes)
     lengths = np.full((w.num_req, w.num_layers), L0, np.int64)
     res.set_lengths(lengths)
-    o.length[:, :] = L0
+    o.set_lengths(lengths)
     assert np.array_equal(res.lengths(), lengths)
     rng = np.random.default_rng(5)
     dev = torch.device("cuda:0")
@@ -89,5 +89,83 @@ def test_append_then_select(hs):
     assert np.array_equal(pinned, before) and np.array_equal(res.lengths(), full)
     with pytest.raises(hs.HisparseError):
         res.set_lengths(full + 1)
+    res.close()
+    pool.free()
+
+
+def test_shrink_drops_cached_tail_then_refetches(hs):
+    """Lowering the lengths after records are cached: the positions cut off
+    leave the cache on the GPU exactly as in the oracle (slot empty, stamp 0,
+    page-table entry -1); records appended again at those positions are
+    misses whose bytes are the new rows, not the old ones."""
+    from oracle import Oracle
+    L0, L1 = 5000, 4000
+    w = tg.Workload("shrink", 3, 2, 6000, 64, 2, 300, 600, 12, tg.LOCALITY, 0.8, seed_index=53)
+    base = tg.trace(w.replace(L_ctx=L0))
+    pool = make_pool(hs, w)
+    pinned = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
+    pool_copy = pinned.copy()
+    rr = w.region_rows()
+    res = make_resolver(hs, w, pool)
+    o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes)
+    lengths = np.full((w.num_req, w.num_layers), L0, np.int64)
+    res.set_lengths(lengths)
+    o.set_lengths(lengths)
+    dev = torch.device("cuda:0")
+    out = torch.empty((w.num_req, w.k), dtype=torch.int32, device=dev)
+    rng = np.random.default_rng(9)
+
+    def forced(S, first, limit):
+        """S with its first entries set to `first`, every row kept distinct
+        (repeats replaced by unused positions below `limit`)."""
+        S = np.where(S >= limit, S % limit, S).astype(np.int32)
+        S[:, :len(first)] = first
+        for r in range(S.shape[0]):
+            _, keep = np.unique(S[r], return_index=True)
+            dup = np.setdiff1d(np.arange(S.shape[1]), keep)
+            S[r, dup] = np.setdiff1d(np.arange(limit), S[r])[: dup.size]
+        return S
+
+    def step(l, S):
+        res.resolve(l, torch.from_numpy(S).to(dev), out)
+        ref = o.resolve(l, S, pool_copy, rr)
+        assert np.all(ref["err"] == 0)
+        assert np.array_equal(out.cpu().numpy(), ref["slot_idx"])
+        st = res.state(l)
+        for key in ("slot_pos", "ts", "clock", "page_table"):
+            assert np.array_equal(st[key], getattr(o, key)[l]), key
+        occ = o.slot_pos[l] >= 0
+        assert np.array_equal(res.cache_layer(l)[occ], o.cache[l][occ])
+        return ref
+
+    # fill the caches; make sure positions in [L1, L0) are resident
+    for t in range(4):
+        for l in range(w.num_layers):
+            step(l, forced(base[t, l], L1 + 100 * t + np.arange(8), L0))
+    cut = {l: o.slot_pos[l] >= L1 for l in range(w.num_layers)}
+    assert all(c.any() for c in cut.values())
+    lengths[:] = L1
+    res.set_lengths(lengths)
+    o.set_lengths(lengths)
+    for l in range(w.num_layers):
+        st = res.state(l)
+        for key in ("slot_pos", "ts", "page_table"):
+            assert np.array_equal(st[key], getattr(o, key)[l]), f"after shrink: {key}"
+        assert not np.any(st["slot_pos"] >= L1)
+    # append new records at the cut-off positions, then select them
+    for i in range(8):
+        for l in range(w.num_layers):
+            rows = rng.integers(0, 256, size=(w.num_req, w.row_bytes), dtype=np.uint8)
+            res.append(l, torch.from_numpy(rows).to(dev))
+            assert o.append(l, rows, pool_copy, rr).tolist() == [0] * w.num_req
+    for l in range(w.num_layers):
+        # the rewritten positions first; everything else below the old cut
+        ref = step(l, forced(base[5, l], L1 + np.arange(8), L1 + 8))
+        assert np.all(ref["hit_mask"][:, :8] == 0)
+        for r in range(w.num_req):
+            for j in range(8):
+                slot = ref["slot_idx"][r, j]
+                assert np.array_equal(res.cache_rows(l, r)[slot], pinned[rr[r * w.num_layers + l] + L1 + j])
+    assert res.error()[0] == 0
     res.close()
     pool.free()

@@ -50,8 +50,8 @@ def test_graph_replay_equals_eager(hs, prefetch):
         eager_step(graphed, t, out_buf)
         eager_step(eager, t, out_eager)
     g = torch.cuda.CUDAGraph()
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g):
+
+    def captured_step():
         cur = torch.cuda.current_stream()
         for g0 in range(0, w.num_layers, w.group):
             graphed.resolve(g0, sel_buf[g0], out_buf[g0], cur)
@@ -61,6 +61,10 @@ def test_graph_replay_equals_eager(hs, prefetch):
                 graphed.prefetch(g0, shared, side)
             for l in shared:
                 graphed.resolve(l, sel_buf[l], out_buf[l], cur)
+
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        captured_step()
     for t in range(2, w.steps):
         sel_buf.copy_(sel[t])
         g.replay()

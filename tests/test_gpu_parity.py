@@ -236,11 +236,11 @@ def test_synchronous_argument_errors(hs):
     assert hs.hisparse_hbm_bytes(h2) == 0
     assert res.hbm_bytes() == hs.hisparse_kv_bytes(2, 2, 32, 8, hs.BF16) == 2 * 2 * 32 * 16
     # metadata: per slot a position, a stamp, a plan entry and a hit-mask byte; per history a
-    # page table of L_ctx entries, four 32-bit words and the 64-bit region row; per layer four
+    # page table of L_ctx entries, four 32-bit words, the 64-bit region row and four 64-bit
     # counters; the error word
     nrl = 2 * 2
     assert hs.hisparse_meta_bytes(res.h) == (nrl * 32 * (4 + 4 + 16 + 1) + nrl * w.L_ctx * 4 + nrl * (4 * 4 + 8)
-                                             + 2 * 4 * 8 + 16)
+                                             + nrl * 4 * 8 + 16)
     res.close()
     pool.free()
 
@@ -433,7 +433,7 @@ def test_instrumentation_changes_nothing(hs):
     dev = torch.device("cuda:0")
     sel = torch.from_numpy(tr).to(dev)
     out = torch.empty((w.num_req, w.k), dtype=torch.int32, device=dev)
-    order = [0, 1, 2, 11, 12, 3, 4, 5, 6, 7, 8, 9, 10]   # the bitmap probe's phases in program order
+    order = list(range(11))   # the bitmap kernel's phases in program order
     for t in range(w.steps):
         for l in range(w.num_layers):
             res.resolve(l, sel[t, l], out)

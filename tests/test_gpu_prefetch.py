@@ -142,3 +142,48 @@ def test_prefetch_ordering_and_divergence_errors(hs):
             assert np.array_equal(st3["slot_pos"][r][row], tr[3, 3, r])
     res.close()
     pool.free()
+
+
+def test_shared_layer_selection_must_be_the_anchors(hs):
+    """A shared layer whose selection is not the anchor's -- the same
+    positions in another order, all of them resident -- is refused with
+    HS_DEV_DIVERGED and publishes -1: its hit mask and stamps would otherwise
+    silently be the anchor's, not its own.  The other shared layers of the
+    group publish normally."""
+    w = tg.PREFETCH.replace(name="prefetch_perm", num_req=2, num_layers=4, group=4, L_ctx=5000, k=64, B=128,
+                            steps=3, W_KV=8)
+    tr = tg.trace(w)
+    pool = make_pool(hs, w)
+    res = make_resolver(hs, w, pool)
+    dev = torch.device("cuda:0")
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    sel = torch.from_numpy(tr).to(dev)
+    out = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
+    for l in range(4):
+        res.resolve(l, sel[0, l], out[l], main)
+    res.resolve(0, sel[1, 0], out[0], main)
+    res.prefetch(0, [1, 2, 3], side)
+    permuted = torch.from_numpy(np.ascontiguousarray(tr[1, 1][:, ::-1])).to(dev)
+    res.resolve(1, permuted, out[1], main)
+    for l in (2, 3):
+        res.resolve(l, sel[1, l], out[l], main)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    code, layer, _ = res.error()
+    assert code == hs.HS_DEV_DIVERGED and layer == 1
+    assert np.all(got[1] == -1)
+    assert np.array_equal(got[2], got[0]) and np.array_equal(got[3], got[0])
+    # the same selection, in the anchor's order, publishes again
+    res.clear_error()
+    res.resolve(0, sel[2, 0], out[0], main)
+    res.prefetch(0, [1, 2, 3], side)
+    for l in (1, 2, 3):
+        res.resolve(l, sel[2, l], out[l], main)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert res.error()[0] == 0
+    for l in (1, 2, 3):
+        assert np.array_equal(got[l], got[0])
+    res.close()
+    pool.free()

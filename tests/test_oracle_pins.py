@@ -250,3 +250,37 @@ def test_append_grows_history_and_is_fetched_on_first_selection():
     before = pool.copy()
     assert o.append(0, rows, pool).tolist() == [E_FULL, E_FULL]
     assert np.array_equal(pool, before) and o.length[0].tolist() == [L_ctx, L_ctx]
+
+
+def test_shrinking_a_history_drops_its_cached_tail():
+    """Lowering a history's length drops the cached copies of the positions
+    it cuts off, so a record appended again at such a position is fetched
+    from the pool rather than served from the old copy (the host pool is
+    the authoritative copy, blog section 2, item 1).  Hand-derived: B = 3,
+    step 0 selects [2, 7] (slots 0, 1, stamp 1); length 5 empties slot 1
+    (position 7 > 4) and keeps slot 0; three appends write positions 5, 6, 7;
+    step 1 selects [7, 2]: 2 hits slot 0 (stamp 4), 7 misses and takes the
+    empty slot 1 (stamp 3) and its new bytes."""
+    L_ctx, row = 10, 16
+    pool = np.zeros((L_ctx, row), np.uint8)
+    for p in range(L_ctx):
+        pool[p] = p + 1
+    o = Oracle(1, 1, 3, L_ctx, row)
+    r0 = o.resolve(0, np.array([[2, 7]], np.int32), pool)
+    assert r0["slot_idx"].tolist() == [[0, 1]] and o.ts[0, 0].tolist() == [1, 1, 0]
+    o.set_lengths([[5]])
+    assert o.slot_pos[0, 0].tolist() == [2, -1, -1]
+    assert o.ts[0, 0].tolist() == [1, 0, 0]
+    assert o.page_table[0, 0, 7] == -1 and o.page_table[0, 0, 2] == 0
+    assert o.length[0, 0] == 5
+    for v in (0x51, 0x61, 0xAB):
+        assert o.append(0, np.full((1, row), v, np.uint8), pool).tolist() == [0]
+    assert o.length[0, 0] == 8 and np.all(pool[7] == 0xAB)
+    r1 = o.resolve(0, np.array([[7, 2]], np.int32), pool)
+    assert r1["slot_idx"].tolist() == [[1, 0]] and r1["hit_mask"].tolist() == [[0, 1]]
+    assert r1["plan"][0, 0].tolist() == [0, 1, -1, 7]
+    assert o.ts[0, 0].tolist() == [4, 3, 0]
+    assert np.all(o.cache[0, 0, 1] == 0xAB)
+    # a length outside [0, L_ctx] is refused
+    with pytest.raises(ValueError):
+        o.set_lengths([[L_ctx + 1]])
