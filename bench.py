@@ -69,6 +69,8 @@ def parse():
     ap.add_argument("--no-probes", action="store_true")
     ap.add_argument("--probe", default="default", choices=["default", "page_table", "slot_scan", "slot_scan_hash"],
                     help="how the metadata kernel finds hits (default: the library's)")
+    ap.add_argument("--meta-lanes", type=int, default=0, choices=[0, 512, 1024],
+                    help="lanes a (request, layer) of the metadata kernel (0: the library's choice)")
     ap.add_argument("--fetch-blocks", type=int, default=0)
     ap.add_argument("--unroll", type=int, default=0)
     ap.add_argument("--coherent", action="store_true")
@@ -131,6 +133,8 @@ def main():
         res.set_option(hs.HS_OPT_ATTN_HEADS, args.attn_heads_per_wg)
     if args.fetch_blocks:
         res.set_option(hs.HS_OPT_FETCH_BLOCKS, args.fetch_blocks)
+    if args.meta_lanes:
+        res.set_option(hs.HS_OPT_META_LANES, args.meta_lanes)
     if args.unroll:
         res.set_option(hs.HS_OPT_FETCH_UNROLL, args.unroll)
     sel = torch.from_numpy(tr).to(dev)
@@ -348,7 +352,8 @@ def main():
     res.close()
 
     if not args.no_hit_only:
-        result["hit_only"] = hit_only_leg(hs, tg, torch, tg.WORKLOADS[args.hit_only_workload], dev, sptr, hbm_peak)
+        result["hit_only"] = hit_only_leg(hs, tg, torch, tg.WORKLOADS[args.hit_only_workload], dev, sptr, hbm_peak,
+                                          meta_lanes=args.meta_lanes)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(tg, w, tr, pool, W, args.cpu_seconds)
@@ -402,7 +407,7 @@ def attention_leg(hs, torch, res, w, out, heads, dev, hbm_peak, iters=20, heads_
             "algorithmic_bytes": io_bytes, "flops": flops}
 
 
-def hit_only_leg(hs, tg, torch, w, dev, sptr, hbm_peak, steps=64):
+def hit_only_leg(hs, tg, torch, w, dev, sptr, hbm_peak, steps=64, meta_lanes=0):
     """Metadata path alone: every step after the first repeats it, so every
     selection hits and nothing crosses the host link.  Timed as captured HIP
     graphs (one per variant) so that host launch cost does not enter.  Only
@@ -415,6 +420,8 @@ def hit_only_leg(hs, tg, torch, w, dev, sptr, hbm_peak, steps=64):
     res = hs.Resolver(w.num_req, w.num_layers, w.B, w.W_KV, hs.BF16, pool, w.L_ctx, w.L_ctx,
                       region_row=np.zeros(w.num_req * w.num_layers, dtype=np.int64))
     out = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
+    if meta_lanes:
+        res.set_option(hs.HS_OPT_META_LANES, meta_lanes)
     for l in range(w.num_layers):
         res.resolve(l, tr[0, l], out[l], sptr)
     # algorithmic bytes per (request, layer) of an all-hit resolve with the

@@ -32,6 +32,7 @@ struct hisparse_ctx {
     bool timing = false;
     int probe = HS_PROBE_SLOT_SCAN;
     int attn_heads = 0;  // heads per attention workgroup: 0 = by shape, 32 or 64
+    int meta_lanes = 0;  // lanes a unit of the bitmap metadata kernel: 0 = by launch size, 512 or 1024
     float* attn_ws = nullptr;       // consumer workspace (partials per chunk)
     size_t attn_ws_floats = 0;
     // ordering of resolve / prefetch (host-side bookkeeping only)
@@ -340,6 +341,7 @@ static int resolve_plan_path(hisparse_t h, int n, const int* layers, const int32
     lb.hash_bits = hash_bits_for(k);
     lb.probe = h->probe;
     lb.nt = h->nt;
+    lb.lanes = h->meta_lanes;
     fb.n = n;
     for (int i = 0; i < n; ++i) {
         const int l = layers[i];
@@ -610,6 +612,10 @@ int hisparse_set_option(hisparse_t h, int key, int64_t value) {
         case HS_OPT_ATTN_HEADS:
             if (value != 0 && value != 32 && value != 64) return HS_E_INVAL;
             h->attn_heads = static_cast<int>(value);
+            return HS_OK;
+        case HS_OPT_META_LANES:
+            if (value != 0 && value != 512 && value != 1024) return HS_E_INVAL;
+            h->meta_lanes = static_cast<int>(value);
             return HS_OK;
         case HS_OPT_PHASE_TRACE:
             if (value && !h->s.phase) {

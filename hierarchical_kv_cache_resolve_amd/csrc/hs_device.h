@@ -60,20 +60,12 @@ __device__ inline void block_or_into(int* word, int v) {
     if (__ballot(v != 0) != 0ull && v != 0) atomicOr(word, v);
 }
 
-// Histogram increment for this lane's bin (-1: none).  When every active
-// lane of the wave has the same bin (an empty cache, or one stamp shared by
-// the whole wave) a single atomic adds the count; otherwise one atomic per
-// lane.  Called by all lanes of the wave.
+// Histogram increment for this lane's bin (-1: none): one LDS atomic per
+// lane.  Lanes of a wave that hit the same bin are serialised by the LDS,
+// which costs less than detecting and merging them with ballots (the ages of
+// a wave's candidate slots are spread over many bins).
 __device__ inline void hist_add(int* hist, int bin) {
-    const unsigned long long act = __ballot(bin >= 0);
-    if (act == 0ull) return;
-    const int lead = __ffsll(static_cast<long long>(act)) - 1;  // wave-uniform
-    const int b0 = __builtin_amdgcn_readlane(bin, lead);
-    if (__ballot(bin == b0) == act) {
-        if ((threadIdx.x & 63) == lead) atomicAdd(&hist[b0], __popcll(act));
-    } else if (bin >= 0) {
-        atomicAdd(&hist[bin], 1);
-    }
+    if (bin >= 0) atomicAdd(&hist[bin], 1);
 }
 
 }  // namespace hs

@@ -69,6 +69,7 @@ struct LayerBatch {
     int nt;       // non-temporal host loads and cache stores in the metadata kernel's own copy
     int copy;     // the metadata kernel copies the misses itself (set by launch_plan)
     int trace;    // phase stamps on (s.phase is set)
+    int lanes;    // bitmap kernel: lanes a unit asked for (0: by launch size)
 };
 
 struct FetchBatch {
@@ -89,7 +90,7 @@ hipError_t launch_plan(const StateBase& s, const LayerBatch& lb, hipStream_t st)
 // The bitmap metadata kernel (resolve_bitmap.hip): its LDS need, its lanes a
 // unit, and its launch (vec: k and B multiples of 4, arrays 16-byte aligned).
 size_t bitmap_lds_bytes(int k, int64_t L_ctx, bool wide);
-int bitmap_lanes(int B, int k, bool wide);
+int bitmap_lanes(int B, int k, bool wide, int asked);
 hipError_t launch_bitmap_resolve(const StateBase& s, const LayerBatch& lb, bool wide, bool vec, hipStream_t st);
 hipError_t launch_trim(const StateBase& s, hipStream_t st);
 // Whether a metadata launch over n layers copies its own misses (a wide

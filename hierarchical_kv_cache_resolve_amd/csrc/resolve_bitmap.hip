@@ -45,8 +45,9 @@ enum : int {
     X_HIST = 48,    // [16] radix-scan partials
     X_MIN = 64,     // [16] per-wave minimum candidate stamp
     X_MAX = 80,     // [16] per-wave maximum candidate stamp
-    X_STAMP = 96,   // [2 * 11] phase stamps of wave 0 while tracing
-    kMiscWords = 128,
+    X_HITS = 96,    // [16] per-wave inclusive hit counts
+    X_STAMP = 112,  // [2 * 11] phase stamps of wave 0 while tracing
+    kMiscWords = 144,
 };
 
 // A lane's contiguous run v[0..N) of elements i0 .. i0+N-1 of g, in pieces of
@@ -108,23 +109,67 @@ __device__ inline void store_run_masked(T* g, int i0, int n, const T (&v)[N], un
     }
 }
 
-// Rank of position p among the selected positions (its bit must be set):
-// the rank of its 16-byte group plus the set bits before it in the group.
-__device__ inline bool bitmap_rank(const uint4* bits4, const int* grank, int p, int& rank) {
-    const uint4 g = bits4[p >> 7];
-    const int base = grank[p >> 7];
-    const int wi = (p >> 5) & 3;
-    const unsigned w = wi == 0 ? g.x : (wi == 1 ? g.y : (wi == 2 ? g.z : g.w));
-    const unsigned bit = 1u << (p & 31);
-    rank = base + __popc(w & (bit - 1u)) + (wi > 0 ? __popc(g.x) : 0) + (wi > 1 ? __popc(g.y) : 0) +
-           (wi > 2 ? __popc(g.z) : 0);
-    return (w & bit) != 0u;
+// Rank of position p among the selected positions (its bit must be set).
+// WR: ranks are kept per 32-bit word of the bitmap -- rank = the word's rank
+// plus the set bits below p in the word (two LDS reads, a handful of ALU
+// instructions).  Otherwise ranks are kept per 16-byte group of words (a
+// quarter of the LDS): rank = the group's rank plus the set bits before p in
+// the group, with one 16-byte read of the group.  Lookups go in batches:
+// every batch's LDS reads are issued first, then the ranks are computed
+// straight-line (selects, no branches).  The empty asm keeps all four words
+// of every group live, so no read is narrowed to 12 bytes plus a branch for
+// the last word.
+template <int N, bool WR>
+__device__ inline void bitmap_ranks(const uint4* bits4, const int* ranks, const int (&p)[N], int (&rank)[N],
+                                    unsigned& isset) {
+    isset = 0;
+    if constexpr (WR) {
+        // a rank per 32-bit word: the word, its rank, the set bits below p
+        const unsigned* bits = reinterpret_cast<const unsigned*>(bits4);
+        unsigned w[N];
+        int base[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            w[i] = bits[p[i] >> 5];
+            base[i] = ranks[p[i] >> 5];
+        }
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const unsigned sh = static_cast<unsigned>(p[i]) & 31u;
+            rank[i] = base[i] + __popc(w[i] & ((1u << sh) - 1u));
+            isset |= ((w[i] >> sh) & 1u) << i;
+        }
+    } else {
+        uint4 g[N];
+        int base[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            g[i] = bits4[p[i] >> 7];
+            base[i] = ranks[p[i] >> 7];
+        }
+#pragma unroll
+        for (int i = 0; i < N; ++i) asm volatile("" : "+v"(g[i].x), "+v"(g[i].y), "+v"(g[i].z), "+v"(g[i].w));
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const unsigned wi = static_cast<unsigned>(p[i] >> 5) & 3u;
+            const unsigned lo = (wi & 1u) ? g[i].y : g[i].x;
+            const unsigned hi = (wi & 1u) ? g[i].w : g[i].z;
+            const unsigned w = (wi & 2u) ? hi : lo;
+            const unsigned bit = 1u << (p[i] & 31);
+            const int pre = (wi > 0u ? __popc(g[i].x) : 0) + (wi > 1u ? __popc(g[i].y) : 0) +
+                            (wi > 2u ? __popc(g[i].z) : 0);
+            rank[i] = base[i] + pre + __popc(w & (bit - 1u));
+            isset |= static_cast<unsigned>((w & bit) != 0u) << i;
+        }
+    }
 }
 
 // The age bin where the count taken from the oldest bin downwards first
 // reaches `need`, and the count of the bins above it.  Every wave computes it
 // on its own from the finished histogram (no barrier, no broadcast): lane i
-// covers the 16 bins [1008 - 16i, 1023 - 16i].
+// sums the 16 bins [1008 - 16i, 1023 - 16i], one wave scan orders the lanes
+// from the top, and the lane where the count crosses `need` walks its own
+// bins from the top.
 __device__ inline void crossing_from_top(const int* hist, int need, int& bin, int& below) {
     const int lane = threadIdx.x & 63;
     const int lo = kHistBins - kHistQ * (lane + 1);
@@ -141,17 +186,19 @@ __device__ inline void crossing_from_top(const int* hist, int need, int& bin, in
 #pragma unroll
     for (int i = 0; i < kHistQ; ++i) c += h[i];
     const int incl = wave_incl_scan(c);
-    int acc = incl - c, my_bin = -1, my_below = 0;
+    const unsigned long long found = __ballot(incl - c < need && need <= incl);
+    const int L = __ffsll(static_cast<long long>(found)) - 1;  // wave-uniform
+    int acc = incl - c, my_bin = lo, my_below = acc;
+    bool done = false;
 #pragma unroll
     for (int i = kHistQ - 1; i >= 0; --i) {
-        if (my_bin < 0 && acc < need && need <= acc + h[i]) {
+        if (!done && need <= acc + h[i]) {
             my_bin = lo + i;
             my_below = acc;
+            done = true;
         }
         acc += h[i];
     }
-    const unsigned long long found = __ballot(my_bin >= 0);
-    const int L = __ffsll(static_cast<long long>(found)) - 1;
     bin = __builtin_amdgcn_readlane(my_bin, L);
     below = __builtin_amdgcn_readlane(my_below, L);
 }
@@ -242,9 +289,9 @@ __device__ inline void radix_select(int* hist, int* misc, const uint32_t (&tsv)[
 // Phase stamps (constant-rate clock) while tracing is on: lane 0 of wave 0
 // keeps them in the misc block (no long-lived scalar registers) and writes
 // them out at the end.  Slots in program order: 0 start, 1 reads issued and
-// LDS cleared, 2 selection inserted, 3 ranks, 4 slot side, 5 selection side,
-// 6 miss list and histogram, 7 threshold, 8 victim ranks, 9 metadata
-// written, 10 end.
+// LDS cleared, 2 selection inserted, 3 ranks and hit test, 4 threshold, 5 slot
+// by rank and victim counts, 6 selection side and victim lists, 9 metadata
+// written, 10 end (7 and 8 unused).
 #define HB_PHASE(i)                                                                      \
     do {                                                                                 \
         if (lb.trace && tid == 0)                                                        \
@@ -307,20 +354,26 @@ __device__ inline void copy_misses(const StateBase& s, const int* mpos, const in
     }
 }
 
-// LDS layout (ints): region 1 holds the lookup structure -- bitmap
-// [4*NG words as NG 16-byte groups], group ranks [NG], slot by rank [k] and
-// a spare word per lane [64] --
-// and, once the selection side is done with it, the miss lists: selection
-// index [k], position [k] and (wide launches) victim slot [k] of each miss.
-// Then the histogram [kHistBins] and the misc block [kMiscWords].
+// LDS layout (ints): region 1 -- bitmap [4*NG words as NG 16-byte groups],
+// ranks [NG per group, or 4*NG per word when WR], slot by rank [k] with a
+// spare word per lane [64], victim
+// slot by victim rank [k], evicted position by victim rank [k] -- then the
+// histogram [kHistBins] and the misc block [kMiscWords].
 //
 // Template parameters: NT lanes a unit; SPL selections and PER slots a lane
 // (contiguous runs j0 = tid*SPL, s0 = tid*PER); VEC: k and B multiples of 4
 // and 16-byte aligned selection / output arrays, so runs move as vectors;
-// WIDE: a launch over many units (held to two or four workgroups a CU, and
-// it copies its own misses).
-template <int NT, int SPL, int PER, bool VEC, bool WIDE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WIDE ? 8 : 1)))
+// WIDE: a launch over many units (held to six waves per SIMD, and it copies
+// its own misses).
+//
+// Barriers: B1 LDS cleared; B2 selection inserted; B3 group ranks, hit test of
+// every slot (a bit test, no rank needed), hit count -- so m = k - h is known
+// here -- and, when the unit missed at its last step, the age histogram of
+// the candidates; B4 slot by rank, and (m > 0) threshold and packed victim
+// counts; B5 (m > 0 only) hits published, victims listed by rank, miss counts.
+// After B5 each missing selection takes the victim of its own rank.
+template <int NT, int SPL, int PER, bool VEC, bool WIDE, bool WR>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WIDE ? 6 : 1)))
 void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     constexpr int NW = NT / 64;
     static_assert(NW <= 16, "per-wave partials fit one row of 16 lanes");
@@ -338,11 +391,10 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     int32_t* mc_u = s.miss_count + rl;
     uint4* const bits4 = reinterpret_cast<uint4*>(lds);
     unsigned* const bits = reinterpret_cast<unsigned*>(lds);
-    int* const grank = lds + 4 * NG;
-    int* const byrank = grank + NG;
-    int* const mj = lds;          // overlays, valid after the selection side
-    int* const mpos = lds + k;
-    int* const msl = lds + 2 * k;
+    int* const grank = lds + 4 * NG;               // [NG] group ranks, or [4*NG] word ranks (WR)
+    int* const byrank = grank + (WR ? 4 * NG : NG);
+    int* const vlist = byrank + k + 64;
+    int* const vold = vlist + k;
     int* const hist = lds + lb.r1_ints;
     int* const misc = hist + kHistBins;
     if (lb.trace && tid == 0) {
@@ -374,21 +426,23 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     // 2. every selected position sets its bit; a bit already set is a
     // repeated position, a position outside the history rejects the request
     // (straight-line: a lane without a valid selection ORs nothing into word 0)
-    int bad = 0, bad_at = 0;
+    {
+        int bad = 0, bad_at = 0;
 #pragma unroll
-    for (int q = 0; q < SPL; ++q) {
-        const int j = j0 + q;
-        const int p = selv[q];
-        const bool live = j < k;
-        const bool inr = live && static_cast<unsigned>(p) < static_cast<unsigned>(hist_len);
-        const unsigned bit = inr ? 1u << (p & 31) : 0u;
-        const unsigned old = atomicOr(&bits[inr ? p >> 5 : 0], bit);
-        const int b = ((live && !inr) ? 1 : 0) | ((old & bit) ? 2 : 0);
-        bad |= b;
-        bad_at = b ? j + 1 : bad_at;
+        for (int q = 0; q < SPL; ++q) {
+            const int j = j0 + q;
+            const int p = selv[q];
+            const bool live = j < k;
+            const bool inr = live && static_cast<unsigned>(p) < static_cast<unsigned>(hist_len);
+            const unsigned bit = inr ? 1u << (p & 31) : 0u;
+            const unsigned old = atomicOr(&bits[inr ? p >> 5 : 0], bit);
+            const int bb = ((live && !inr) ? 1 : 0) | ((old & bit) ? 2 : 0);
+            bad |= bb;
+            bad_at = bb ? j + 1 : bad_at;
+        }
+        block_or_into(&misc[X_FLAGS], bad);
+        if (bad) atomicMax(&misc[X_BADAT], bad_at);
     }
-    block_or_into(&misc[X_FLAGS], bad);
-    if (bad) atomicMax(&misc[X_BADAT], bad_at);
     __syncthreads();
     HB_PHASE(2);
     const int flags = misc[X_FLAGS];
@@ -406,59 +460,58 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         return;
     }
 
-    // 3. group ranks: lane tid owns the 16-byte groups [tid*gpl, tid*gpl + gpl);
-    // each wave takes its run of ranks with one LDS atomic, so ranks map the
-    // selected positions one to one onto [0, k) whatever order the waves'
-    // atomics land in, with no barrier between counting and ranking
+    // 3. group ranks: lane tid owns groups tid, tid + NT, ... (consecutive
+    // lanes, consecutive 16-byte pieces); each wave takes its run of ranks
+    // with one LDS atomic, so ranks map the selected positions one to one
+    // onto [0, k) whatever order the waves' atomics land in
     {
-        const int gpl = (NG + NT - 1) / NT;
-        const int g0 = tid * gpl;
         int cnt = 0;
-        for (int i = 0; i < gpl; ++i) {
-            if (g0 + i < NG) {
-                const uint4 v = bits4[g0 + i];
-                cnt += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
-            }
+        for (int g = tid; g < NG; g += NT) {
+            const uint4 v = bits4[g];
+            cnt += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
         }
         const int incl = wave_incl_scan(cnt);
         int wb = 0;
         if (lane == 63) wb = atomicAdd(&misc[X_RANK], incl);
         int base = __builtin_amdgcn_readlane(wb, 63) + incl - cnt;
-        for (int i = 0; i < gpl; ++i) {
-            if (g0 + i < NG) {
-                const uint4 v = bits4[g0 + i];
-                grank[g0 + i] = base;
+        for (int g = tid; g < NG; g += NT) {
+            const uint4 v = bits4[g];
+            if constexpr (WR) {
+                int4 rk;
+                rk.x = base;
+                rk.y = rk.x + __popc(v.x);
+                rk.z = rk.y + __popc(v.y);
+                rk.w = rk.z + __popc(v.z);
+                reinterpret_cast<int4*>(grank)[g] = rk;
+                base = rk.w + __popc(v.w);
+            } else {
+                grank[g] = base;
                 base += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
             }
         }
     }
-    __syncthreads();
-    HB_PHASE(3);
-
-    // 4. slot side: each cached slot whose position is selected records
-    // itself at that position's rank and takes the hit stamp 2t+2; the run of
-    // stamps goes back as whole pieces
+    // hit test of this lane's slots (one bit each: a cached position whose
+    // bit is set is selected), the hit stamps 2t+2 written back as whole
+    // pieces of the stamp run, and the hit count
     const uint32_t ts_hit = 2u * t + 2u, ts_miss = 2u * t + 1u;
-    // (straight-line: a slot that is not a hit writes its lane's spare word
-    // byrank[k + lane] instead)
-    unsigned hitbits = 0;
     const int nbits_pos = NG * 128;
+    unsigned hitbits = 0;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
         const int p = spos[q];
         const bool live = s0 + q < B && p >= 0 && p < nbits_pos;
-        int rank;
-        const bool hit = bitmap_rank(bits4, grank, live ? p : 0, rank) && live;
-        byrank[hit ? rank : k + lane] = s0 + q;
-        hitbits |= static_cast<unsigned>(hit) << q;
-        // at most four lookups in flight: bounds the registers they hold
-        if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        const unsigned w = bits[live ? p >> 5 : 0];
+        hitbits |= static_cast<unsigned>(live && ((w >> (p & 31)) & 1u)) << q;
     }
     if (hitbits) {
         uint32_t tsn[PER];
 #pragma unroll
         for (int q = 0; q < PER; ++q) tsn[q] = ((hitbits >> q) & 1u) ? ts_hit : tsv[q];
         store_run_masked<PER, VEC, uint32_t>(ts_g, s0, B, tsn, hitbits);
+    }
+    {
+        const int hincl = wave_incl_scan(__popc(hitbits));
+        if (lane == 63) misc[X_HITS + wave] = hincl;
     }
     if (spec) {
         // candidate ages (2t - stamp; no stamp exceeds 2t before step t);
@@ -474,22 +527,108 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         }
     }
     __syncthreads();
-    HB_PHASE(4);
+    HB_PHASE(3);
+    const int h = sum_before(misc + X_HITS, NW);
+    const int m = k - h;
+
+    // 4. each hit slot records itself at its position's rank (a slot that is
+    // not a hit writes its lane's spare word byrank[k + lane] instead)
+    {
+        constexpr int NB = PER < 4 ? PER : 4;
+#pragma unroll
+        for (int q0 = 0; q0 < PER; q0 += NB) {
+            int pp[NB], rk[NB];
+            unsigned isset;
+#pragma unroll
+            for (int i = 0; i < NB; ++i) pp[i] = ((hitbits >> (q0 + i)) & 1u) ? spos[q0 + i] : 0;
+            bitmap_ranks<NB, WR>(bits4, grank, pp, rk, isset);
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const bool hit = (hitbits >> (q0 + i)) & 1u;
+                byrank[hit ? rk[i] : k + lane] = s0 + q0 + i;
+            }
+        }
+    }
+    // threshold stamp T and how many candidates stamped exactly T go (lowest
+    // slots first; every other victim is older than T), then the victim
+    // counts in slot order, strict and tied packed into one scan (strict in
+    // the low 16 bits, tied in the high; both at most B <= 16384)
+    uint32_t T = 0;
+    int need_eq = 0, packed = 0, vincl = 0;
+    unsigned strict_bits = 0, tie_bits = 0;
+    if (m > 0) {
+        if (!spec) {
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                int bin = -1;
+                if (s0 + q < B && !((hitbits >> q) & 1u)) {
+                    const uint32_t age = 2u * t - tsv[q];
+                    bin = age < kHistBins - 1 ? static_cast<int>(age) : kHistBins - 1;
+                }
+                hist_add(hist, bin);
+            }
+            __syncthreads();
+        }
+        const int ncand = B - h;
+        if (m == ncand) {
+            T = 0xFFFFFFFFu;  // every candidate is a victim (stamps never reach this value)
+        } else {
+            int bin, below;
+            crossing_from_top(hist, m, bin, below);
+            if (bin < kHistBins - 1) {
+                T = 2u * t - static_cast<uint32_t>(bin);
+                need_eq = m - below;
+            } else {
+                // All m victims are at least 1023 ages old: select among those
+                // with a radix select on their stamps (hist must start at zero).
+                __syncthreads();
+                for (int i = tid; i < kHistBins; i += NT) hist[i] = 0;
+                unsigned old_bits = 0;
+#pragma unroll
+                for (int q = 0; q < PER; ++q)
+                    if (s0 + q < B && !((hitbits >> q) & 1u) &&
+                        2u * t - tsv[q] >= static_cast<uint32_t>(kHistBins - 1))
+                        old_bits |= 1u << q;
+                __syncthreads();
+                radix_select<NT, PER>(hist, misc, tsv, old_bits, m, T, need_eq);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const bool cand = s0 + q < B && !((hitbits >> q) & 1u);
+            strict_bits |= static_cast<unsigned>(cand && tsv[q] < T) << q;
+            tie_bits |= static_cast<unsigned>(cand && tsv[q] == T) << q;
+        }
+        packed = __popc(strict_bits) | (__popc(tie_bits) << 16);
+        vincl = wave_incl_scan(packed);
+        if (lane == 63) misc[X_VICT + wave] = vincl;
+        HB_PHASE(4);
+    }
+    __syncthreads();
+    HB_PHASE(5);
 
     // 5. selection side: the slot recorded at each selection's rank is its
-    // hit (published now), or nothing (a miss, published by its victim lane)
+    // hit, published now, or nothing (a miss)
     int slv[SPL];
     unsigned mf = 0;
-#pragma unroll
-    for (int q = 0; q < SPL; ++q) {
+    {
         // (a lane past the end looks up position 0; its rank stays within
         // [0, k], so the read stays inside byrank and is discarded)
-        const bool live = j0 + q < k;
-        int rank;
-        bitmap_rank(bits4, grank, live ? selv[q] : 0, rank);
-        const int v = byrank[rank];
-        slv[q] = live ? v : kEmpty;
-        mf |= static_cast<unsigned>(live && v < 0) << q;
+        int pp[SPL], rk[SPL];
+        unsigned isset;
+#pragma unroll
+        for (int q = 0; q < SPL; ++q) pp[q] = j0 + q < k ? selv[q] : 0;
+        bitmap_ranks<SPL, WR>(bits4, grank, pp, rk, isset);
+        (void)isset;
+        int v[SPL];
+#pragma unroll
+        for (int q = 0; q < SPL; ++q) v[q] = byrank[rk[q]];
+#pragma unroll
+        for (int q = 0; q < SPL; ++q) {
+            const bool live = j0 + q < k;
+            slv[q] = live ? v[q] : kEmpty;
+            mf |= static_cast<unsigned>(live && v[q] < 0) << q;
+        }
     }
     {
         constexpr int W = SPL < 4 ? SPL : 4;
@@ -527,12 +666,6 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
             }
         }
     }
-    const int mc = __popc(mf);
-    const int mincl = wave_incl_scan(mc);
-    if (lane == 63) misc[X_MISS + wave] = mincl;
-    __syncthreads();
-    HB_PHASE(5);
-    const int m = sum_before(misc + X_MISS, NW);
     if (m == 0) {
         // every selection hit: the hit stamps are written, nothing else changes
         if (tid == 0) finish_unit(s, clock_u, mc_u, rl, t, k, 0);
@@ -540,122 +673,61 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         HB_PHASE_FLUSH();
         return;
     }
-
-    // 6. misses in ascending selection order (region 1 is free now), and the
-    // age histogram of the candidate slots unless it was built early
+    // misses per wave (for each miss's rank), and the victims: the slot of
+    // victim rank i goes to vlist[i], its evicted position to vold[i] (and
+    // back to host-only: no write-back, the host copy is authoritative); its
+    // stamp becomes 2t+1 in this lane's run, written back whole
+    const int mc = __popc(mf);
+    const int mincl = wave_incl_scan(mc);
+    if (lane == 63) misc[X_MISS + wave] = mincl;
     {
-        int mb = mincl - mc + sum_before(misc + X_MISS, wave);
-#pragma unroll
-        for (int q = 0; q < SPL; ++q) {
-            if ((mf >> q) & 1u) {
-                mj[mb] = j0 + q;
-                mpos[mb] = selv[q];
-                ++mb;
-            }
-        }
-    }
-    if (!spec) {
+        const int vpre = vincl - packed + sum_before(misc + X_VICT, wave);
+        int sb = vpre & 0xFFFF, tb = vpre >> 16;
+        int32_t* pt = s.page_table + rl * s.L_ctx;
+        unsigned vbits = 0;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            int bin = -1;
-            if (s0 + q < B && !((hitbits >> q) & 1u)) {
-                const uint32_t age = 2u * t - tsv[q];
-                bin = age < kHistBins - 1 ? static_cast<int>(age) : kHistBins - 1;
+            const bool st = (strict_bits >> q) & 1u, ti = (tie_bits >> q) & 1u;
+            const int rank = st ? sb + min(tb, need_eq) : ((ti && tb < need_eq) ? sb + tb : -1);
+            sb += st ? 1 : 0;
+            tb += ti ? 1 : 0;
+            if (rank >= 0 && rank < m) {
+                vlist[rank] = s0 + q;
+                vold[rank] = spos[q];
+                if (spos[q] >= 0) pt[spos[q]] = -1;
+                vbits |= 1u << q;
             }
-            hist_add(hist, bin);
+        }
+        if (vbits) {
+            uint32_t tsn[PER];
+#pragma unroll
+            for (int q = 0; q < PER; ++q)
+                tsn[q] = ((vbits >> q) & 1u) ? ts_miss : (((hitbits >> q) & 1u) ? ts_hit : tsv[q]);
+            store_run_masked<PER, VEC, uint32_t>(ts_g, s0, B, tsn, vbits | hitbits);
         }
     }
     __syncthreads();
     HB_PHASE(6);
 
-    // 7. threshold stamp T and how many candidates stamped exactly T go
-    // (lowest slots first); every other victim is older than T
-    const int h = k - m;
-    const int ncand = B - h;
-    uint32_t T;
-    int need_eq;
-    if (m == ncand) {
-        T = 0xFFFFFFFFu;  // every candidate is a victim (stamps never reach this value)
-        need_eq = 0;
-    } else {
-        int bin, below;
-        crossing_from_top(hist, m, bin, below);
-        if (bin < kHistBins - 1) {
-            T = 2u * t - static_cast<uint32_t>(bin);
-            need_eq = m - below;
-        } else {
-            // All m victims are at least 1023 ages old: select among those
-            // with a radix select on their stamps (hist must start at zero).
-            __syncthreads();
-            for (int i = tid; i < kHistBins; i += NT) hist[i] = 0;
-            unsigned old_bits = 0;
+    // 6. the i-th miss (ascending selection index) takes the victim of rank i
+    // (ascending slot): plan entry, page table, slot map and publication
+    {
+        int32_t* pt = s.page_table + rl * s.L_ctx;
+        int4* plan = s.plan + rl * B;
+        int i = mincl - mc + sum_before(misc + X_MISS, wave);
 #pragma unroll
-            for (int q = 0; q < PER; ++q)
-                if (s0 + q < B && !((hitbits >> q) & 1u) && 2u * t - tsv[q] >= static_cast<uint32_t>(kHistBins - 1))
-                    old_bits |= 1u << q;
-            __syncthreads();
-            radix_select<NT, PER>(hist, misc, tsv, old_bits, m, T, need_eq);
+        for (int q = 0; q < SPL; ++q) {
+            if ((mf >> q) & 1u) {
+                const int j = j0 + q, p = selv[q];
+                const int v = vlist[i], old = vold[i];
+                plan[i] = make_int4(j, v, old, p);
+                pt[p] = v;
+                spos_g[v] = p;
+                out[j] = v;
+                if constexpr (WIDE) vold[i] = p;  // the copy reads positions from here
+                ++i;
+            }
         }
-    }
-    HB_PHASE(7);
-
-    // 8. victim ranks in slot order: strictly older candidates and tied
-    // candidates are counted together in one packed scan (strict in the low
-    // 16 bits, tied in the high; both at most B <= 16384)
-    unsigned strict_bits = 0, tie_bits = 0;
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        const bool cand = s0 + q < B && !((hitbits >> q) & 1u);
-        strict_bits |= static_cast<unsigned>(cand && tsv[q] < T) << q;
-        tie_bits |= static_cast<unsigned>(cand && tsv[q] == T) << q;
-    }
-    const int packed = __popc(strict_bits) | (__popc(tie_bits) << 16);
-    const int vincl = wave_incl_scan(packed);
-    if (lane == 63) misc[X_VICT + wave] = vincl;
-    __syncthreads();
-    HB_PHASE(8);
-    const int vpre = vincl - packed + sum_before(misc + X_VICT, wave);
-    int sb = vpre & 0xFFFF, tb = vpre >> 16;
-
-    // 9. the rank-th miss (ascending j) takes the rank-th victim (ascending
-    // slot); the evicted position goes back to host-only (no write-back: the
-    // host copy is authoritative); the victim lane publishes the miss
-    int32_t* pt = s.page_table + rl * s.L_ctx;
-    int4* plan = s.plan + rl * B;
-    unsigned vbits = 0;
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        int rank = -1;
-        if ((strict_bits >> q) & 1u) {
-            rank = sb + min(tb, need_eq);
-            ++sb;
-        } else if ((tie_bits >> q) & 1u) {
-            if (tb < need_eq) rank = sb + tb;
-            ++tb;
-        }
-        if (rank >= 0 && rank < m) {
-            const int slot = s0 + q;
-            const int j = mj[rank];
-            const int newp = mpos[rank];
-            const int old = spos[q];
-            plan[rank] = make_int4(j, slot, old, newp);
-            if (old >= 0) pt[old] = -1;
-            pt[newp] = slot;
-            out[j] = slot;
-            if constexpr (WIDE) msl[rank] = slot;
-            spos[q] = newp;
-            vbits |= 1u << q;
-        }
-    }
-    if (vbits) {
-        // the pieces holding a victim are written again whole: victims get
-        // 2t+1, hits keep the 2t+2 written above, the rest their stamps
-        uint32_t tsn[PER];
-#pragma unroll
-        for (int q = 0; q < PER; ++q)
-            tsn[q] = ((vbits >> q) & 1u) ? ts_miss : (((hitbits >> q) & 1u) ? ts_hit : tsv[q]);
-        store_run_masked<PER, VEC, int>(spos_g, s0, B, spos, vbits);
-        store_run_masked<PER, VEC, uint32_t>(ts_g, s0, B, tsn, vbits);
     }
     HB_PHASE(9);
     if (tid == 0) finish_unit(s, clock_u, mc_u, rl, t, k, m);
@@ -664,9 +736,9 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         // copying at once the link is as busy as under the chip-wide fetch
         // kernel, and the launch after it is saved
         if (lb.copy) {
-            __syncthreads();  // every victim slot is in msl
-            if (lb.nt) copy_misses<NT, true>(s, mpos, msl, rl, r, layer, m);
-            else copy_misses<NT, false>(s, mpos, msl, rl, r, layer, m);
+            __syncthreads();  // every miss's position is in vold
+            if (lb.nt) copy_misses<NT, true>(s, vold, vlist, rl, r, layer, m);
+            else copy_misses<NT, false>(s, vold, vlist, rl, r, layer, m);
         }
     }
     HB_PHASE(10);
@@ -675,11 +747,12 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
 
 template <int NT, int SPL, int PER, bool VEC, bool WIDE>
 hipError_t launch_b(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
+    constexpr bool WR = !WIDE;  // as bitmap_word_ranks
     static LdsGrants granted;  // per instantiation
-    const void* fn = reinterpret_cast<const void*>(&bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE>);
+    const void* fn = reinterpret_cast<const void*>(&bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE, WR>);
     const hipError_t e = ensure_lds_limit(fn, lds, granted);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE>), dim3(s.R, lb.n), dim3(NT), lds, st, s, lb);
+    hipLaunchKernelGGL((bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE, WR>), dim3(s.R, lb.n), dim3(NT), lds, st, s, lb);
     return hipGetLastError();
 }
 
@@ -712,32 +785,38 @@ hipError_t launch_s(const StateBase& s, const LayerBatch& lb, size_t lds, bool v
 
 }  // namespace
 
-// Ints of region 1 of the bitmap kernel's LDS, rounded to 16 bytes.
-static size_t bitmap_r1_ints(int k, int ngroups, bool wide) {
-    // bitmap, group ranks, slot by rank (k) and one spare word per lane (64)
-    const size_t look = 5 * static_cast<size_t>(ngroups) + static_cast<size_t>(k) + 64;
-    const size_t miss = (wide ? 3 : 2) * static_cast<size_t>(k);
-    const size_t r1 = look > miss ? look : miss;
+// Ints of region 1 of the bitmap kernel's LDS, rounded to 16 bytes: bitmap,
+// ranks (per group, or per word), slot by rank with a spare word per lane,
+// victim lists.
+static size_t bitmap_r1_ints(int k, int ngroups, bool word_ranks) {
+    const size_t r1 = (word_ranks ? 8 : 5) * static_cast<size_t>(ngroups) + 3 * static_cast<size_t>(k) + 64;
     return (r1 + 3) & ~static_cast<size_t>(3);
 }
 
+// Word ranks (fewer instructions a lookup) unless the launch is wide, where
+// the LDS a unit needs decides how many units share a CU.
+static bool bitmap_word_ranks(bool wide) { return !wide; }
+
 size_t bitmap_lds_bytes(int k, int64_t L_ctx, bool wide) {
     const int ng = static_cast<int>((L_ctx + 127) >> 7);
-    return sizeof(int) * (bitmap_r1_ints(k, ng, wide) + kHistBins + kMiscWords);
+    return sizeof(int) * (bitmap_r1_ints(k, ng, bitmap_word_ranks(wide)) + kHistBins + kMiscWords);
 }
 
-int bitmap_lanes(int B, int k, bool wide) {
-    // 512 lanes let four units share a CU in wide launches (fewer lanes per
-    // unit, more units in flight); a few units per launch take 1024 lanes
-    return (wide && B <= 8 * 512 && k <= 4 * 512) ? 512 : 1024;
+int bitmap_lanes(int B, int k, bool wide, int asked) {
+    // 512 lanes let three units share a CU in wide launches; a few units per
+    // launch take 1024 lanes unless asked otherwise
+    const bool can512 = B <= 8 * 512 && k <= 4 * 512;
+    if (asked == 512) return can512 ? 512 : 1024;
+    if (asked == 1024) return 1024;
+    return (wide && can512) ? 512 : 1024;
 }
 
 hipError_t launch_bitmap_resolve(const StateBase& s, const LayerBatch& lb_in, bool wide, bool vec, hipStream_t st) {
     LayerBatch lb = lb_in;
     lb.ngroups = static_cast<int>((s.L_ctx + 127) >> 7);
-    lb.r1_ints = static_cast<int>(bitmap_r1_ints(lb.k, lb.ngroups, wide));
+    lb.r1_ints = static_cast<int>(bitmap_r1_ints(lb.k, lb.ngroups, bitmap_word_ranks(wide)));
     const size_t lds = bitmap_lds_bytes(lb.k, s.L_ctx, wide);
-    if (bitmap_lanes(s.B, lb.k, wide) == 512) {
+    if (bitmap_lanes(s.B, lb.k, wide, lb.lanes) == 512) {
         return wide ? launch_s<512, true>(s, lb, lds, vec, st) : launch_s<512, false>(s, lb, lds, vec, st);
     }
     return wide ? launch_s<1024, true>(s, lb, lds, vec, st) : launch_s<1024, false>(s, lb, lds, vec, st);

@@ -228,6 +228,9 @@ int hisparse_reset(hisparse_t h);
 #define HS_PROBE_SLOT_SCAN_HASH 2 /* the slot scan with the LDS hash whatever the history length */
 #define HS_OPT_ATTN_HEADS 7     /* heads per workgroup of hisparse_attend_mla: 32 or 64, or 0 to */
                                 /* choose by shape (default)                                      */
+#define HS_OPT_META_LANES 8     /* lanes a (request, layer) of the bitmap metadata kernel: 512 or */
+                                /* 1024, or 0 to choose by launch size (default); 512 applies     */
+                                /* only up to B = 4096 and k = 2048                               */
 int hisparse_set_option(hisparse_t h, int key, int64_t value);
 
 /* Per-kernel times of launches issued while HS_OPT_TIMING was on, measured
