@@ -109,58 +109,27 @@ __device__ inline void store_run_masked(T* g, int i0, int n, const T (&v)[N], un
     }
 }
 
-// Rank of position p among the selected positions (its bit must be set).
-// WR: ranks are kept per 32-bit word of the bitmap -- rank = the word's rank
-// plus the set bits below p in the word (two LDS reads, a handful of ALU
-// instructions).  Otherwise ranks are kept per 16-byte group of words (a
-// quarter of the LDS): rank = the group's rank plus the set bits before p in
-// the group, with one 16-byte read of the group.  Lookups go in batches:
-// every batch's LDS reads are issued first, then the ranks are computed
-// straight-line (selects, no branches).  The empty asm keeps all four words
-// of every group live, so no read is narrowed to 12 bytes plus a branch for
-// the last word.
-template <int N, bool WR>
-__device__ inline void bitmap_ranks(const uint4* bits4, const int* ranks, const int (&p)[N], int (&rank)[N],
+// Ranks of positions p[0..N) among the selected positions, and which of them
+// are selected: each 32-bit word of the bitmap carries the rank of its first
+// bit (16-bit ranks: k <= 4096), so rank = the word's rank + the set bits
+// below p in the word -- two LDS reads and a handful of ALU instructions.
+// All N lookups' reads are issued before any rank is computed.
+template <int N>
+__device__ inline void bitmap_ranks(const unsigned* bits, const uint16_t* wrank, const int (&p)[N], int (&rank)[N],
                                     unsigned& isset) {
+    unsigned w[N];
+    int base[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        w[i] = bits[p[i] >> 5];
+        base[i] = wrank[p[i] >> 5];
+    }
     isset = 0;
-    if constexpr (WR) {
-        // a rank per 32-bit word: the word, its rank, the set bits below p
-        const unsigned* bits = reinterpret_cast<const unsigned*>(bits4);
-        unsigned w[N];
-        int base[N];
 #pragma unroll
-        for (int i = 0; i < N; ++i) {
-            w[i] = bits[p[i] >> 5];
-            base[i] = ranks[p[i] >> 5];
-        }
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const unsigned sh = static_cast<unsigned>(p[i]) & 31u;
-            rank[i] = base[i] + __popc(w[i] & ((1u << sh) - 1u));
-            isset |= ((w[i] >> sh) & 1u) << i;
-        }
-    } else {
-        uint4 g[N];
-        int base[N];
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            g[i] = bits4[p[i] >> 7];
-            base[i] = ranks[p[i] >> 7];
-        }
-#pragma unroll
-        for (int i = 0; i < N; ++i) asm volatile("" : "+v"(g[i].x), "+v"(g[i].y), "+v"(g[i].z), "+v"(g[i].w));
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const unsigned wi = static_cast<unsigned>(p[i] >> 5) & 3u;
-            const unsigned lo = (wi & 1u) ? g[i].y : g[i].x;
-            const unsigned hi = (wi & 1u) ? g[i].w : g[i].z;
-            const unsigned w = (wi & 2u) ? hi : lo;
-            const unsigned bit = 1u << (p[i] & 31);
-            const int pre = (wi > 0u ? __popc(g[i].x) : 0) + (wi > 1u ? __popc(g[i].y) : 0) +
-                            (wi > 2u ? __popc(g[i].z) : 0);
-            rank[i] = base[i] + pre + __popc(w & (bit - 1u));
-            isset |= static_cast<unsigned>((w & bit) != 0u) << i;
-        }
+    for (int i = 0; i < N; ++i) {
+        const unsigned sh = static_cast<unsigned>(p[i]) & 31u;
+        rank[i] = base[i] + __popc(w[i] & ((1u << sh) - 1u));
+        isset |= ((w[i] >> sh) & 1u) << i;
     }
 }
 
@@ -355,8 +324,8 @@ __device__ inline void copy_misses(const StateBase& s, const int* mpos, const in
 }
 
 // LDS layout (ints): region 1 -- bitmap [4*NG words as NG 16-byte groups],
-// ranks [NG per group, or 4*NG per word when WR], slot by rank [k] with a
-// spare word per lane [64], victim
+// 16-bit rank of each word [4*NG halves], slot by rank [k] with a spare word
+// per lane [64], victim
 // slot by victim rank [k], evicted position by victim rank [k] -- then the
 // histogram [kHistBins] and the misc block [kMiscWords].
 //
@@ -372,7 +341,7 @@ __device__ inline void copy_misses(const StateBase& s, const int* mpos, const in
 // the candidates; B4 slot by rank, and (m > 0) threshold and packed victim
 // counts; B5 (m > 0 only) hits published, victims listed by rank, miss counts.
 // After B5 each missing selection takes the victim of its own rank.
-template <int NT, int SPL, int PER, bool VEC, bool WIDE, bool WR>
+template <int NT, int SPL, int PER, bool VEC, bool WIDE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WIDE ? 6 : 1)))
 void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     constexpr int NW = NT / 64;
@@ -391,8 +360,8 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     int32_t* mc_u = s.miss_count + rl;
     uint4* const bits4 = reinterpret_cast<uint4*>(lds);
     unsigned* const bits = reinterpret_cast<unsigned*>(lds);
-    int* const grank = lds + 4 * NG;               // [NG] group ranks, or [4*NG] word ranks (WR)
-    int* const byrank = grank + (WR ? 4 * NG : NG);
+    uint16_t* const wrank = reinterpret_cast<uint16_t*>(lds + 4 * NG);  // [4*NG] rank of each word
+    int* const byrank = lds + 6 * NG;
     int* const vlist = byrank + k + 64;
     int* const vold = vlist + k;
     int* const hist = lds + lb.r1_ints;
@@ -414,6 +383,9 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     load_run<SPL, VEC, int>(sel, j0, k, selv, kEmpty);
     int spos[PER];
     load_run<PER, VEC, int>(spos_g, s0, B, spos, kEmpty);
+    // (the stamp run is read even by a unit that will hit everywhere: its
+    // hit stamps go back as whole 16-byte pieces, which measured faster than
+    // scattered 4-byte stores without the read)
     uint32_t tsv[PER];
     load_run<PER, VEC, uint32_t>(ts_g, s0, B, tsv, 0u);
     for (int g = tid; g < NG; g += NT) bits4[g] = make_uint4(0u, 0u, 0u, 0u);
@@ -476,18 +448,10 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         int base = __builtin_amdgcn_readlane(wb, 63) + incl - cnt;
         for (int g = tid; g < NG; g += NT) {
             const uint4 v = bits4[g];
-            if constexpr (WR) {
-                int4 rk;
-                rk.x = base;
-                rk.y = rk.x + __popc(v.x);
-                rk.z = rk.y + __popc(v.y);
-                rk.w = rk.z + __popc(v.z);
-                reinterpret_cast<int4*>(grank)[g] = rk;
-                base = rk.w + __popc(v.w);
-            } else {
-                grank[g] = base;
-                base += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
-            }
+            const unsigned r0 = static_cast<unsigned>(base);
+            const unsigned r1 = r0 + __popc(v.x), r2 = r1 + __popc(v.y), r3 = r2 + __popc(v.z);
+            reinterpret_cast<uint2*>(wrank)[g] = make_uint2(r0 | (r1 << 16), r2 | (r3 << 16));
+            base = static_cast<int>(r3) + __popc(v.w);
         }
     }
     // hit test of this lane's slots (one bit each: a cached position whose
@@ -541,7 +505,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
             unsigned isset;
 #pragma unroll
             for (int i = 0; i < NB; ++i) pp[i] = ((hitbits >> (q0 + i)) & 1u) ? spos[q0 + i] : 0;
-            bitmap_ranks<NB, WR>(bits4, grank, pp, rk, isset);
+            bitmap_ranks<NB>(bits, wrank, pp, rk, isset);
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
                 const bool hit = (hitbits >> (q0 + i)) & 1u;
@@ -618,7 +582,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         unsigned isset;
 #pragma unroll
         for (int q = 0; q < SPL; ++q) pp[q] = j0 + q < k ? selv[q] : 0;
-        bitmap_ranks<SPL, WR>(bits4, grank, pp, rk, isset);
+        bitmap_ranks<SPL>(bits, wrank, pp, rk, isset);
         (void)isset;
         int v[SPL];
 #pragma unroll
@@ -747,12 +711,11 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
 
 template <int NT, int SPL, int PER, bool VEC, bool WIDE>
 hipError_t launch_b(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
-    constexpr bool WR = !WIDE;  // as bitmap_word_ranks
     static LdsGrants granted;  // per instantiation
-    const void* fn = reinterpret_cast<const void*>(&bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE, WR>);
+    const void* fn = reinterpret_cast<const void*>(&bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE>);
     const hipError_t e = ensure_lds_limit(fn, lds, granted);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE, WR>), dim3(s.R, lb.n), dim3(NT), lds, st, s, lb);
+    hipLaunchKernelGGL((bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE>), dim3(s.R, lb.n), dim3(NT), lds, st, s, lb);
     return hipGetLastError();
 }
 
@@ -785,21 +748,18 @@ hipError_t launch_s(const StateBase& s, const LayerBatch& lb, size_t lds, bool v
 
 }  // namespace
 
-// Ints of region 1 of the bitmap kernel's LDS, rounded to 16 bytes: bitmap,
-// ranks (per group, or per word), slot by rank with a spare word per lane,
-// victim lists.
-static size_t bitmap_r1_ints(int k, int ngroups, bool word_ranks) {
-    const size_t r1 = (word_ranks ? 8 : 5) * static_cast<size_t>(ngroups) + 3 * static_cast<size_t>(k) + 64;
+// Ints of region 1 of the bitmap kernel's LDS, rounded to 16 bytes: bitmap
+// (4 per group), 16-bit word ranks (2 per group), slot by rank with a spare
+// word per lane, victim lists.
+static size_t bitmap_r1_ints(int k, int ngroups) {
+    const size_t r1 = 6 * static_cast<size_t>(ngroups) + 3 * static_cast<size_t>(k) + 64;
     return (r1 + 3) & ~static_cast<size_t>(3);
 }
 
-// Word ranks (fewer instructions a lookup) unless the launch is wide, where
-// the LDS a unit needs decides how many units share a CU.
-static bool bitmap_word_ranks(bool wide) { return !wide; }
-
 size_t bitmap_lds_bytes(int k, int64_t L_ctx, bool wide) {
     const int ng = static_cast<int>((L_ctx + 127) >> 7);
-    return sizeof(int) * (bitmap_r1_ints(k, ng, bitmap_word_ranks(wide)) + kHistBins + kMiscWords);
+    (void)wide;
+    return sizeof(int) * (bitmap_r1_ints(k, ng) + kHistBins + kMiscWords);
 }
 
 int bitmap_lanes(int B, int k, bool wide, int asked) {
@@ -814,7 +774,7 @@ int bitmap_lanes(int B, int k, bool wide, int asked) {
 hipError_t launch_bitmap_resolve(const StateBase& s, const LayerBatch& lb_in, bool wide, bool vec, hipStream_t st) {
     LayerBatch lb = lb_in;
     lb.ngroups = static_cast<int>((s.L_ctx + 127) >> 7);
-    lb.r1_ints = static_cast<int>(bitmap_r1_ints(lb.k, lb.ngroups, bitmap_word_ranks(wide)));
+    lb.r1_ints = static_cast<int>(bitmap_r1_ints(lb.k, lb.ngroups));
     const size_t lds = bitmap_lds_bytes(lb.k, s.L_ctx, wide);
     if (bitmap_lanes(s.B, lb.k, wide, lb.lanes) == 512) {
         return wide ? launch_s<512, true>(s, lb, lds, vec, st) : launch_s<512, false>(s, lb, lds, vec, st);
