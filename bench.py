@@ -4,13 +4,16 @@ A step is one decode step through every layer of the workload: for each
 layer, one hisparse_resolve over all requests (hash build, cache probe,
 victim choice, metadata update, host fetch of the misses, publication).
 Inputs (the whole selection trace and the pinned host pool) are resident
-before the timed region starts.
+before the timed region starts.  The default workload is the largest
+single-GPU configuration, gqa_record (64 requests x 16 layers, 4 KB records).
 
 Printed: one JSON line with resolved selections/s (the headline), miss-fetch
 GB/s against host-link peaks measured in the same run, the dominant kernel's
 roofline (the fetch kernel, bound by the host link), a hit-only leg for the
-metadata path against a measured HBM peak, and the CPU oracle timed on a
-bounded sample of the same workload.
+metadata path against a measured HBM peak, the MLA attention consumer at the
+latent-record shape, a sweep of every workload's throughput and link
+fraction against the same run's peaks, and the CPU oracle timed on a bounded
+sample of the same workload (one pinned core, then every core).
 """
 from __future__ import annotations
 
@@ -31,12 +34,14 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 
 
-def fetch_traffic():
-    """Scaled FETCH_SIZE + WRITE_SIZE bytes per fetch_kernel launch from the
-    committed counter summary, or None if the kernel source changed since."""
+def fetch_traffic(workload="mla_latent"):
+    """Scaled FETCH_SIZE + WRITE_SIZE bytes per fetch_kernel launch of a
+    workload from its committed counter summary, or None if there is none or
+    the kernel source changed since it was taken."""
     import hashlib
     import re
-    prof = os.path.join(ROOT, "profiles", "fetch_kernel_traffic_mla_latent.md")
+    rel = os.path.join("profiles", f"fetch_kernel_traffic_{workload}.md")
+    prof = os.path.join(ROOT, rel)
     src = os.path.join(ROOT, "hierarchical_kv_cache_resolve_amd", "csrc", "fetch.hip")
     try:
         text = open(prof).read()
@@ -49,8 +54,7 @@ def fetch_traffic():
     if not (m and rd and wr) or m.group(1) != digest:
         return None
     return {"read_bytes": int(rd.group(1)), "write_bytes": int(wr.group(1)),
-            "total_bytes": int(rd.group(1)) + int(wr.group(1)),
-            "source": "profiles/fetch_kernel_traffic_mla_latent.md"}
+            "total_bytes": int(rd.group(1)) + int(wr.group(1)), "source": rel}
 
 
 def log(msg):
@@ -60,9 +64,9 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=240)
-    ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="mla_latent")
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="gqa_record")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hit-only", action="store_true")
@@ -88,6 +92,9 @@ def parse():
                     help="skip the separate timing of the MLA attention consumer on the workload's shape")
     ap.add_argument("--hit-only-workload", default="gqa_record",
                     help="shapes of the hit-only leg (its pool aliases every history onto one region)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the sweep of the other workloads (each on an aliased 4 GiB pool)")
+    ap.add_argument("--sweep-steps", type=int, default=24)
     return ap.parse_args()
 
 
@@ -156,10 +163,14 @@ def main():
         elif attn is not None:
             res.attend_mla(l, attn["q"], out[l], attn["scale"], attn["o"], attn["lse"], sp)
 
-    def step(t, sp, capturing=False, prefetch=use_prefetch):
+    def step(t, sp, capturing=False, prefetch=use_prefetch, hook=None):
         if not prefetch:
             for l in range(w.num_layers):
+                if hook:
+                    hook(l, "before")
                 res.resolve(l, sel[t, l], out[l], sp)
+                if hook:
+                    hook(l, "after")
                 consume(l, sp)
             return
         # shared-selection groups: anchor, replay of its plan on the side
@@ -172,7 +183,11 @@ def main():
             res.prefetch(g0, shared, side)
             consume(g0, sp)
             for l in shared:
+                if hook:
+                    hook(l, "before")
                 res.resolve(l, sel[t, l], out[l], sp)
+                if hook:
+                    hook(l, "after")
                 consume(l, sp)
 
     def timed_run(prefetch):
@@ -242,6 +257,7 @@ def main():
                         "consumer_between_layers": args.consumer,
                         "saving": 1.0 - elapsed / off}
         log(f"prefetch on {elapsed * 1e3 / K:.3f} ms/step, off {off * 1e3 / K:.3f} ms/step")
+        prefetch_cmp.update(exposed_io(hs, torch, res, w, step, W, K, sptr))
 
     sels = K * w.num_layers * w.num_req * w.k
     misses = s1.misses - s0.misses
@@ -323,11 +339,13 @@ def main():
             "peak": link_peak,
             "unit": "GB/s",
             "frac": achieved / link_peak,
-            # the counters were taken on mla_latent's launches: no figure for other workloads
-            "traffic": (fetch_traffic() or {}).get("total_bytes") if w.name == "mla_latent" else None,
-            "traffic_detail": fetch_traffic() if w.name == "mla_latent" else None,
+            "frac_published": achieved / PCIE5_X16_GBPS,
+            # HBM + link bytes of the workload's fetch launches from its committed counter summary
+            # (None if there is none, or if the kernel source changed since it was taken)
+            "traffic": (fetch_traffic(w.name) or {}).get("total_bytes"),
+            "traffic_detail": fetch_traffic(w.name),
             "peak_note": "peak = max(SDMA H2D copy, 16 B-load streaming kernel) measured in this run; "
-                         f"published PCIe 5.0 x16 = {PCIE5_X16_GBPS} GB/s per direction",
+                         f"frac_published against PCIe 5.0 x16 = {PCIE5_X16_GBPS} GB/s per direction",
             "avg_launch_ms": fetch_avg_ms,
             "bytes_per_launch": fetch_bytes / tim.fetch_launches,
         }
@@ -351,6 +369,12 @@ def main():
 
     res.close()
 
+    if not args.no_attention_leg and not mla_records:
+        # the consumer needs 576-element latent records: it runs at the latent
+        # workload's shape on a pool that aliases every history onto one region
+        result["attention"] = attention_leg_latent_shape(hs, tg, torch, dev, sptr, args.heads, hbm_peak,
+                                                         heads_per_wg=args.attn_heads_per_wg)
+
     if not args.no_hit_only:
         result["hit_only"] = hit_only_leg(hs, tg, torch, tg.WORKLOADS[args.hit_only_workload], dev, sptr, hbm_peak,
                                           meta_lanes=args.meta_lanes)
@@ -360,7 +384,11 @@ def main():
         result["cpu_baseline_threads"] = cpu_baseline_threads(tg, w, tr, pool, W,
                                                               result["cpu_baseline"]["steps"])
 
+    # the pinned pools of the sweep fit only once the workload's pool is released
     pool.free()
+    if not args.no_sweep:
+        result["sweep"] = sweep(hs, tg, torch, dev, sptr, w.name, link_peak if link_sdma else None,
+                                args.sweep_steps, nthreads)
     print(json.dumps(result), flush=True)
 
 
@@ -506,33 +534,182 @@ def hit_only_leg(hs, tg, torch, w, dev, sptr, hbm_peak, steps=64, meta_lanes=0):
     return r
 
 
-def cpu_baseline(tg, w, tr, pool, warm_steps, seconds):
-    """The oracle as it stands, single-threaded, on the first steps of the same
-    workload until about `seconds` of resolve time have passed."""
-    from oracle import Oracle
-    pool_np = pool.numpy_view()
-    rr = w.region_rows()
-    o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes, model_bytes=True)
-    for t in range(warm_steps):
+def exposed_io(hs, torch, res, w, step, W, K, sptr):
+    """Exact prefetch on a shared-selection workload: how much of the shared
+    layers' resolve time the main stream still waits for.  The same K steps
+    run twice from a reset cache, prefetch off and on, with HIP events on the
+    main stream right before and after every shared layer's resolve; with
+    prefetch off that interval is the layer's own metadata work and host
+    fetch, with prefetch on it is the wait for the side stream's replay plus
+    the publish-only resolve.  The replay's own duration on the side stream
+    comes from the library's per-launch timing."""
+    shared = [l for l in range(w.num_layers) if l % w.group != 0]
+    out = {}
+    for prefetch in (False, True):
+        res.reset()
+        for t in range(W):
+            step(t, sptr, prefetch=prefetch)
+        torch.cuda.synchronize()
+        ev = []
+        res.set_option(hs.HS_OPT_TIMING, 1)
+        res.timing(clear=True)
+
+        def hook(l, when, _ev=ev):
+            if l in shared:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                _ev.append((l, when, e))
+
+        for t in range(W, W + K):
+            step(t, sptr, prefetch=prefetch, hook=hook)
+        torch.cuda.synchronize()
+        tim = res.timing(clear=True)
+        res.set_option(hs.HS_OPT_TIMING, 0)
+        total = 0.0
+        for (l0, w0, e0), (l1, w1, e1) in zip(ev[0::2], ev[1::2]):
+            assert l0 == l1 and w0 == "before" and w1 == "after"
+            total += e0.elapsed_time(e1)
+        key = "on" if prefetch else "off"
+        out[f"shared_resolve_exposed_ms_{key}"] = total / K
+        if prefetch:
+            out["replay_ms_per_step"] = tim.replay_ms / K
+            out["replay_launches_per_step"] = tim.replay_launches / K
+    out["io_hidden_frac"] = 1.0 - out["shared_resolve_exposed_ms_on"] / out["shared_resolve_exposed_ms_off"]
+    out["shared_layers"] = shared
+    out["exposed_io_note"] = ("per step, summed over the shared layers: main-stream time from right before to "
+                              "right after each shared layer's resolve (HIP events on the main stream)")
+    log(f"exposed shared-layer resolve: off {out['shared_resolve_exposed_ms_off']:.3f} ms/step, "
+        f"on {out['shared_resolve_exposed_ms_on']:.3f} ms/step -> hidden {out['io_hidden_frac']:.2f}")
+    return out
+
+
+def aliased(w, gib=4):
+    """The workload with its pool capped at about `gib` GiB (whole histories;
+    histories alias onto the physical regions modulo their number)."""
+    rows = max(w.L_ctx, ((gib << 30) // w.row_bytes) // w.L_ctx * w.L_ctx)
+    return w.replace(pool_rows_cap=min(rows, w.logical_rows))
+
+
+def attention_leg_latent_shape(hs, tg, torch, dev, sptr, heads, hbm_peak, heads_per_wg=0):
+    """The MLA consumer at the latent-record workload's shape (16 requests,
+    k = 2048, 576-element bf16 records, 128 heads), on slots published by two
+    RESOLVE steps of that workload over a pool in which every history aliases
+    onto one region."""
+    w = tg.WORKLOADS["mla_latent"].replace(pool_rows_cap=tg.WORKLOADS["mla_latent"].L_ctx)
+    tr = torch.from_numpy(tg.trace(w, steps=2)).to(dev)
+    pool = hs.HostPool.allocate(w.pool_rows * w.row_bytes)
+    tg.pool_fill(pool.ptr, 0, w.pool_rows * w.W_KV, w.pool_seed)
+    res = hs.Resolver(w.num_req, w.num_layers, w.B, w.W_KV, hs.BF16, pool, w.L_ctx, w.pool_rows,
+                      region_row=w.region_rows())
+    if heads_per_wg:
+        res.set_option(hs.HS_OPT_ATTN_HEADS, heads_per_wg)
+    out = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
+    for t in range(2):
         for l in range(w.num_layers):
-            o.resolve(l, tr[t, l], pool_np, rr)
-    n_steps, spent = 0, 0.0
-    t = warm_steps
-    while spent < seconds and t < tr.shape[0]:
+            res.resolve(l, tr[t, l], out[l], sptr)
+    torch.cuda.synchronize()
+    r = attention_leg(hs, torch, res, w, out, heads, dev, hbm_peak, heads_per_wg=heads_per_wg)
+    r["workload"] = "mla_latent shapes (16 requests x 8 layers, k=2048, 576-element bf16 records), aliased pool"
+    res.close()
+    pool.free()
+    return r
+
+
+def sweep(hs, tg, torch, dev, sptr, skip, link_peak, steps, nthreads):
+    """Every other workload at its full cache shape on an aliased pool of
+    about 4 GiB (the host fetch reads whatever row a history's position maps
+    to, so only the pool's footprint changes): steps run as one captured
+    graph after 8 eager warm-up steps, then replayed with per-launch timing.
+    Reports selections/s, the miss fetch over the step and the fetch kernel's
+    rate, each against the host-link peak measured earlier in this run."""
+    rows = {}
+    warm = 8
+    for name, w0 in tg.WORKLOADS.items():
+        if name == skip:
+            continue
+        w = aliased(w0)
+        tr = torch.from_numpy(tg.trace(w, steps=warm + steps, threads=nthreads)).to(dev)
+        pool = hs.HostPool.allocate(w.pool_rows * w.row_bytes)
+        tg.pool_fill(pool.ptr, 0, w.pool_rows * w.W_KV, w.pool_seed, nthreads)
+        res = hs.Resolver(w.num_req, w.num_layers, w.B, w.W_KV, hs.BF16, pool, w.L_ctx, w.pool_rows,
+                          region_row=w.region_rows())
+        out = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
+
+        def run_steps(t0, t1, sp):
+            for t in range(t0, t1):
+                for l in range(w.num_layers):
+                    res.resolve(l, tr[t, l], out[l], sp)
+
+        run_steps(0, warm, sptr)
+        torch.cuda.synchronize()
+        s0 = res.stats()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_steps(warm, warm + steps, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for l in range(w.num_layers):
-            o.resolve(l, tr[t, l], pool_np, rr)
-        spent += time.perf_counter() - t0
-        n_steps += 1
-        t += 1
-    o.close()
-    sels = n_steps * w.num_layers * w.num_req * w.k
-    log(f"cpu oracle: {n_steps} steps in {spent:.1f}s -> {sels / spent / 1e6:.2f} M sel/s")
-    return {"value": sels / spent, "unit": "selections/s", "cores": 1, "kind": "oracle",
-            "sample": f"steps {warm_steps}..{warm_steps + n_steps - 1} of {w.name} (all {w.num_req} requests x "
-                      f"{w.num_layers} layers, miss rows copied from the same pinned pool), after "
-                      f"{warm_steps} untimed warm steps; single thread",
-            "steps": n_steps, "cpu_model": cpu_model()}
+        g.replay()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        s1 = res.stats()
+        del g
+        res.reset()
+        run_steps(0, warm, sptr)
+        res.set_option(hs.HS_OPT_TIMING, 1)
+        res.timing(clear=True)
+        r0 = res.stats()
+        run_steps(warm, warm + steps, sptr)
+        torch.cuda.synchronize()
+        r1 = res.stats()
+        tim = res.timing(clear=True)
+        res.check_error()
+        miss_bytes = s1.miss_bytes - s0.miss_bytes
+        sels = steps * w.num_layers * w.num_req * w.k
+        fetch_gbps = (r1.miss_bytes - r0.miss_bytes) / (tim.fetch_ms * 1e-3) / 1e9 if tim.fetch_ms else None
+        row = {"selections_per_s": sels / dt, "ms_per_step": dt * 1e3 / steps,
+               "miss_rate": (s1.misses - s0.misses) / sels, "miss_fetch_GBps": miss_bytes / dt / 1e9,
+               "fetch_kernel_GBps": fetch_gbps, "plan_avg_us": tim.plan_ms * 1e3 / max(1, tim.plan_launches),
+               "fetch_avg_us": tim.fetch_ms * 1e3 / max(1, tim.fetch_launches),
+               "pool_GB": round(pool.nbytes / 1e9, 2), "logical_pool_GB": round(w.logical_rows * w.row_bytes / 1e9, 1)}
+        if link_peak:
+            row["miss_fetch_frac_of_link_peak"] = row["miss_fetch_GBps"] / link_peak
+            row["fetch_kernel_frac_of_link_peak"] = fetch_gbps / link_peak if fetch_gbps else None
+        rows[name] = row
+        log(f"sweep {name}: {row['selections_per_s'] / 1e6:.1f} M sel/s, {row['ms_per_step']:.3f} ms/step, "
+            f"miss {row['miss_fetch_GBps']:.1f} GB/s, fetch kernel "
+            f"{fetch_gbps if fetch_gbps else 0:.1f} GB/s, plan {row['plan_avg_us']:.1f} us")
+        res.close()
+        pool.free()
+        del tr, out
+        torch.cuda.empty_cache()
+    return rows
+
+
+def gpu_numa_node(torch):
+    """NUMA node of the GPU's PCI device (sysfs), or None."""
+    try:
+        p = torch.cuda.get_device_properties(0)
+        bdf = f"{getattr(p, 'pci_domain_id', 0):04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+        node = int(open(f"/sys/bus/pci/devices/{bdf}/numa_node").read().strip())
+        return node if node >= 0 else None
+    except (AttributeError, OSError, ValueError):
+        return None
+
+
+def node_cpus(node):
+    """CPUs of a NUMA node that this process may run on (all allowed CPUs if unknown)."""
+    allowed = sorted(os.sched_getaffinity(0))
+    if node is None:
+        return allowed
+    try:
+        cpus = set()
+        for part in open(f"/sys/devices/system/node/node{node}/cpulist").read().strip().split(","):
+            lo, _, hi = part.partition("-")
+            cpus.update(range(int(lo), int(hi or lo) + 1))
+        on_node = [c for c in allowed if c in cpus]
+        return on_node or allowed
+    except (OSError, ValueError):
+        return allowed
 
 
 def cpu_model():
@@ -545,37 +722,98 @@ def cpu_model():
     return None
 
 
+def cpu_baseline(tg, w, tr, pool, warm_steps, seconds):
+    """The oracle as it stands, single-threaded and pinned to one core on the
+    GPU's NUMA node, on the first steps of the same workload until about
+    `seconds` of resolve time have passed (miss rows copied from the same
+    pinned pool into its host cache model).  Runs after every GPU leg."""
+    import torch
+    from oracle import Oracle
+    node = gpu_numa_node(torch)
+    core = node_cpus(node)[0]
+    saved = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {core})
+    try:
+        pool_np = pool.numpy_view()
+        rr = w.region_rows()
+        o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes, model_bytes=True)
+        for t in range(warm_steps):
+            for l in range(w.num_layers):
+                o.resolve(l, tr[t, l], pool_np, rr)
+        n_steps, spent = 0, 0.0
+        t = warm_steps
+        while spent < seconds and t < tr.shape[0]:
+            t0 = time.perf_counter()
+            for l in range(w.num_layers):
+                o.resolve(l, tr[t, l], pool_np, rr)
+            spent += time.perf_counter() - t0
+            n_steps += 1
+            t += 1
+        o.close()
+    finally:
+        os.sched_setaffinity(0, saved)
+    sels = n_steps * w.num_layers * w.num_req * w.k
+    log(f"cpu oracle (core {core}, node {node}): {n_steps} steps in {spent:.1f}s -> {sels / spent / 1e6:.2f} M sel/s")
+    return {"value": sels / spent, "unit": "selections/s", "cores": 1, "kind": "oracle",
+            "sample": f"steps {warm_steps}..{warm_steps + n_steps - 1} of {w.name} (all {w.num_req} requests x "
+                      f"{w.num_layers} layers, miss rows copied from the same pinned pool), after "
+                      f"{warm_steps} untimed warm steps; single thread pinned to one core",
+            "steps": n_steps, "core": core, "numa_node": node,
+            "numa_note": None if node is not None else
+            "the platform reports no NUMA node for the GPU's PCI device (sysfs numa_node -1 or absent): "
+            "pinned to the first allowed core",
+            "cpu_model": cpu_model()}
+
+
 def cpu_baseline_threads(tg, w, tr, pool, warm_steps, n_steps):
-    """The same oracle sample with one thread per layer (layers are independent
-    and the oracle keeps no state shared between them; its calls release the
-    interpreter lock), wall clock around all threads."""
+    """The same oracle sample on every allowed core: the (request, layer)
+    units are independent, so each thread owns a share of them (one oracle
+    instance per unit) and runs all their steps; each thread is pinned to its
+    own core.  Wall clock around the timed steps of all threads."""
     import threading
     from oracle import Oracle
     pool_np = pool.numpy_view()
     rr = w.region_rows()
-    o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes, model_bytes=True)
+    cpus = sorted(os.sched_getaffinity(0))
+    n = len(cpus)
+    units = [(r, l) for r in range(w.num_req) for l in range(w.num_layers)]
+    shares = [units[i::n] for i in range(n)]
+    ready = threading.Barrier(n + 1)
+    go = threading.Barrier(n + 1)
+    done = threading.Barrier(n + 1)
 
-    def run_layer(l, t0, t1):
-        for t in range(t0, t1):
-            o.resolve(l, tr[t, l], pool_np, rr)
+    def worker(i):
+        os.sched_setaffinity(0, {cpus[i]})
+        mine = [(r, l, Oracle(1, 1, w.B, w.L_ctx, w.row_bytes, model_bytes=True),
+                 np.array([rr[r * w.num_layers + l]], dtype=np.int64)) for r, l in shares[i]]
+        for t in range(warm_steps):
+            for r, l, o, reg in mine:
+                o.resolve(0, tr[t, l, r:r + 1], pool_np, reg)
+        ready.wait()
+        go.wait()
+        for t in range(warm_steps, warm_steps + n_steps):
+            for r, l, o, reg in mine:
+                o.resolve(0, tr[t, l, r:r + 1], pool_np, reg)
+        done.wait()
+        for _, _, o, _ in mine:
+            o.close()
 
-    def run_all(t0, t1):
-        th = [threading.Thread(target=run_layer, args=(l, t0, t1)) for l in range(w.num_layers)]
-        for x in th:
-            x.start()
-        for x in th:
-            x.join()
-
-    run_all(0, warm_steps)
+    th = [threading.Thread(target=worker, args=(i,)) for i in range(n)]
+    for x in th:
+        x.start()
+    ready.wait()
     t0 = time.perf_counter()
-    run_all(warm_steps, warm_steps + n_steps)
+    go.wait()
+    done.wait()
     spent = time.perf_counter() - t0
-    o.close()
+    for x in th:
+        x.join()
     sels = n_steps * w.num_layers * w.num_req * w.k
-    log(f"cpu oracle, {w.num_layers} threads: {n_steps} steps in {spent:.1f}s -> {sels / spent / 1e6:.2f} M sel/s")
-    return {"value": sels / spent, "unit": "selections/s", "cores": w.num_layers, "kind": "oracle",
-            "sample": f"the single-thread sample, one thread per layer", "cpu_model": cpu_model(),
-            "host_cpus": os.cpu_count()}
+    log(f"cpu oracle, {n} threads: {n_steps} steps in {spent:.2f}s -> {sels / spent / 1e6:.2f} M sel/s")
+    return {"value": sels / spent, "unit": "selections/s", "cores": n, "kind": "oracle",
+            "sample": f"the single-thread sample, {len(units)} (request, layer) units spread over {n} threads, "
+                      "one per allowed core", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "allowed_cpus": n}
 
 
 if __name__ == "__main__":

@@ -61,3 +61,18 @@ def test_traffic_values_come_from_the_summary_table(tmp_path, monkeypatch):
     wr = int(re.search(r"\| written \(scaled WRITE_SIZE\) \| (\d+) \|", text).group(1))
     assert t == {"read_bytes": rd, "write_bytes": wr, "total_bytes": rd + wr,
                  "source": "profiles/fetch_kernel_traffic_mla_latent.md"}
+
+
+def test_traffic_summary_of_each_workload_parses():
+    """Every committed fetch-traffic summary names its workload and either
+    matches the current fetch kernel source or is ignored."""
+    import glob
+    sys.path.insert(0, ROOT)
+    import bench
+    for f in glob.glob(os.path.join(ROOT, "profiles", "fetch_kernel_traffic_*.md")):
+        name = os.path.basename(f)[len("fetch_kernel_traffic_"):-3]
+        t = bench.fetch_traffic(name)
+        if t is not None:
+            assert t["source"] == f"profiles/fetch_kernel_traffic_{name}.md"
+            assert t["read_bytes"] > 0 and t["write_bytes"] > 0
+    assert bench.fetch_traffic("no_such_workload") is None
