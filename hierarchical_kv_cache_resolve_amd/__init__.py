@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libhisparse.so")
 HS_OK = 0
 HS_E_INVAL, HS_E_HANDLE, HS_E_LAYER, HS_E_K, HS_E_ALIGN = -1, -2, -3, -4, -5
 HS_E_POOL, HS_E_NOMEM, HS_E_HIP, HS_E_DEVICE, HS_E_ORDER = -6, -7, -8, -9, -10
+HS_E_SCRATCH = -11
+HS_SCRATCH_BYTES = 64 << 20
 HS_DEV_RANGE, HS_DEV_DUP, HS_DEV_NOT_RESIDENT, HS_DEV_DIVERGED, HS_DEV_FULL = 1, 2, 3, 4, 5
 HS_MAX_B, HS_MAX_K, HS_MAX_REQ = 16384, 4096, 1024
 BF16, FP16, FP8, FP32 = 0, 1, 2, 3
@@ -30,7 +32,7 @@ HS_PROBE_PAGE_TABLE, HS_PROBE_SLOT_SCAN, HS_PROBE_SLOT_SCAN_HASH = 0, 1, 2
 
 _ERR_NAMES = {v: k for k, v in dict(HS_E_INVAL=-1, HS_E_HANDLE=-2, HS_E_LAYER=-3, HS_E_K=-4, HS_E_ALIGN=-5,
                                      HS_E_POOL=-6, HS_E_NOMEM=-7, HS_E_HIP=-8, HS_E_DEVICE=-9,
-                                     HS_E_ORDER=-10).items()}
+                                     HS_E_ORDER=-10, HS_E_SCRATCH=-11).items()}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (no fallback path exists)")
@@ -92,6 +94,7 @@ _sig("hisparse_host_alloc", _i32, _sz, _i32, ctypes.POINTER(_vp))
 _sig("hisparse_host_free", _i32, _vp)
 _sig("hisparse_gather_checksum", _i32, _vp, _i32, _vp, _i32, _vp, _vp)
 _sig("hisparse_attend_mla", _i32, _vp, _i32, _vp, _i32, _vp, _i32, ctypes.c_float, _vp, _vp, _vp)
+_sig("hisparse_attend_mla_noalloc", _i32, _vp, _i32, _vp, _i32, _vp, _i32, ctypes.c_float, _vp, _vp, _vp)
 for _n in ("hisparse_probe_link_sdma", "hisparse_probe_link_kernel", "hisparse_probe_hbm"):
     _sig(_n, _i32, _vp, _vp, _sz, _i32, _vp, ctypes.POINTER(ctypes.c_double))
 
@@ -249,6 +252,10 @@ def hisparse_gather_checksum(h, layer, d_slot_idx, k, d_out, stream) -> int:
 
 def hisparse_attend_mla(h, layer, d_q, num_heads, d_slot_idx, k, scale, d_out, d_lse, stream) -> int:
     return _lib.hisparse_attend_mla(h, layer, d_q, num_heads, d_slot_idx, k, scale, d_out, d_lse, stream)
+
+
+def hisparse_attend_mla_noalloc(h, layer, d_q, num_heads, d_slot_idx, k, scale, d_out, d_lse, stream) -> int:
+    return _lib.hisparse_attend_mla_noalloc(h, layer, d_q, num_heads, d_slot_idx, k, scale, d_out, d_lse, stream)
 
 
 def _probe(name, src, dst, nbytes, iters, stream):

@@ -53,9 +53,46 @@ struct hisparse_ctx {
     int64_t acc_n[4] = {0, 0, 0, 0};
 };
 
+// Scratch area of the no-allocation attention entry point: the fp32 split-k
+// partials of hisparse_attend_mla_noalloc live here instead of in a workspace
+// the handle allocates.  Each GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not the device copy: kernels and copies use the address that
+// hipGetSymbolAddress returns for the current device (scratch_ptr below).
+constexpr size_t kScratchFloats = static_cast<size_t>(16) << 20;  // 64 MiB
+static __device__ __align__(256) float scratch[kScratchFloats];
+
 namespace {
 
 enum { K_PLAN = 0, K_FETCH = 1, K_REPLAY = 2, K_PUBLISH = 3 };
+
+// Device address of `scratch` on each device, looked up once per device with
+// that device current (at hisparse_create).
+constexpr int kScratchDevices = 64;
+std::mutex& scratch_mutex() {
+    static std::mutex m;
+    return m;
+}
+float* scratch_ptr[kScratchDevices] = {};
+
+int lookup_scratch(int device) {
+    if (device < 0 || device >= kScratchDevices) return HS_E_INVAL;
+    std::lock_guard<std::mutex> g(scratch_mutex());
+    if (scratch_ptr[device]) return HS_OK;
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return HS_E_HIP;
+    }
+    scratch_ptr[device] = static_cast<float*>(p);
+    return HS_OK;
+}
+
+float* device_scratch(int device) {
+    if (device < 0 || device >= kScratchDevices) return nullptr;
+    std::lock_guard<std::mutex> g(scratch_mutex());
+    return scratch_ptr[device];
+}
 constexpr size_t kRingPairs = 8192;
 
 #define HS_TRY(expr)                                      \
@@ -304,6 +341,11 @@ int hisparse_create(int num_req, int num_layers, int B, int W_KV, int dtype, con
         free_all(h);
         delete h;
         return HS_E_HIP;
+    }
+    if ((rc = lookup_scratch(h->device)) != HS_OK) {
+        free_all(h);
+        delete h;
+        return rc;
     }
     hipStream_t st = nullptr;
     if ((rc = init_state(h, st)) != HS_OK) {
@@ -726,18 +768,28 @@ int hisparse_gather_checksum(hisparse_t h, int layer, const int32_t* d_slot_idx,
                : HS_E_HIP;
 }
 
-int hisparse_attend_mla(hisparse_t h, int layer, const void* d_q, int num_heads, const int32_t* d_slot_idx, int k,
-                        float scale, float* d_out, float* d_lse, void* stream) {
+// Argument checks and the launch shape shared by both attention entry points.
+static int attend_shape(hisparse_t h, int layer, const void* d_q, int num_heads, const int32_t* d_slot_idx, int k,
+                        float* d_out, int* ht, int* chunk, size_t* need) {
     if (!valid(h)) return HS_E_HANDLE;
     if (layer < 0 || layer >= h->NL) return HS_E_LAYER;
     if (!d_q || !d_slot_idx || !d_out || num_heads < 64 || num_heads % 64 != 0 || num_heads > HS_MAX_HEADS)
         return HS_E_INVAL;
     if (h->dtype != HS_BF16 || h->W_KV != 576) return HS_E_INVAL;
     if (k < 1 || k > h->B) return HS_E_K;
-    const int ht = h->attn_heads ? h->attn_heads / 16 : hs::attend_head_tiles(h->R, num_heads, k);
-    const int chunk = hs::attend_chunk(h->R, num_heads, k, ht);
-    const int nchunk = (k + chunk - 1) / chunk;
-    const size_t need = hs::attend_workspace_floats(h->R, num_heads, nchunk);
+    *ht = h->attn_heads ? h->attn_heads / 16 : hs::attend_head_tiles(h->R, num_heads, k);
+    *chunk = hs::attend_chunk(h->R, num_heads, k, *ht);
+    const int nchunk = (k + *chunk - 1) / *chunk;
+    *need = hs::attend_workspace_floats(h->R, num_heads, nchunk);
+    return HS_OK;
+}
+
+int hisparse_attend_mla(hisparse_t h, int layer, const void* d_q, int num_heads, const int32_t* d_slot_idx, int k,
+                        float scale, float* d_out, float* d_lse, void* stream) {
+    int ht = 0, chunk = 0;
+    size_t need = 0;
+    const int rc = attend_shape(h, layer, d_q, num_heads, d_slot_idx, k, d_out, &ht, &chunk, &need);
+    if (rc != HS_OK) return rc;
     if (need > h->attn_ws_floats) {
         HS_TRY(hipDeviceSynchronize());
         if (h->attn_ws) (void)hipFree(h->attn_ws);
@@ -750,6 +802,26 @@ int hisparse_attend_mla(hisparse_t h, int layer, const void* d_q, int num_heads,
     }
     return hs::launch_attend_mla(h->s, layer, static_cast<const uint16_t*>(d_q), num_heads, d_slot_idx, k, scale,
                                  d_out, d_lse, h->attn_ws, ht, chunk, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? HS_OK
+               : HS_E_HIP;
+}
+
+int hisparse_attend_mla_noalloc(hisparse_t h, int layer, const void* d_q, int num_heads, const int32_t* d_slot_idx,
+                                int k, float scale, float* d_out, float* d_lse, void* stream) {
+    int ht = 0, chunk = 0;
+    size_t need = 0;
+    const int rc = attend_shape(h, layer, d_q, num_heads, d_slot_idx, k, d_out, &ht, &chunk, &need);
+    if (rc != HS_OK) return rc;
+    if (need > kScratchFloats) return HS_E_SCRATCH;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != h->device) {
+        (void)hipGetLastError();
+        return HS_E_INVAL;  // the handle's device must be current
+    }
+    float* ws = device_scratch(dev);
+    if (!ws) return HS_E_HIP;
+    return hs::launch_attend_mla(h->s, layer, static_cast<const uint16_t*>(d_q), num_heads, d_slot_idx, k, scale,
+                                 d_out, d_lse, ws, ht, chunk, static_cast<hipStream_t>(stream)) == hipSuccess
                ? HS_OK
                : HS_E_HIP;
 }

@@ -76,6 +76,7 @@ typedef struct hisparse_ctx* hisparse_t;
 #define HS_E_HIP (-8)     /* a HIP runtime call failed */
 #define HS_E_DEVICE (-9)  /* the sticky device error word is set */
 #define HS_E_ORDER (-10)  /* prefetch / shared-layer resolve issued out of order */
+#define HS_E_SCRATCH (-11) /* the call needs more scratch than the fixed no-allocation area holds */
 
 /* ---- device error codes (sticky word) -------------------------------------- */
 #define HS_DEV_RANGE 1        /* a position outside [0, length) of its history (length <= L_ctx) */
@@ -280,6 +281,23 @@ int hisparse_gather_checksum(hisparse_t h, int layer, const int32_t* d_slot_idx,
  * Errors: HS_E_HANDLE, HS_E_LAYER, HS_E_INVAL, HS_E_K, HS_E_NOMEM, HS_E_HIP. */
 int hisparse_attend_mla(hisparse_t h, int layer, const void* d_q, int num_heads, const int32_t* d_slot_idx, int k,
                         float scale, float* d_out, float* d_lse, void* stream);
+
+/* hisparse_attend_mla without any allocation, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * must not call hipMalloc, harnesses that forbid it).  Same arguments, same
+ * kernels and the same results as hisparse_attend_mla; its fp32 split-k
+ * partials go to a fixed device area of HS_SCRATCH_BYTES that the library
+ * holds on each GPU until the process ends, instead of the handle's
+ * workspace.  A call whose partials, num_req * num_heads * chunks * 514
+ * floats, exceed that area is refused with HS_E_SCRATCH (at most 64 MiB:
+ * e.g. 32 requests x 128 heads x k = 2048).  The handle's device must be
+ * current (else HS_E_INVAL).  All calls on one GPU share the area: calls that
+ * overlap on one GPU (on different streams, or from different handles) race
+ * and must be ordered by the caller.  Nothing in the area needs clearing
+ * between calls.  Errors: those of hisparse_attend_mla, HS_E_SCRATCH. */
+#define HS_SCRATCH_BYTES 67108864 /* 64 MiB */
+int hisparse_attend_mla_noalloc(hisparse_t h, int layer, const void* d_q, int num_heads, const int32_t* d_slot_idx,
+                                int k, float scale, float* d_out, float* d_lse, void* stream);
 
 /* Peak probes (synchronous; time `iters` repetitions with HIP events):
  *   link_sdma  : hipMemcpyAsync host -> device (copy engines);
