@@ -163,56 +163,20 @@ def main():
         elif attn is not None:
             res.attend_mla(l, attn["q"], out[l], attn["scale"], attn["o"], attn["lse"], sp)
 
-    def step(t, sp, capturing=False, prefetch=use_prefetch, hook=None):
-        if not prefetch:
-            for l in range(w.num_layers):
-                if hook:
-                    hook(l, "before")
-                res.resolve(l, sel[t, l], out[l], sp)
-                if hook:
-                    hook(l, "after")
-                consume(l, sp)
-            return
-        # shared-selection groups: anchor, replay of its plan on the side
-        # stream, then the shared layers only publish
-        for g0 in range(0, w.num_layers, w.group):
-            res.resolve(g0, sel[t, g0], out[g0], sp)
-            shared = list(range(g0 + 1, min(g0 + w.group, w.num_layers)))
-            if capturing:
-                side.wait_stream(torch.cuda.current_stream())
-            res.prefetch(g0, shared, side)
-            consume(g0, sp)
-            for l in shared:
-                if hook:
-                    hook(l, "before")
-                res.resolve(l, sel[t, l], out[l], sp)
-                if hook:
-                    hook(l, "after")
-                consume(l, sp)
+    step = make_step(res, w, sel, out, consume, side, use_prefetch)
 
     def timed_run(prefetch):
         """Run steps W..W+K-1 (as one captured graph unless --graph 0); returns seconds."""
-        graph = None
         if args.graph:
             # the timed steps as one HIP graph: every input already resident,
             # every pointer fixed, the step clock on the device
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                cap = torch.cuda.current_stream().cuda_stream
-                for t in range(W, W + K):
-                    step(t, cap, capturing=True, prefetch=prefetch)
-            torch.cuda.synchronize()
+            return graph_time(torch, step, W, W + K, prefetch)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        if graph is not None:
-            graph.replay()
-        else:
-            for t in range(W, W + K):
-                step(t, sptr, prefetch=prefetch)
+        for t in range(W, W + K):
+            step(t, sptr, prefetch=prefetch)
         torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
-        del graph
-        return dt
+        return time.perf_counter() - t0
 
     for t in range(W):
         step(t, sptr)
@@ -253,7 +217,7 @@ def main():
         for t in range(W):
             step(t, sptr, prefetch=False)
         off = timed_run(False)
-        prefetch_cmp = {"ms_per_step_prefetch_on": elapsed * 1e3 / K, "ms_per_step_prefetch_off": off * 1e3 / K,
+        prefetch_cmp = {"workload": w.name, "ms_per_step_prefetch_on": elapsed * 1e3 / K, "ms_per_step_prefetch_off": off * 1e3 / K,
                         "consumer_between_layers": args.consumer,
                         "saving": 1.0 - elapsed / off}
         log(f"prefetch on {elapsed * 1e3 / K:.3f} ms/step, off {off * 1e3 / K:.3f} ms/step")
@@ -388,8 +352,66 @@ def main():
     pool.free()
     if not args.no_sweep:
         result["sweep"] = sweep(hs, tg, torch, dev, sptr, w.name, link_peak if link_sdma else None,
-                                args.sweep_steps, nthreads)
+                                args.sweep_steps, nthreads, args.heads)
+        if "prefetch" not in result:
+            for row in result["sweep"].values():
+                if "prefetch" in row:
+                    result["prefetch"] = row["prefetch"]
     print(json.dumps(result), flush=True)
+
+
+def make_step(res, w, sel, out, consume, side, default_prefetch):
+    """One decode step of the workload: RESOLVE of every layer, each followed
+    by the consumer.  With exact prefetch (shared-selection groups), each
+    anchor is resolved, its plan replayed into the group's shared layers on
+    the side stream, and the shared layers then only publish.  `hook(l,
+    when)` runs right before and after each shared layer's resolve."""
+    import torch
+
+    def step(t, sp, capturing=False, prefetch=None, hook=None):
+        if prefetch is None:
+            prefetch = default_prefetch
+        if not prefetch:
+            for l in range(w.num_layers):
+                if hook:
+                    hook(l, "before")
+                res.resolve(l, sel[t, l], out[l], sp)
+                if hook:
+                    hook(l, "after")
+                consume(l, sp)
+            return
+        for g0 in range(0, w.num_layers, w.group):
+            res.resolve(g0, sel[t, g0], out[g0], sp)
+            shared = list(range(g0 + 1, min(g0 + w.group, w.num_layers)))
+            if capturing:
+                side.wait_stream(torch.cuda.current_stream())
+            res.prefetch(g0, shared, side)
+            consume(g0, sp)
+            for l in shared:
+                if hook:
+                    hook(l, "before")
+                res.resolve(l, sel[t, l], out[l], sp)
+                if hook:
+                    hook(l, "after")
+                consume(l, sp)
+
+    return step
+
+
+def graph_time(torch, step, t0, t1, prefetch):
+    """Capture steps t0..t1-1 as one HIP graph, replay it once; seconds."""
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = torch.cuda.current_stream().cuda_stream
+        for t in range(t0, t1):
+            step(t, cap, capturing=True, prefetch=prefetch)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t_start
+    del graph
+    return dt
 
 
 def attention_buffers(torch, w, heads, dev):
@@ -570,17 +592,47 @@ def exposed_io(hs, torch, res, w, step, W, K, sptr):
             assert l0 == l1 and w0 == "before" and w1 == "after"
             total += e0.elapsed_time(e1)
         key = "on" if prefetch else "off"
-        out[f"shared_resolve_exposed_ms_{key}"] = total / K
+        out[f"exposed_io_ms_{key}"] = total / K
         if prefetch:
             out["replay_ms_per_step"] = tim.replay_ms / K
             out["replay_launches_per_step"] = tim.replay_launches / K
-    out["io_hidden_frac"] = 1.0 - out["shared_resolve_exposed_ms_on"] / out["shared_resolve_exposed_ms_off"]
+    out["io_hidden_frac"] = 1.0 - out["exposed_io_ms_on"] / out["exposed_io_ms_off"]
     out["shared_layers"] = shared
     out["exposed_io_note"] = ("per step, summed over the shared layers: main-stream time from right before to "
                               "right after each shared layer's resolve (HIP events on the main stream)")
-    log(f"exposed shared-layer resolve: off {out['shared_resolve_exposed_ms_off']:.3f} ms/step, "
-        f"on {out['shared_resolve_exposed_ms_on']:.3f} ms/step -> hidden {out['io_hidden_frac']:.2f}")
+    log(f"exposed shared-layer resolve: off {out['exposed_io_ms_off']:.3f} ms/step, "
+        f"on {out['exposed_io_ms_on']:.3f} ms/step -> hidden {out['io_hidden_frac']:.2f}")
     return out
+
+
+def prefetch_leg(hs, torch, res, w, sel, out, dev, sptr, W, K, heads):
+    """Exact prefetch on a shared-selection workload with MLA attention after
+    every layer: the step time with prefetch on and off (one captured graph
+    each, from a reset cache after W warm steps), then the shared layers'
+    exposed resolve time both ways (exposed_io)."""
+    side = torch.cuda.Stream()
+    attn = attention_buffers(torch, w, heads, dev)
+    res.attend_mla(0, attn["q"], out[0], attn["scale"], attn["o"], attn["lse"])  # sizes the workspace
+    torch.cuda.synchronize()
+
+    def consume(l, sp):
+        res.attend_mla(l, attn["q"], out[l], attn["scale"], attn["o"], attn["lse"], sp)
+
+    step = make_step(res, w, sel, out, consume, side, True)
+    secs = {}
+    for prefetch in (True, False):
+        res.reset()
+        for t in range(W):
+            step(t, sptr, prefetch=prefetch)
+        torch.cuda.synchronize()
+        secs[prefetch] = graph_time(torch, step, W, W + K, prefetch)
+    r = {"workload": w.name, "consumer_between_layers": "attention",
+         "ms_per_step_prefetch_on": secs[True] * 1e3 / K, "ms_per_step_prefetch_off": secs[False] * 1e3 / K,
+         "saving": 1.0 - secs[True] / secs[False]}
+    log(f"prefetch ({w.name}): on {r['ms_per_step_prefetch_on']:.3f} ms/step, off {r['ms_per_step_prefetch_off']:.3f}")
+    r.update(exposed_io(hs, torch, res, w, step, W, K, sptr))
+    res.check_error()
+    return r
 
 
 def aliased(w, gib=4):
@@ -615,13 +667,15 @@ def attention_leg_latent_shape(hs, tg, torch, dev, sptr, heads, hbm_peak, heads_
     return r
 
 
-def sweep(hs, tg, torch, dev, sptr, skip, link_peak, steps, nthreads):
+def sweep(hs, tg, torch, dev, sptr, skip, link_peak, steps, nthreads, heads=128):
     """Every other workload at its full cache shape on an aliased pool of
     about 4 GiB (the host fetch reads whatever row a history's position maps
     to, so only the pool's footprint changes): steps run as one captured
     graph after 8 eager warm-up steps, then replayed with per-launch timing.
     Reports selections/s, the miss fetch over the step and the fetch kernel's
-    rate, each against the host-link peak measured earlier in this run."""
+    rate, each against the host-link peak measured earlier in this run.  A
+    shared-selection workload with latent records also runs the exact-prefetch
+    leg (prefetch on and off, MLA attention between layers, exposed IO)."""
     rows = {}
     warm = 8
     for name, w0 in tg.WORKLOADS.items():
@@ -662,6 +716,7 @@ def sweep(hs, tg, torch, dev, sptr, skip, link_peak, steps, nthreads):
         torch.cuda.synchronize()
         r1 = res.stats()
         tim = res.timing(clear=True)
+        res.set_option(hs.HS_OPT_TIMING, 0)
         res.check_error()
         miss_bytes = s1.miss_bytes - s0.miss_bytes
         sels = steps * w.num_layers * w.num_req * w.k
@@ -674,6 +729,8 @@ def sweep(hs, tg, torch, dev, sptr, skip, link_peak, steps, nthreads):
         if link_peak:
             row["miss_fetch_frac_of_link_peak"] = row["miss_fetch_GBps"] / link_peak
             row["fetch_kernel_frac_of_link_peak"] = fetch_gbps / link_peak if fetch_gbps else None
+        if w.group > 1 and w.W_KV == 576 and w.elem_bytes == 2:
+            row["prefetch"] = prefetch_leg(hs, torch, res, w, tr, out, dev, sptr, warm, steps, heads)
         rows[name] = row
         log(f"sweep {name}: {row['selections_per_s'] / 1e6:.1f} M sel/s, {row['ms_per_step']:.3f} ms/step, "
             f"miss {row['miss_fetch_GBps']:.1f} GB/s, fetch kernel "

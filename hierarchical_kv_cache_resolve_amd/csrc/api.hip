@@ -205,10 +205,12 @@ int wait_event(hipStream_t st, hipEvent_t ev, bool ev_in_capture) {
     return HS_OK;
 }
 
-// Launch `fn` bracketed by timing events when timing is on.
+// Launch `fn` bracketed by timing events when timing is on.  A launch being
+// captured into a graph is not timed: its events would be graph nodes, never
+// recorded on the stream, and could not be read back.
 template <typename F>
 int timed(hisparse_ctx* h, int kind, hipStream_t st, F fn) {
-    if (!h->timing) {
+    if (!h->timing || capturing(st)) {
         return fn() == hipSuccess ? HS_OK : HS_E_HIP;
     }
     if (h->ring_used >= h->ring.size()) {

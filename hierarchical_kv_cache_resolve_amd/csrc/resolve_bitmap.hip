@@ -8,17 +8,18 @@
 // structure over the selected positions in shared memory, every cached slot
 // probed against it to mark hits, LRU victims for the misses (hits ranked
 // above newly fetched misses), then metadata update and publication.  The
-// lookup structure is a bitmap over the history's positions plus the rank of
-// each 16-byte group of bitmap words: the rank of a selected position is its
+// lookup structure is a bitmap over the history's positions plus a 16-bit
+// rank for each 32-bit bitmap word: the rank of a selected position is its
 // index among the selected positions, so a position maps to its selection in
 // O(1) with no probe chains.
 //
 // The kernel is laid out for the all-hit case, which decides the cost of a
-// layer whose selection barely moves: five barriers, every hit published as
-// soon as the selection side finds it, each lane's run of hit stamps written
-// back as whole 16-byte pieces.  Only a unit with misses goes on to the
-// victim search (age histogram, threshold, slot-order ranking), and there
-// the lane that takes a victim slot publishes the miss itself.
+// layer whose selection barely moves: four barriers, hits found on the slot
+// side by one bit test each, every hit published as soon as the selection
+// side reads its slot, each lane's run of hit stamps written back as whole
+// 16-byte pieces.  Only a unit with misses goes on to the victim search (age
+// histogram, threshold, slot-order ranking; one more barrier), and there the
+// lane of each miss publishes it from the victim list.
 //
 // Determinism: victims are the m candidate slots with the smallest
 // (stamp, slot) keys, assigned in ascending slot order to the misses in

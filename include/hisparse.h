@@ -235,8 +235,9 @@ int hisparse_reset(hisparse_t h);
 int hisparse_set_option(hisparse_t h, int key, int64_t value);
 
 /* Per-kernel times of launches issued while HS_OPT_TIMING was on, measured
- * with HIP events on the launch stream.  Synchronises the device.  `clear`
- * non-zero restarts the accumulation. */
+ * with HIP events on the launch stream (launches captured into a graph are
+ * not timed).  Synchronises the device.  `clear` non-zero restarts the
+ * accumulation. */
 typedef struct {
     double plan_ms, fetch_ms, replay_ms, publish_ms;
     int64_t plan_launches, fetch_launches, replay_launches, publish_launches;

@@ -29,10 +29,12 @@
  *
  * Readings where the pages leave a step open (each is also listed in the
  * design notes):
- *   - recency: "recency bits ... for LRU" is read as a per-slot stamp; a
- *     miss fetched at step t is stamped 2t+1 and a hit 2t+2, which places
- *     hits above newly fetched misses and both above anything older
- *     (pith "What carries the argument").
+ *   - recency: the per-slot recency information that the blog's section 2
+ *     (item 3, metadata) keeps for LRU is read as a 32-bit stamp per slot; a
+ *     miss fetched at step t is stamped 2t+1 and a hit 2t+2, so a step's hits
+ *     rank above the records it fetched and both above anything older (the
+ *     per-step refinement of LRU in the pith review's "What carries the
+ *     argument").
  *   - ties between equal stamps are broken by the lower slot index; empty
  *     slots (stamp 0) therefore go first, lowest slot first.
  *   - the i-th miss in ascending selection index j receives the i-th victim

@@ -133,3 +133,46 @@ def test_graph_replay_of_wide_batched_launches(hs):
     del g
     res.close()
     pool.free()
+
+
+def test_timing_skips_captured_launches(hs):
+    """Per-launch timing left on while a step is captured: the captured
+    launches are not timed (their events would never be recorded on the
+    stream), the eager launches around the capture are, and reading the
+    times after the replays succeeds."""
+    w = tg.PREFETCH.replace(name="graph_timing", num_req=4, num_layers=4, group=1, L_ctx=30000,
+                            k=512, B=1024, steps=6, W_KV=64)
+    print(f"[graph] {w.name} R={w.num_req} L={w.num_layers} B={w.B} k={w.k}", flush=True)
+    tr = tg.trace(w)
+    pool = make_pool(hs, w)
+    res = make_resolver(hs, w, pool)
+    dev = torch.device("cuda:0")
+    sel = torch.from_numpy(tr).to(dev)
+    sel_buf = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
+    out_buf = torch.empty_like(sel_buf)
+    cur = torch.cuda.current_stream()
+    res.set_option(hs.HS_OPT_TIMING, 1)
+    res.timing(clear=True)
+    for l in range(w.num_layers):  # one eager step: timed
+        res.resolve(l, sel[0, l], out_buf[l], cur)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        c = torch.cuda.current_stream()
+        for l in range(w.num_layers):
+            res.resolve(l, sel_buf[l], out_buf[l], c)
+    for t in (1, 2):
+        sel_buf.copy_(sel[t])
+        g.replay()
+    torch.cuda.synchronize()
+    for l in range(w.num_layers):  # one more eager step: timed
+        res.resolve(l, sel[3, l], out_buf[l], cur)
+    tim = res.timing(clear=True)
+    assert tim.plan_launches == 2 * w.num_layers and tim.fetch_launches == 2 * w.num_layers
+    assert tim.dropped == 0 and tim.plan_ms > 0 and tim.fetch_ms > 0
+    assert res.error()[0] == 0
+    st = res.state(0)
+    assert int(st["clock"][0]) == 4  # every step, captured or not, advanced the clock
+    del g
+    res.close()
+    pool.free()
