@@ -26,6 +26,15 @@ __device__ inline int wave_incl_scan(int x) {
     return x;
 }
 
+// Inclusive prefix sum within each row of 16 lanes (four DPP row shifts).
+__device__ inline int row_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    return x;
+}
+
 __device__ inline unsigned wave_min(unsigned v) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v = min(v, static_cast<unsigned>(__shfl_xor(static_cast<int>(v), off, 64)));

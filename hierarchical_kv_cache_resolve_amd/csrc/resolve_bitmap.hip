@@ -110,6 +110,17 @@ __device__ inline void store_run_masked(T* g, int i0, int n, const T (&v)[N], un
     }
 }
 
+// Bits 0 .. min(N, avail) - 1: which elements of a lane's run of N exist.
+// Per-element existence is carried as a bit mask in one register and tested
+// where it is used, rather than as N predicates the compiler would keep (or
+// spill) as scalar lane masks.
+template <int N>
+__device__ inline unsigned run_mask(int avail) {
+    static_assert(N <= 16, "runs of at most 16");
+    const int c = avail < 0 ? 0 : (avail > N ? N : avail);
+    return (1u << c) - 1u;
+}
+
 // Ranks of positions p[0..N) among the selected positions, and which of them
 // are selected: each 32-bit word of the bitmap carries the rank of its first
 // bit (16-bit ranks: k <= 4096), so rank = the word's rank + the set bits
@@ -138,39 +149,28 @@ __device__ inline void bitmap_ranks(const unsigned* bits, const uint16_t* wrank,
 // reaches `need`, and the count of the bins above it.  Every wave computes it
 // on its own from the finished histogram (no barrier, no broadcast): lane i
 // sums the 16 bins [1008 - 16i, 1023 - 16i], one wave scan orders the lanes
-// from the top, and the lane where the count crosses `need` walks its own
-// bins from the top.
+// from the top and a ballot finds the lane L where the count crosses `need`;
+// then lanes 0..15 take L's bins from the top down, one each, and a scan over
+// that row of 16 lanes finds the bin.  Requires 0 < need <= the histogram's
+// total.
 __device__ inline void crossing_from_top(const int* hist, int need, int& bin, int& below) {
     const int lane = threadIdx.x & 63;
     const int lo = kHistBins - kHistQ * (lane + 1);
-    int h[kHistQ];
+    int c = 0;
 #pragma unroll
     for (int i = 0; i < kHistQ; i += 4) {
         const int4 v = *reinterpret_cast<const int4*>(hist + lo + i);
-        h[i] = v.x;
-        h[i + 1] = v.y;
-        h[i + 2] = v.z;
-        h[i + 3] = v.w;
+        c += v.x + v.y + v.z + v.w;
     }
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < kHistQ; ++i) c += h[i];
     const int incl = wave_incl_scan(c);
-    const unsigned long long found = __ballot(incl - c < need && need <= incl);
-    const int L = __ffsll(static_cast<long long>(found)) - 1;  // wave-uniform
-    int acc = incl - c, my_bin = lo, my_below = acc;
-    bool done = false;
-#pragma unroll
-    for (int i = kHistQ - 1; i >= 0; --i) {
-        if (!done && need <= acc + h[i]) {
-            my_bin = lo + i;
-            my_below = acc;
-            done = true;
-        }
-        acc += h[i];
-    }
-    bin = __builtin_amdgcn_readlane(my_bin, L);
-    below = __builtin_amdgcn_readlane(my_below, L);
+    const int L = __ffsll(static_cast<long long>(__ballot(incl - c < need && need <= incl))) - 1;  // wave-uniform
+    const int loL = kHistBins - kHistQ * (L + 1);
+    const int aboveL = __builtin_amdgcn_readlane(incl - c, L);
+    const int hb = lane < kHistQ ? hist[loL + kHistQ - 1 - lane] : 0;
+    const int x = row_incl_scan(hb);
+    const int F = __ffsll(static_cast<long long>(__ballot(lane < kHistQ && need <= aboveL + x))) - 1;
+    bin = loL + kHistQ - 1 - F;
+    below = aboveL + __builtin_amdgcn_readlane(x - hb, F);
 }
 
 // Fallback threshold search among the slots flagged in `elig` (this lane's
@@ -326,9 +326,10 @@ __device__ inline void copy_misses(const StateBase& s, const int* mpos, const in
 
 // LDS layout (ints): region 1 -- bitmap [4*NG words as NG 16-byte groups],
 // 16-bit rank of each word [4*NG halves], slot by rank [k] with a spare word
-// per lane [64], victim
-// slot by victim rank [k], evicted position by victim rank [k] -- then the
-// histogram [kHistBins] and the misc block [kMiscWords].
+// per lane [64], then victim slot by victim rank [k] and evicted position by
+// victim rank [k] (wide launches: the two victim lists start at word 0 and
+// overlay the rest of region 1) -- then the histogram [kHistBins] and the
+// misc block [kMiscWords].
 //
 // Template parameters: NT lanes a unit; SPL selections and PER slots a lane
 // (contiguous runs j0 = tid*SPL, s0 = tid*PER); VEC: k and B multiples of 4
@@ -336,14 +337,16 @@ __device__ inline void copy_misses(const StateBase& s, const int* mpos, const in
 // WIDE: a launch over many units (held to six waves per SIMD, and it copies
 // its own misses).
 //
-// Barriers: B1 LDS cleared; B2 selection inserted; B3 group ranks, hit test of
+// Barriers: B1 LDS cleared; B2 selection inserted; B3 word ranks, hit test of
 // every slot (a bit test, no rank needed), hit count -- so m = k - h is known
 // here -- and, when the unit missed at its last step, the age histogram of
 // the candidates; B4 slot by rank, and (m > 0) threshold and packed victim
-// counts; B5 (m > 0 only) hits published, victims listed by rank, miss counts.
-// After B5 each missing selection takes the victim of its own rank.
+// counts; (m > 0 only) hits published and miss counts, then -- wide launches:
+// after one more barrier, as the lists overlay the bitmap -- victims listed
+// by rank, B5.  After B5 each missing selection takes the victim of its own
+// rank.
 template <int NT, int SPL, int PER, bool VEC, bool WIDE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WIDE ? 6 : 1)))
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WIDE ? (NT == 512 ? 8 : 6) : 1)))
 void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     constexpr int NW = NT / 64;
     static_assert(NW <= 16, "per-wave partials fit one row of 16 lanes");
@@ -363,7 +366,10 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     unsigned* const bits = reinterpret_cast<unsigned*>(lds);
     uint16_t* const wrank = reinterpret_cast<uint16_t*>(lds + 4 * NG);  // [4*NG] rank of each word
     int* const byrank = lds + 6 * NG;
-    int* const vlist = byrank + k + 64;
+    // victim lists: a wide launch lays them over the bitmap, its ranks and
+    // the slot by rank once every wave is done reading those (one more
+    // barrier, only in units with misses), so four units fit a CU's LDS
+    int* const vlist = WIDE ? lds : byrank + k + 64;
     int* const vold = vlist + k;
     int* const hist = lds + lb.r1_ints;
     int* const misc = hist + kHistBins;
@@ -380,6 +386,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     const int hist_len = s.length[rl];
     const bool spec = *mc_u > 0;  // expect misses: build the age histogram early
     const int j0 = tid * SPL, s0 = tid * PER;
+    const unsigned insel = run_mask<SPL>(k - j0), inslot = run_mask<PER>(B - s0);
     int selv[SPL];
     load_run<SPL, VEC, int>(sel, j0, k, selv, kEmpty);
     int spos[PER];
@@ -405,7 +412,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         for (int q = 0; q < SPL; ++q) {
             const int j = j0 + q;
             const int p = selv[q];
-            const bool live = j < k;
+            const bool live = (insel >> q) & 1u;
             const bool inr = live && static_cast<unsigned>(p) < static_cast<unsigned>(hist_len);
             const unsigned bit = inr ? 1u << (p & 31) : 0u;
             const unsigned old = atomicOr(&bits[inr ? p >> 5 : 0], bit);
@@ -461,13 +468,28 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     const uint32_t ts_hit = 2u * t + 2u, ts_miss = 2u * t + 1u;
     const int nbits_pos = NG * 128;
     unsigned hitbits = 0;
+    {
+        unsigned w[PER];
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        const int p = spos[q];
-        const bool live = s0 + q < B && p >= 0 && p < nbits_pos;
-        const unsigned w = bits[live ? p >> 5 : 0];
-        hitbits |= static_cast<unsigned>(live && ((w >> (p & 31)) & 1u)) << q;
+        for (int q = 0; q < PER; ++q) {
+            // (a slot past the end of the run holds -1, as does an empty one)
+            const int p = spos[q];
+            const bool live = static_cast<unsigned>(p) < static_cast<unsigned>(nbits_pos);
+            w[q] = bits[live ? p >> 5 : 0];
+        }
+        // every word is read whether or not its slot is live (the empty asm
+        // uses each one unconditionally), so no read sits in a branch of its
+        // own that waits for it on the spot
+#pragma unroll
+        for (int q = 0; q < PER; ++q) asm volatile("" : "+v"(w[q]));
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int p = spos[q];
+            const bool live = static_cast<unsigned>(p) < static_cast<unsigned>(nbits_pos);
+            hitbits |= static_cast<unsigned>(live && ((w[q] >> (p & 31)) & 1u)) << q;
+        }
     }
+    const unsigned candbits = inslot & ~hitbits;  // slots that may be evicted
     if (hitbits) {
         uint32_t tsn[PER];
 #pragma unroll
@@ -484,7 +506,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
             int bin = -1;
-            if (s0 + q < B && !((hitbits >> q) & 1u)) {
+            if ((candbits >> q) & 1u) {
                 const uint32_t age = 2u * t - tsv[q];
                 bin = age < kHistBins - 1 ? static_cast<int>(age) : kHistBins - 1;
             }
@@ -526,7 +548,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
 #pragma unroll
             for (int q = 0; q < PER; ++q) {
                 int bin = -1;
-                if (s0 + q < B && !((hitbits >> q) & 1u)) {
+                if ((candbits >> q) & 1u) {
                     const uint32_t age = 2u * t - tsv[q];
                     bin = age < kHistBins - 1 ? static_cast<int>(age) : kHistBins - 1;
                 }
@@ -551,7 +573,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
                 unsigned old_bits = 0;
 #pragma unroll
                 for (int q = 0; q < PER; ++q)
-                    if (s0 + q < B && !((hitbits >> q) & 1u) &&
+                    if (((candbits >> q) & 1u) &&
                         2u * t - tsv[q] >= static_cast<uint32_t>(kHistBins - 1))
                         old_bits |= 1u << q;
                 __syncthreads();
@@ -560,7 +582,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         }
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            const bool cand = s0 + q < B && !((hitbits >> q) & 1u);
+            const bool cand = (candbits >> q) & 1u;
             strict_bits |= static_cast<unsigned>(cand && tsv[q] < T) << q;
             tie_bits |= static_cast<unsigned>(cand && tsv[q] == T) << q;
         }
@@ -582,7 +604,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         int pp[SPL], rk[SPL];
         unsigned isset;
 #pragma unroll
-        for (int q = 0; q < SPL; ++q) pp[q] = j0 + q < k ? selv[q] : 0;
+        for (int q = 0; q < SPL; ++q) pp[q] = ((insel >> q) & 1u) ? selv[q] : 0;
         bitmap_ranks<SPL>(bits, wrank, pp, rk, isset);
         (void)isset;
         int v[SPL];
@@ -590,7 +612,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         for (int q = 0; q < SPL; ++q) v[q] = byrank[rk[q]];
 #pragma unroll
         for (int q = 0; q < SPL; ++q) {
-            const bool live = j0 + q < k;
+            const bool live = (insel >> q) & 1u;
             slv[q] = live ? v[q] : kEmpty;
             mf |= static_cast<unsigned>(live && v[q] < 0) << q;
         }
@@ -645,6 +667,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     const int mc = __popc(mf);
     const int mincl = wave_incl_scan(mc);
     if (lane == 63) misc[X_MISS + wave] = mincl;
+    if constexpr (WIDE) __syncthreads();  // the victim lists overwrite the bitmap
     {
         const int vpre = vincl - packed + sum_before(misc + X_VICT, wave);
         int sb = vpre & 0xFFFF, tb = vpre >> 16;
@@ -660,10 +683,11 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
                 vlist[rank] = s0 + q;
                 vold[rank] = spos[q];
                 if (spos[q] >= 0) pt[spos[q]] = -1;
+                if constexpr (WIDE) ts_g[s0 + q] = ts_miss;  // (the stamp run is not kept live this far)
                 vbits |= 1u << q;
             }
         }
-        if (vbits) {
+        if (!WIDE && vbits) {
             uint32_t tsn[PER];
 #pragma unroll
             for (int q = 0; q < PER; ++q)
@@ -751,16 +775,16 @@ hipError_t launch_s(const StateBase& s, const LayerBatch& lb, size_t lds, bool v
 
 // Ints of region 1 of the bitmap kernel's LDS, rounded to 16 bytes: bitmap
 // (4 per group), 16-bit word ranks (2 per group), slot by rank with a spare
-// word per lane, victim lists.
-static size_t bitmap_r1_ints(int k, int ngroups) {
-    const size_t r1 = 6 * static_cast<size_t>(ngroups) + 3 * static_cast<size_t>(k) + 64;
+// word per lane, victim lists (after the rest, or over it in wide launches).
+static size_t bitmap_r1_ints(int k, int ngroups, bool wide) {
+    const size_t base = 6 * static_cast<size_t>(ngroups) + static_cast<size_t>(k) + 64;
+    const size_t r1 = wide ? std::max(base, 2 * static_cast<size_t>(k)) : base + 2 * static_cast<size_t>(k);
     return (r1 + 3) & ~static_cast<size_t>(3);
 }
 
 size_t bitmap_lds_bytes(int k, int64_t L_ctx, bool wide) {
     const int ng = static_cast<int>((L_ctx + 127) >> 7);
-    (void)wide;
-    return sizeof(int) * (bitmap_r1_ints(k, ng) + kHistBins + kMiscWords);
+    return sizeof(int) * (bitmap_r1_ints(k, ng, wide) + kHistBins + kMiscWords);
 }
 
 int bitmap_lanes(int B, int k, bool wide, int asked) {
@@ -775,7 +799,7 @@ int bitmap_lanes(int B, int k, bool wide, int asked) {
 hipError_t launch_bitmap_resolve(const StateBase& s, const LayerBatch& lb_in, bool wide, bool vec, hipStream_t st) {
     LayerBatch lb = lb_in;
     lb.ngroups = static_cast<int>((s.L_ctx + 127) >> 7);
-    lb.r1_ints = static_cast<int>(bitmap_r1_ints(lb.k, lb.ngroups));
+    lb.r1_ints = static_cast<int>(bitmap_r1_ints(lb.k, lb.ngroups, wide));
     const size_t lds = bitmap_lds_bytes(lb.k, s.L_ctx, wide);
     if (bitmap_lanes(s.B, lb.k, wide, lb.lanes) == 512) {
         return wide ? launch_s<512, true>(s, lb, lds, vec, st) : launch_s<512, false>(s, lb, lds, vec, st);
