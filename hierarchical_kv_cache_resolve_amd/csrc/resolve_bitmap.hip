@@ -136,6 +136,10 @@ __device__ inline void bitmap_ranks(const unsigned* bits, const uint16_t* wrank,
         w[i] = bits[p[i] >> 5];
         base[i] = wrank[p[i] >> 5];
     }
+    // (the empty asm uses every read unconditionally, so no read is moved
+    // into a branch of its own that would wait for it on the spot)
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(w[i]), "+v"(base[i]));
     isset = 0;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -260,8 +264,8 @@ __device__ inline void radix_select(int* hist, int* misc, const uint32_t (&tsv)[
 // keeps them in the misc block (no long-lived scalar registers) and writes
 // them out at the end.  Slots in program order: 0 start, 1 reads issued and
 // LDS cleared, 2 selection inserted, 3 ranks and hit test, 4 threshold, 5 slot
-// by rank and victim counts, 6 selection side and victim lists, 9 metadata
-// written, 10 end (7 and 8 unused).
+// by rank and victim counts, 7 selection side looked up, 8 hits published,
+// 6 victim lists, 9 metadata written, 10 end.
 #define HB_PHASE(i)                                                                      \
     do {                                                                                 \
         if (lb.trace && tid == 0)                                                        \
@@ -327,9 +331,9 @@ __device__ inline void copy_misses(const StateBase& s, const int* mpos, const in
 // LDS layout (ints): region 1 -- bitmap [4*NG words as NG 16-byte groups],
 // 16-bit rank of each word [4*NG halves], slot by rank [k] with a spare word
 // per lane [64], then victim slot by victim rank [k] and evicted position by
-// victim rank [k] (wide launches: the two victim lists start at word 0 and
-// overlay the rest of region 1) -- then the histogram [kHistBins] and the
-// misc block [kMiscWords].
+// victim rank [k], each with a spare word per lane [64] (wide launches: the
+// two victim lists start at word 0 and overlay the rest of region 1) -- then
+// the histogram [kHistBins] and the misc block [kMiscWords].
 //
 // Template parameters: NT lanes a unit; SPL selections and PER slots a lane
 // (contiguous runs j0 = tid*SPL, s0 = tid*PER); VEC: k and B multiples of 4
@@ -370,7 +374,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     // the slot by rank once every wave is done reading those (one more
     // barrier, only in units with misses), so four units fit a CU's LDS
     int* const vlist = WIDE ? lds : byrank + k + 64;
-    int* const vold = vlist + k;
+    int* const vold = vlist + k + 64;  // (each list has a spare word per lane)
     int* const hist = lds + lb.r1_ints;
     int* const misc = hist + kHistBins;
     if (lb.trace && tid == 0) {
@@ -611,12 +615,15 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
 #pragma unroll
         for (int q = 0; q < SPL; ++q) v[q] = byrank[rk[q]];
 #pragma unroll
+        for (int q = 0; q < SPL; ++q) asm volatile("" : "+v"(v[q]));
+#pragma unroll
         for (int q = 0; q < SPL; ++q) {
             const bool live = (insel >> q) & 1u;
             slv[q] = live ? v[q] : kEmpty;
             mf |= static_cast<unsigned>(live && v[q] < 0) << q;
         }
     }
+    HB_PHASE(7);
     {
         constexpr int W = SPL < 4 ? SPL : 4;
         constexpr unsigned PM = (1u << W) - 1u;
@@ -653,6 +660,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
             }
         }
     }
+    HB_PHASE(8);
     if (m == 0) {
         // every selection hit: the hit stamps are written, nothing else changes
         if (tid == 0) finish_unit(s, clock_u, mc_u, rl, t, k, 0);
@@ -679,13 +687,19 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
             const int rank = st ? sb + min(tb, need_eq) : ((ti && tb < need_eq) ? sb + tb : -1);
             sb += st ? 1 : 0;
             tb += ti ? 1 : 0;
-            if (rank >= 0 && rank < m) {
-                vlist[rank] = s0 + q;
-                vold[rank] = spos[q];
-                if (spos[q] >= 0) pt[spos[q]] = -1;
-                if constexpr (WIDE) ts_g[s0 + q] = ts_miss;  // (the stamp run is not kept live this far)
-                vbits |= 1u << q;
-            }
+            const bool victim = rank >= 0 && rank < m;
+            // (straight-line: a slot that is not a victim writes its lane's
+            // spare words past the lists instead)
+            const int at = victim ? rank : k + lane;
+            vlist[at] = s0 + q;
+            vold[at] = spos[q];
+            vbits |= static_cast<unsigned>(victim) << q;
+        }
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            if (((vbits >> q) & 1u) && spos[q] >= 0) pt[spos[q]] = -1;
+            if constexpr (WIDE)
+                if ((vbits >> q) & 1u) ts_g[s0 + q] = ts_miss;  // (the stamp run is not kept live this far)
         }
         if (!WIDE && vbits) {
             uint32_t tsn[PER];
@@ -778,7 +792,8 @@ hipError_t launch_s(const StateBase& s, const LayerBatch& lb, size_t lds, bool v
 // word per lane, victim lists (after the rest, or over it in wide launches).
 static size_t bitmap_r1_ints(int k, int ngroups, bool wide) {
     const size_t base = 6 * static_cast<size_t>(ngroups) + static_cast<size_t>(k) + 64;
-    const size_t r1 = wide ? std::max(base, 2 * static_cast<size_t>(k)) : base + 2 * static_cast<size_t>(k);
+    const size_t lists = 2 * (static_cast<size_t>(k) + 64);
+    const size_t r1 = wide ? std::max(base, lists) : base + lists;
     return (r1 + 3) & ~static_cast<size_t>(3);
 }
 

@@ -433,7 +433,7 @@ def test_instrumentation_changes_nothing(hs):
     dev = torch.device("cuda:0")
     sel = torch.from_numpy(tr).to(dev)
     out = torch.empty((w.num_req, w.k), dtype=torch.int32, device=dev)
-    order = list(range(11))   # the bitmap kernel's phases in program order
+    order = [0, 1, 2, 3, 4, 5, 7, 8, 6, 9, 10]   # the bitmap kernel's stamp slots in program order
     for t in range(w.steps):
         for l in range(w.num_layers):
             res.resolve(l, sel[t, l], out)
