@@ -75,6 +75,9 @@ def parse():
                     help="how the metadata kernel finds hits (default: the library's)")
     ap.add_argument("--meta-lanes", type=int, default=0, choices=[0, 512, 1024],
                     help="lanes a (request, layer) of the metadata kernel (0: the library's choice)")
+    ap.add_argument("--meta-wgs", type=int, default=None,
+                    help="workgroups per (request, layer) that plan alike and copy their misses (0: a separate "
+                         "fetch launch, -1: by launch size; default: the library's)")
     ap.add_argument("--fetch-blocks", type=int, default=0)
     ap.add_argument("--unroll", type=int, default=0)
     ap.add_argument("--coherent", action="store_true")
@@ -142,6 +145,8 @@ def main():
         res.set_option(hs.HS_OPT_FETCH_BLOCKS, args.fetch_blocks)
     if args.meta_lanes:
         res.set_option(hs.HS_OPT_META_LANES, args.meta_lanes)
+    if args.meta_wgs is not None:
+        res.set_option(hs.HS_OPT_META_WGS, args.meta_wgs)
     if args.unroll:
         res.set_option(hs.HS_OPT_FETCH_UNROLL, args.unroll)
     sel = torch.from_numpy(tr).to(dev)
@@ -283,8 +288,12 @@ def main():
                                 "published_pcie5_x16": PCIE5_X16_GBPS}
     result["miss_fetch_frac_of_link_peak"] = result["miss_fetch_GBps"] / link_peak if link_sdma else None
 
-    if tim is not None and tim.fetch_launches:
-        fetch_avg_ms = tim.fetch_ms / tim.fetch_launches
+    if tim is not None and (tim.fetch_launches or tim.plan_launches):
+        # units split over several workgroups copy their misses inside the
+        # metadata launch: then that launch is the copying kernel
+        split = tim.fetch_launches == 0
+        copy_ms, copy_launches = (tim.plan_ms, tim.plan_launches) if split else (tim.fetch_ms, tim.fetch_launches)
+        fetch_avg_ms = copy_ms / copy_launches
         plan_avg_ms = tim.plan_ms / tim.plan_launches
         # algorithmic bytes of the fetch kernel: every missed record crosses the
         # host link once (and is written once to HBM).  With prefetch, the main
@@ -295,9 +304,11 @@ def main():
                               if r0l is not None)
         else:
             fetch_bytes = miss_bytes
-        achieved = fetch_bytes / (tim.fetch_ms * 1e-3) / 1e9
+        achieved = fetch_bytes / (copy_ms * 1e-3) / 1e9
         result["roofline"] = {
-            "kernel": "fetch_kernel (host-mapped 16 B loads -> HBM cache rows)",
+            "kernel": ("bitmap_resolve_kernel (units split over workgroups: plan and host-mapped 16 B loads -> HBM "
+                       "cache rows in one launch)" if split else
+                       "fetch_kernel (host-mapped 16 B loads -> HBM cache rows)"),
             "bound": "host_link",
             "achieved": achieved,
             "peak": link_peak,
@@ -306,12 +317,12 @@ def main():
             "frac_published": achieved / PCIE5_X16_GBPS,
             # HBM + link bytes of the workload's fetch launches from its committed counter summary
             # (None if there is none, or if the kernel source changed since it was taken)
-            "traffic": (fetch_traffic(w.name) or {}).get("total_bytes"),
-            "traffic_detail": fetch_traffic(w.name),
+            "traffic": None if split else (fetch_traffic(w.name) or {}).get("total_bytes"),
+            "traffic_detail": None if split else fetch_traffic(w.name),
             "peak_note": "peak = max(SDMA H2D copy, 16 B-load streaming kernel) measured in this run; "
                          f"frac_published against PCIe 5.0 x16 = {PCIE5_X16_GBPS} GB/s per direction",
             "avg_launch_ms": fetch_avg_ms,
-            "bytes_per_launch": fetch_bytes / tim.fetch_launches,
+            "bytes_per_launch": fetch_bytes / copy_launches,
         }
         if tim.replay_launches:
             result["kernels_replay"] = {"replay_avg_ms": tim.replay_ms / tim.replay_launches,
@@ -319,13 +330,15 @@ def main():
                                         "publish_avg_ms": tim.publish_ms / max(1, tim.publish_launches),
                                         "replay_GBps": (miss_bytes - fetch_bytes) / (tim.replay_ms * 1e-3) / 1e9}
         result["kernels"] = {
-            "fetch_avg_ms": fetch_avg_ms, "fetch_launches": tim.fetch_launches,
+            "split_units": split,
+            "fetch_avg_ms": fetch_avg_ms if not split else None, "fetch_launches": tim.fetch_launches,
             "plan_avg_ms": plan_avg_ms, "plan_launches": tim.plan_launches,
             "plan_share_of_step": tim.plan_ms / (elapsed * 1e3),
-            "fetch_share_of_step": tim.fetch_ms / (elapsed * 1e3),
+            "fetch_share_of_step": copy_ms / (elapsed * 1e3),
             "timing_dropped": tim.dropped,
         }
-        log(f"fetch avg {fetch_avg_ms * 1e3:.1f} us ({achieved:.1f} GB/s), plan avg {plan_avg_ms * 1e3:.1f} us")
+        log(f"{'split resolve' if split else 'fetch'} avg {fetch_avg_ms * 1e3:.1f} us ({achieved:.1f} GB/s), "
+            f"plan avg {plan_avg_ms * 1e3:.1f} us")
 
     if not args.no_attention_leg and mla_records:
         result["attention"] = attention_leg(hs, torch, res, w, out, args.heads, dev, hbm_peak,
@@ -341,7 +354,7 @@ def main():
 
     if not args.no_hit_only:
         result["hit_only"] = hit_only_leg(hs, tg, torch, tg.WORKLOADS[args.hit_only_workload], dev, sptr, hbm_peak,
-                                          meta_lanes=args.meta_lanes)
+                                          meta_lanes=args.meta_lanes, meta_wgs=args.meta_wgs)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(tg, w, tr, pool, W, args.cpu_seconds)
@@ -457,7 +470,7 @@ def attention_leg(hs, torch, res, w, out, heads, dev, hbm_peak, iters=20, heads_
             "algorithmic_bytes": io_bytes, "flops": flops}
 
 
-def hit_only_leg(hs, tg, torch, w, dev, sptr, hbm_peak, steps=64, meta_lanes=0):
+def hit_only_leg(hs, tg, torch, w, dev, sptr, hbm_peak, steps=64, meta_lanes=0, meta_wgs=None):
     """Metadata path alone: every step after the first repeats it, so every
     selection hits and nothing crosses the host link.  Timed as captured HIP
     graphs (one per variant) so that host launch cost does not enter.  Only
@@ -472,6 +485,8 @@ def hit_only_leg(hs, tg, torch, w, dev, sptr, hbm_peak, steps=64, meta_lanes=0):
     out = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
     if meta_lanes:
         res.set_option(hs.HS_OPT_META_LANES, meta_lanes)
+    if meta_wgs is not None:
+        res.set_option(hs.HS_OPT_META_WGS, meta_wgs)
     for l in range(w.num_layers):
         res.resolve(l, tr[0, l], out[l], sptr)
     # algorithmic bytes per (request, layer) of an all-hit resolve with the
@@ -523,8 +538,28 @@ def hit_only_leg(hs, tg, torch, w, dev, sptr, hbm_peak, steps=64, meta_lanes=0):
     torch.cuda.synchronize()
     batched_pt = time.perf_counter() - t0
     res.set_option(hs.HS_OPT_PROBE, hs.HS_PROBE_SLOT_SCAN)
+    # the per-layer launches with each (request, layer) split over several
+    # workgroups that plan it alike and would copy its misses themselves: one
+    # launch a layer (the default keeps the fetch launch at shapes whose
+    # misses could reach tens of MB)
+    split_g = max(1, min(32, -(-256 // w.num_req)))
+    res.set_option(hs.HS_OPT_META_WGS, split_g)
+    g4 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g4):
+        cap = torch.cuda.current_stream().cuda_stream
+        for _ in range(steps):
+            for l in layers:
+                res.resolve(l, tr[1, l], out[l], cap)
+    torch.cuda.synchronize()
+    g4.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g4.replay()
+    torch.cuda.synchronize()
+    per_layer_split = time.perf_counter() - t0
+    res.set_option(hs.HS_OPT_META_WGS, -1 if meta_wgs is None else meta_wgs)
     st = res.stats()
-    del g1, g2, g3
+    del g1, g2, g3, g4
     res.close()
     pool.free()
     total = per_rl * w.num_req * w.num_layers * steps
@@ -535,6 +570,8 @@ def hit_only_leg(hs, tg, torch, w, dev, sptr, hbm_peak, steps=64, meta_lanes=0):
         "bytes_per_request_layer_page_table_probe": per_rl_pt,
         "per_layer_launch_GBps": total / per_layer / 1e9,
         "per_layer_resolve_us": per_layer / (steps * w.num_layers) * 1e6,
+        "per_layer_split_resolve_us": per_layer_split / (steps * w.num_layers) * 1e6,
+        "per_layer_split_wgs": split_g,
         "batched_all_layers_GBps": total / batched / 1e9,
         "batched_step_us": batched / steps * 1e6,
         "batched_page_table_GBps": total_pt / batched_pt / 1e9,
@@ -547,9 +584,11 @@ def hit_only_leg(hs, tg, torch, w, dev, sptr, hbm_peak, steps=64, meta_lanes=0):
     }
     if hbm_peak:
         r["per_layer_frac_of_hbm_peak"] = r["per_layer_launch_GBps"] / hbm_peak
+        r["per_layer_split_frac_of_hbm_peak"] = total / per_layer_split / 1e9 / hbm_peak
         r["batched_frac_of_hbm_peak"] = r["batched_all_layers_GBps"] / hbm_peak
         r["batched_page_table_frac_of_hbm_peak"] = r["batched_page_table_GBps"] / hbm_peak
-    log(f"hit-only: per-layer {r['per_layer_resolve_us']:.1f} us/resolve ({r['per_layer_launch_GBps']:.1f} GB/s), "
+    log(f"hit-only: per-layer {r['per_layer_resolve_us']:.1f} us/resolve ({r['per_layer_launch_GBps']:.1f} GB/s; "
+        f"split units {r['per_layer_split_resolve_us']:.1f} us), "
         f"batched {r['batched_step_us']:.1f} us/step ({r['batched_all_layers_GBps']:.1f} GB/s), "
         f"batched page-table probe {r['batched_page_table_step_us']:.1f} us/step "
         f"({r['batched_page_table_GBps']:.1f} GB/s)")
@@ -720,9 +759,13 @@ def sweep(hs, tg, torch, dev, sptr, skip, link_peak, steps, nthreads, heads=128)
         res.check_error()
         miss_bytes = s1.miss_bytes - s0.miss_bytes
         sels = steps * w.num_layers * w.num_req * w.k
-        fetch_gbps = (r1.miss_bytes - r0.miss_bytes) / (tim.fetch_ms * 1e-3) / 1e9 if tim.fetch_ms else None
+        split = tim.fetch_launches == 0
+        copy_ms = tim.plan_ms if split else tim.fetch_ms
+        fetch_gbps = (r1.miss_bytes - r0.miss_bytes) / (copy_ms * 1e-3) / 1e9 if copy_ms else None
         row = {"selections_per_s": sels / dt, "ms_per_step": dt * 1e3 / steps,
                "miss_rate": (s1.misses - s0.misses) / sels, "miss_fetch_GBps": miss_bytes / dt / 1e9,
+               "split_units": split,
+               "copy_kernel": "bitmap_resolve_kernel (split units)" if split else "fetch_kernel",
                "fetch_kernel_GBps": fetch_gbps, "plan_avg_us": tim.plan_ms * 1e3 / max(1, tim.plan_launches),
                "fetch_avg_us": tim.fetch_ms * 1e3 / max(1, tim.fetch_launches),
                "pool_GB": round(pool.nbytes / 1e9, 2), "logical_pool_GB": round(w.logical_rows * w.row_bytes / 1e9, 1)}
@@ -733,7 +776,7 @@ def sweep(hs, tg, torch, dev, sptr, skip, link_peak, steps, nthreads, heads=128)
             row["prefetch"] = prefetch_leg(hs, torch, res, w, tr, out, dev, sptr, warm, steps, heads)
         rows[name] = row
         log(f"sweep {name}: {row['selections_per_s'] / 1e6:.1f} M sel/s, {row['ms_per_step']:.3f} ms/step, "
-            f"miss {row['miss_fetch_GBps']:.1f} GB/s, fetch kernel "
+            f"miss {row['miss_fetch_GBps']:.1f} GB/s, copy kernel "
             f"{fetch_gbps if fetch_gbps else 0:.1f} GB/s, plan {row['plan_avg_us']:.1f} us")
         res.close()
         pool.free()

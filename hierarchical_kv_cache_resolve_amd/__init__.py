@@ -28,6 +28,7 @@ ELEM_BYTES = {BF16: 2, FP16: 2, FP8: 1, FP32: 4}
 HS_OPT_FETCH_BLOCKS, HS_OPT_FETCH_UNROLL, HS_OPT_TIMING, HS_OPT_NT_LOADS, HS_OPT_PHASE_TRACE, HS_OPT_PROBE = 1, 2, 3, 4, 5, 6
 HS_OPT_ATTN_HEADS = 7
 HS_OPT_META_LANES = 8
+HS_OPT_META_WGS, HS_MAX_META_WGS = 9, 64
 HS_PROBE_PAGE_TABLE, HS_PROBE_SLOT_SCAN, HS_PROBE_SLOT_SCAN_HASH = 0, 1, 2
 
 _ERR_NAMES = {v: k for k, v in dict(HS_E_INVAL=-1, HS_E_HANDLE=-2, HS_E_LAYER=-3, HS_E_K=-4, HS_E_ALIGN=-5,

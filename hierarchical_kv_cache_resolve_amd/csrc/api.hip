@@ -33,12 +33,14 @@ struct hisparse_ctx {
     int probe = HS_PROBE_SLOT_SCAN;
     int attn_heads = 0;  // heads per attention workgroup: 0 = by shape, 32 or 64
     int meta_lanes = 0;  // lanes a unit of the bitmap metadata kernel: 0 = by launch size, 512 or 1024
+    int meta_wgs = -1;   // workgroups a unit that copies its own misses: -1 = by launch size, 0 = never, G
     float* attn_ws = nullptr;       // consumer workspace (partials per chunk)
     size_t attn_ws_floats = 0;
     // ordering of resolve / prefetch (host-side bookkeeping only)
     std::vector<hipEvent_t> ev_plan, ev_join;
     std::vector<int> pending_anchor;   // shared layer -> anchor whose replay it must publish, or -1
     std::vector<char> join_outstanding;
+    std::vector<char> anchor;  // the layer's plan has been replayed into shared layers
     std::vector<char> plan_in_capture, join_in_capture;  // event recorded while its stream was capturing
     std::vector<char> last_was_plan;
     std::vector<int64_t> steps;
@@ -120,7 +122,7 @@ int hash_bits_for(int k) {
 void free_all(hisparse_ctx* h) {
     hs::StateBase& s = h->s;
     void* ptrs[] = {s.cache, s.slot_pos, s.ts, s.page_table, s.clock, s.plan, s.miss_count,
-                    s.hit_mask, s.status, s.err, s.stats, s.phase, s.length, h->d_region_row};
+                    s.hit_mask, s.status, s.err, s.stats, s.phase, s.length, s.arrive, h->d_region_row};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     for (hipEvent_t e : h->ev_plan)
@@ -156,6 +158,7 @@ int init_state(hisparse_ctx* h, hipStream_t st) {
     HS_TRY(hipMemsetAsync(s.status, 0, nrl * sizeof(int32_t), st));
     HS_TRY(hipMemsetAsync(s.err, 0, 4 * sizeof(int32_t), st));
     HS_TRY(hipMemsetAsync(s.stats, 0, nrl * 4 * sizeof(unsigned long long), st));
+    HS_TRY(hipMemsetAsync(s.arrive, 0, nrl * sizeof(uint32_t), st));
     HS_TRY(hipStreamSynchronize(st));
     std::fill(h->pending_anchor.begin(), h->pending_anchor.end(), -1);
     std::fill(h->join_outstanding.begin(), h->join_outstanding.end(), 0);
@@ -304,6 +307,7 @@ int hisparse_create(int num_req, int num_layers, int B, int W_KV, int dtype, con
     HS_ALLOC(err, int32_t, 4)
     HS_ALLOC(stats, unsigned long long, static_cast<size_t>(nrl) * 4)
     HS_ALLOC(length, int32_t, static_cast<size_t>(nrl))
+    HS_ALLOC(arrive, uint32_t, static_cast<size_t>(nrl))
 #undef HS_ALLOC
     if ((rc = alloc_dev(&p, sizeof(int64_t) * static_cast<size_t>(nrl))) != HS_OK) {
         free_all(h);
@@ -330,6 +334,7 @@ int hisparse_create(int num_req, int num_layers, int B, int W_KV, int dtype, con
     }
     h->pending_anchor.assign(num_layers, -1);
     h->join_outstanding.assign(num_layers, 0);
+    h->anchor.assign(num_layers, 0);
     h->plan_in_capture.assign(num_layers, 0);
     h->join_in_capture.assign(num_layers, 0);
     h->last_was_plan.assign(num_layers, 0);
@@ -400,6 +405,12 @@ static int resolve_plan_path(hisparse_t h, int n, const int* layers, const int32
         lb.layer[i] = l;
         fb.layer[i] = l;
     }
+    // An anchor keeps one workgroup per unit and the fetch launch: its plan is
+    // then ready for the shared layers' replay before its own rows are
+    // copied, instead of after (a split launch copies inside the launch).
+    bool any_anchor = false;
+    for (int i = 0; i < n; ++i) any_anchor = any_anchor || h->anchor[layers[i]];
+    lb.wgs = any_anchor ? 0 : hs::plan_wgs(h->s, lb, h->meta_wgs);
     int rc = timed(h, K_PLAN, st, [&] { return hs::launch_plan(h->s, lb, st); });
     if (rc != HS_OK) return rc;
     const bool cap = capturing(st);
@@ -407,7 +418,7 @@ static int resolve_plan_path(hisparse_t h, int n, const int* layers, const int32
         HS_TRY(hipEventRecord(h->ev_plan[layers[i]], st));
         h->plan_in_capture[layers[i]] = cap;
     }
-    if (!hs::plan_copies_misses(h->s, n)) {
+    if (!hs::plan_copies_misses(h->s, lb)) {
         rc = timed(h, K_FETCH, st, [&] { return hs::launch_fetch(h->s, fb, h->fetch_blocks, h->unroll, h->nt, st); });
         if (rc != HS_OK) return rc;
     }
@@ -506,6 +517,7 @@ int hisparse_prefetch(hisparse_t h, int anchor, const int* shared, int n, void* 
     HS_TRY(hipEventRecord(h->ev_join[anchor], side));
     h->join_in_capture[anchor] = capturing(side);
     h->join_outstanding[anchor] = 1;
+    h->anchor[anchor] = 1;
     for (int i = 0; i < n; ++i) h->pending_anchor[shared[i]] = anchor;
     return HS_OK;
 }
@@ -564,7 +576,7 @@ size_t hisparse_meta_bytes(hisparse_t h) {
     const size_t nrl = static_cast<size_t>(h->R) * h->NL;
     return nrl * h->B * (sizeof(int32_t) + sizeof(uint32_t) + sizeof(int4) + 1) +
            nrl * static_cast<size_t>(h->L_ctx) * sizeof(int32_t) +
-           nrl * (4 * sizeof(int32_t) + sizeof(int64_t)) +  // clock, miss count, status, length; region row
+           nrl * (5 * sizeof(int32_t) + sizeof(int64_t)) +  // clock, miss count, status, length, arrival; region row
            nrl * 4 * sizeof(unsigned long long) + 4 * sizeof(int32_t);  // counters; error word
 }
 
@@ -660,6 +672,10 @@ int hisparse_set_option(hisparse_t h, int key, int64_t value) {
         case HS_OPT_META_LANES:
             if (value != 0 && value != 512 && value != 1024) return HS_E_INVAL;
             h->meta_lanes = static_cast<int>(value);
+            return HS_OK;
+        case HS_OPT_META_WGS:
+            if (value < -1 || value > HS_MAX_META_WGS) return HS_E_INVAL;
+            h->meta_wgs = static_cast<int>(value);
             return HS_OK;
         case HS_OPT_PHASE_TRACE:
             if (value && !h->s.phase) {

@@ -48,6 +48,7 @@ struct StateBase {
     unsigned long long* phase;      // [layer][req][kPhaseSlots] wall-clock stamps, or null (off)
     uint8_t* pool;                  // device-visible pointer to the host pool
     int32_t* length;                // [layer][req] positions written so far in each history
+    uint32_t* arrive;               // [layer][req] workgroups of a split unit done (0 between launches)
     const int64_t* region_row;      // [req * num_layers + layer]
     int64_t L_ctx;
     int64_t row_bytes;
@@ -70,6 +71,8 @@ struct LayerBatch {
     int copy;     // the metadata kernel copies the misses itself (set by launch_plan)
     int trace;    // phase stamps on (s.phase is set)
     int lanes;    // bitmap kernel: lanes a unit asked for (0: by launch size)
+    int wgs;      // bitmap kernel: workgroups a unit (0: one, with a fetch launch after it; G >= 1:
+                  // G workgroups plan it alike and copy its misses between them, set by plan_wgs)
 };
 
 struct FetchBatch {
@@ -93,9 +96,13 @@ size_t bitmap_lds_bytes(int k, int64_t L_ctx, bool wide);
 int bitmap_lanes(int B, int k, bool wide, int asked);
 hipError_t launch_bitmap_resolve(const StateBase& s, const LayerBatch& lb, bool wide, bool vec, hipStream_t st);
 hipError_t launch_trim(const StateBase& s, hipStream_t st);
-// Whether a metadata launch over n layers copies its own misses (a wide
-// launch: no fetch launch follows it).
-bool plan_copies_misses(const StateBase& s, int n);
+// Workgroups a unit of a metadata launch takes when it copies its own misses
+// between several workgroups (0: it does not; a fetch launch follows).
+// `asked`: -1 by launch size, 0 never, G >= 1 that many.
+int plan_wgs(const StateBase& s, const LayerBatch& lb, int asked);
+// Whether a metadata launch copies its own misses (a wide launch, or one
+// whose units take several workgroups: no fetch launch follows it).
+bool plan_copies_misses(const StateBase& s, const LayerBatch& lb);
 hipError_t launch_publish(const StateBase& s, const LayerBatch& lb, hipStream_t st);
 hipError_t launch_fetch(const StateBase& s, const FetchBatch& fb, int blocks, int unroll, bool nt, hipStream_t st);
 hipError_t launch_replay_meta(const StateBase& s, const ReplayBatch& rb, hipStream_t st);

@@ -21,6 +21,7 @@
 // over the stamps (10-bit digits relative to the minimum candidate stamp) and
 // one block-wide prefix scan that counts strictly-older slots and tied slots
 // together, so the result does not depend on wave scheduling.
+#include <algorithm>
 #include <climits>
 
 #include "hs_device.h"
@@ -883,24 +884,49 @@ static bool plan_is_wide(const StateBase& s, int n) {
     return static_cast<int64_t>(s.R) * n > 256;
 }
 
-bool plan_copies_misses(const StateBase& s, int n) {
-    // (rows up to 8 MB keep the copy's piece index inside 32 bits)
-    return plan_is_wide(s, n) && s.row_bytes <= (static_cast<int64_t>(1) << 23);
+// Runs of the bitmap kernel move as 16-byte vectors when k and B are
+// multiples of 4 and the caller's selection and output arrays are aligned.
+static bool bitmap_vec(const StateBase& s, const LayerBatch& lb) {
+    bool vec = (lb.k & 3) == 0 && (s.B & 3) == 0;
+    for (int i = 0; i < lb.n && vec; ++i)
+        vec = (reinterpret_cast<uintptr_t>(lb.sel[i]) & 15u) == 0 && (reinterpret_cast<uintptr_t>(lb.out[i]) & 15u) == 0;
+    return vec;
+}
+
+int plan_wgs(const StateBase& s, const LayerBatch& lb, int asked) {
+    if (asked == 0 || lb.probe != HS_PROBE_SLOT_SCAN || plan_is_wide(s, lb.n)) return 0;
+    if (bitmap_lds_bytes(lb.k, s.L_ctx, false) > 160 * 1024) return 0;
+    if (bitmap_lanes(s.B, lb.k, false, lb.lanes) != 1024 || !bitmap_vec(s, lb)) return 0;
+    if (s.row_bytes > (static_cast<int64_t>(1) << 20)) return 0;  // (piece indices stay inside 32 bits)
+    if (asked > 0) return asked;
+    // by launch size.  A split unit copies only its own misses, so the units
+    // with the most misses set the end of the launch, where the fetch kernel
+    // spreads all of a launch's misses evenly over the chip: measured, the
+    // split launch saves about 2 us a layer where a layer's misses are a few
+    // MB (16 requests of 1152-byte records: 0.796 against 0.810 ms a step of
+    // 8 layers) and loses 2 % where they are tens of MB (64 requests of 4 KB
+    // records).  Split only launches whose misses cannot exceed 64 MB, into
+    // about 256 workgroups so the copy spreads over the chip.
+    const int units = s.R * lb.n;
+    if (static_cast<int64_t>(units) * lb.k * s.row_bytes > (static_cast<int64_t>(64) << 20)) return 0;
+    return std::min(32, (256 + units - 1) / units);
+}
+
+bool plan_copies_misses(const StateBase& s, const LayerBatch& lb) {
+    // (rows up to 8 MB keep the wide copy's piece index inside 32 bits)
+    return lb.wgs > 0 || (plan_is_wide(s, lb.n) && s.row_bytes <= (static_cast<int64_t>(1) << 23));
 }
 
 hipError_t launch_plan(const StateBase& s, const LayerBatch& lb_in, hipStream_t st) {
     LayerBatch lb = lb_in;
     const bool wide = plan_is_wide(s, lb.n);
-    lb.copy = plan_copies_misses(s, lb.n) ? 1 : 0;
+    lb.copy = plan_copies_misses(s, lb) ? 1 : 0;
     lb.trace = s.phase != nullptr ? 1 : 0;
     if (lb.probe == HS_PROBE_SLOT_SCAN && bitmap_lds_bytes(lb.k, s.L_ctx, wide) <= 160 * 1024) {
         // the default: a bitmap over the history's positions, whenever it
         // fits the LDS of one CU.  Runs move as 16-byte vectors when k and B
         // are multiples of 4 and the caller's arrays are 16-byte aligned.
-        bool vec = (lb.k & 3) == 0 && (s.B & 3) == 0;
-        for (int i = 0; i < lb.n && vec; ++i)
-            vec = (reinterpret_cast<uintptr_t>(lb.sel[i]) & 15u) == 0 && (reinterpret_cast<uintptr_t>(lb.out[i]) & 15u) == 0;
-        return launch_bitmap_resolve(s, lb, wide, vec, st);
+        return launch_bitmap_resolve(s, lb, wide, bitmap_vec(s, lb), st);
     }
     const int H = 1 << lb.hash_bits;
     const int probe = lb.probe == HS_PROBE_PAGE_TABLE ? PROBE_TABLE : PROBE_HASH;

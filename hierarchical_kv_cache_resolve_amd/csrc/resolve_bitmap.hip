@@ -41,6 +41,7 @@ enum : int {
     X_RANK = 2,     // first group rank not yet handed to a wave
     X_BIN = 3,      // radix select: crossing bin of the current pass
     X_BELOW = 4,    // radix select: candidates below it
+    X_LAST = 5,     // split unit: this workgroup arrived last
     X_MISS = 16,    // [16] per-wave inclusive miss counts
     X_VICT = 32,    // [16] per-wave packed (strict | tie << 16) victim counts
     X_HIST = 48,    // [16] radix-scan partials
@@ -268,12 +269,12 @@ __device__ inline void radix_select(int* hist, int* misc, const uint32_t (&tsv)[
 // 6 victim lists, 9 metadata written, 10 end.
 #define HB_PHASE(i)                                                                      \
     do {                                                                                 \
-        if (lb.trace && tid == 0)                                                        \
+        if (lb.trace && tid == 0 && lead)                                                \
             reinterpret_cast<unsigned long long*>(misc + X_STAMP)[(i)] = wall_clock64(); \
     } while (0)
 #define HB_PHASE_FLUSH()                                                                                 \
     do {                                                                                                 \
-        if (lb.trace && tid == 0) {                                                                      \
+        if (lb.trace && tid == 0 && lead) {                                                              \
             const unsigned long long* st_ = reinterpret_cast<const unsigned long long*>(misc + X_STAMP); \
             for (int i_ = 0; i_ < 11; ++i_) s.phase[rl * kPhaseSlots + i_] = st_[i_];                    \
         }                                                                                                \
@@ -296,26 +297,25 @@ __device__ inline void finish_unit(const StateBase& s, uint32_t* clock_u, int32_
     atomicAdd(st + 3, 1ull);
 }
 
-// Copy the m missed rows of one (request, layer) from the host pool into
-// their victim slots (launches over many request-layers, where no separate
-// fetch launch follows): miss i reads position mpos[i] into slot msl[i].
-// Same flat (row, 16-byte piece) order and 16-byte loads as the fetch kernel.
-template <int NT, bool NTL>
+// Copy missed rows of one (request, layer) from the host pool into their
+// victim slots (launches where no separate fetch launch follows): miss i
+// reads position mpos[i] into slot msl[i].  The pieces [c_begin, c_end) of the
+// flat (row, 16-byte piece) space of the unit's misses are copied, in the
+// fetch kernel's order and with its 16-byte loads, U pieces a lane a round.
+template <int NT, bool NTL, int U>
 __device__ inline void copy_misses(const StateBase& s, const int* mpos, const int* msl, int64_t rl, int r, int layer,
-                                   int m) {
-    constexpr int U = 4;
+                                   int c_begin, int c_end) {
     const int row16 = static_cast<int>(s.row_bytes >> 4);
-    const int total = m * row16;
     const uint8_t* src_base = s.pool + s.region_row[static_cast<int64_t>(r) * s.NL + layer] * s.row_bytes;
     uint8_t* dst_base = s.cache + rl * s.B * s.row_bytes;
-    for (int c0 = threadIdx.x; c0 < total; c0 += NT * U) {
+    for (int c0 = c_begin + static_cast<int>(threadIdx.x); c0 < c_end; c0 += NT * U) {
         u32x4 v[U];
         u32x4* dst[U];
 #pragma unroll
         for (int x = 0; x < U; ++x) {
             const int c = c0 + x * NT;
             dst[x] = nullptr;
-            if (c < total) {
+            if (c < c_end) {
                 const int i = c / row16, off = c - i * row16;
                 const u32x4* src = reinterpret_cast<const u32x4*>(src_base + static_cast<int64_t>(mpos[i]) * s.row_bytes) + off;
                 dst[x] = reinterpret_cast<u32x4*>(dst_base + static_cast<int64_t>(msl[i]) * s.row_bytes) + off;
@@ -338,8 +338,16 @@ __device__ inline void copy_misses(const StateBase& s, const int* mpos, const in
 // Template parameters: NT lanes a unit; SPL selections and PER slots a lane
 // (contiguous runs j0 = tid*SPL, s0 = tid*PER); VEC: k and B multiples of 4
 // and 16-byte aligned selection / output arrays, so runs move as vectors;
-// WIDE: a launch over many units (held to six waves per SIMD, and it copies
-// its own misses).
+// WIDE: a launch over many units (held to eight waves per SIMD at 512 lanes,
+// and it copies its own misses); SPLIT: each unit takes lb.wgs workgroups,
+// which all plan it alike (the plan is deterministic) and copy its misses
+// between them, so no fetch launch follows.  A split unit's workgroups read
+// the old slot map, stamps and clock; only the last one to finish (a counter
+// per unit, no workgroup ever waits for another) writes the new metadata, so
+// none is overwritten while another workgroup may still read it.  A unit
+// without misses is the exception: the lead workgroup ends it at once, as
+// what it writes (hit stamps, clock) changes nothing the others need when
+// every selection hits.
 //
 // Barriers: B1 LDS cleared; B2 selection inserted; B3 word ranks, hit test of
 // every slot (a bit test, no rank needed), hit count -- so m = k - h is known
@@ -349,14 +357,18 @@ __device__ inline void copy_misses(const StateBase& s, const int* mpos, const in
 // after one more barrier, as the lists overlay the bitmap -- victims listed
 // by rank, B5.  After B5 each missing selection takes the victim of its own
 // rank.
-template <int NT, int SPL, int PER, bool VEC, bool WIDE>
+template <int NT, int SPL, int PER, bool VEC, bool WIDE, bool SPLIT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WIDE ? (NT == 512 ? 8 : 6) : 1)))
 void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     constexpr int NW = NT / 64;
     static_assert(NW <= 16, "per-wave partials fit one row of 16 lanes");
+    static_assert(!(WIDE && SPLIT), "a wide launch has one workgroup a unit");
     extern __shared__ int lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-    const int r = blockIdx.x;
+    const int G = SPLIT ? lb.wgs : 1;
+    const int r = SPLIT ? static_cast<int>(blockIdx.x) / G : static_cast<int>(blockIdx.x);
+    const int g = SPLIT ? static_cast<int>(blockIdx.x) - r * G : 0;
+    const bool lead = g == 0;  // publishes slot_idx and the hit mask, stamps phases
     const int layer = lb.layer[blockIdx.y];
     const int k = lb.k, B = s.B, NG = lb.ngroups;
     const int64_t rl = static_cast<int64_t>(layer) * s.R + r;
@@ -377,7 +389,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     int* const vold = vlist + k + 64;  // (each list has a spare word per lane)
     int* const hist = lds + lb.r1_ints;
     int* const misc = hist + kHistBins;
-    if (lb.trace && tid == 0) {
+    if (lb.trace && tid == 0 && lead) {
         // the stamp words lie outside the part of the misc block cleared below
         unsigned long long* st0 = reinterpret_cast<unsigned long long*>(misc + X_STAMP);
         st0[0] = wall_clock64();
@@ -432,6 +444,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     const int flags = misc[X_FLAGS];
     if (flags) {
         // reject: -1 everywhere, state unchanged
+        if (!lead) return;
         for (int j = tid; j < k; j += NT) {
             out[j] = -1;
             s.hit_mask[rl * B + j] = 0;
@@ -494,7 +507,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         }
     }
     const unsigned candbits = inslot & ~hitbits;  // slots that may be evicted
-    if (hitbits) {
+    if (!SPLIT && hitbits) {
         uint32_t tsn[PER];
 #pragma unroll
         for (int q = 0; q < PER; ++q) tsn[q] = ((hitbits >> q) & 1u) ? ts_hit : tsv[q];
@@ -624,7 +637,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         }
     }
     HB_PHASE(7);
-    {
+    if (lead) {
         constexpr int W = SPL < 4 ? SPL : 4;
         constexpr unsigned PM = (1u << W) - 1u;
         uint8_t* hm = s.hit_mask + rl * B;
@@ -663,6 +676,17 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     HB_PHASE(8);
     if (m == 0) {
         // every selection hit: the hit stamps are written, nothing else changes
+        if constexpr (SPLIT) {
+            // (the other workgroups of the unit find no miss either: the slot
+            // map does not change, and stamps and clock only matter to misses)
+            if (!lead) return;
+            if (hitbits) {
+                uint32_t tsn[PER];
+#pragma unroll
+                for (int q = 0; q < PER; ++q) tsn[q] = ((hitbits >> q) & 1u) ? ts_hit : tsv[q];
+                store_run_masked<PER, VEC, uint32_t>(ts_g, s0, B, tsn, hitbits);
+            }
+        }
         if (tid == 0) finish_unit(s, clock_u, mc_u, rl, t, k, 0);
         HB_PHASE(10);
         HB_PHASE_FLUSH();
@@ -676,11 +700,11 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     const int mincl = wave_incl_scan(mc);
     if (lane == 63) misc[X_MISS + wave] = mincl;
     if constexpr (WIDE) __syncthreads();  // the victim lists overwrite the bitmap
+    unsigned vbits = 0;
     {
         const int vpre = vincl - packed + sum_before(misc + X_VICT, wave);
         int sb = vpre & 0xFFFF, tb = vpre >> 16;
         int32_t* pt = s.page_table + rl * s.L_ctx;
-        unsigned vbits = 0;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
             const bool st = (strict_bits >> q) & 1u, ti = (tie_bits >> q) & 1u;
@@ -695,13 +719,15 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
             vold[at] = spos[q];
             vbits |= static_cast<unsigned>(victim) << q;
         }
+        if constexpr (!SPLIT) {
 #pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            if (((vbits >> q) & 1u) && spos[q] >= 0) pt[spos[q]] = -1;
-            if constexpr (WIDE)
-                if ((vbits >> q) & 1u) ts_g[s0 + q] = ts_miss;  // (the stamp run is not kept live this far)
+            for (int q = 0; q < PER; ++q) {
+                if (((vbits >> q) & 1u) && spos[q] >= 0) pt[spos[q]] = -1;
+                if constexpr (WIDE)
+                    if ((vbits >> q) & 1u) ts_g[s0 + q] = ts_miss;  // (the stamp run is not kept live this far)
+            }
         }
-        if (!WIDE && vbits) {
+        if (!WIDE && !SPLIT && vbits) {
             uint32_t tsn[PER];
 #pragma unroll
             for (int q = 0; q < PER; ++q)
@@ -714,10 +740,11 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
 
     // 6. the i-th miss (ascending selection index) takes the victim of rank i
     // (ascending slot): plan entry, page table, slot map and publication
-    {
+    const int i0 = mincl - mc + sum_before(misc + X_MISS, wave);  // this lane's first miss
+    if constexpr (!SPLIT) {
         int32_t* pt = s.page_table + rl * s.L_ctx;
         int4* plan = s.plan + rl * B;
-        int i = mincl - mc + sum_before(misc + X_MISS, wave);
+        int i = i0;
 #pragma unroll
         for (int q = 0; q < SPL; ++q) {
             if ((mf >> q) & 1u) {
@@ -731,36 +758,117 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
                 ++i;
             }
         }
-    }
-    HB_PHASE(9);
-    if (tid == 0) finish_unit(s, clock_u, mc_u, rl, t, k, m);
-    if constexpr (WIDE) {
-        // a wide launch copies its own misses: with hundreds of workgroups
-        // copying at once the link is as busy as under the chip-wide fetch
-        // kernel, and the launch after it is saved
-        if (lb.copy) {
-            __syncthreads();  // every miss's position is in vold
-            if (lb.nt) copy_misses<NT, true>(s, vold, vlist, rl, r, layer, m);
-            else copy_misses<NT, false>(s, vold, vlist, rl, r, layer, m);
+        HB_PHASE(9);
+        if (tid == 0) finish_unit(s, clock_u, mc_u, rl, t, k, m);
+        if constexpr (WIDE) {
+            // a wide launch copies its own misses: with hundreds of workgroups
+            // copying at once the link is as busy as under the chip-wide fetch
+            // kernel, and the launch after it is saved
+            if (lb.copy) {
+                __syncthreads();  // every miss's position is in vold
+                const int total = m * static_cast<int>(s.row_bytes >> 4);
+                if (lb.nt) copy_misses<NT, true, 4>(s, vold, vlist, rl, r, layer, 0, total);
+                else copy_misses<NT, false, 4>(s, vold, vlist, rl, r, layer, 0, total);
+            }
         }
+        HB_PHASE(10);
+        HB_PHASE_FLUSH();
+    } else {
+        // every workgroup lists each miss's position (the slot by rank is no
+        // longer read) for the copy; the lead publishes the misses' slots
+        int* const mpos = byrank;
+        {
+            int i = i0;
+#pragma unroll
+            for (int q = 0; q < SPL; ++q) {
+                if ((mf >> q) & 1u) {
+                    mpos[i] = selv[q];
+                    if (lead) out[j0 + q] = vlist[i];
+                    ++i;
+                }
+            }
+        }
+        __syncthreads();  // every miss's position is listed
+        HB_PHASE(9);
+        {
+            // this workgroup's share of the flat (row, piece) space of the misses
+            const int total = m * static_cast<int>(s.row_bytes >> 4);
+            const int c_begin = static_cast<int>(static_cast<int64_t>(total) * g / G);
+            const int c_end = static_cast<int>(static_cast<int64_t>(total) * (g + 1) / G);
+            // (one host load a lane in flight, as in the fetch kernel, where each
+            // piece's address waits for a global load: with every workgroup
+            // of the launch copying, that is megabytes in flight, and more
+            // per lane measured slower over the host link)
+            if (lb.nt) copy_misses<NT, true, 1>(s, mpos, vlist, rl, r, layer, c_begin, c_end);
+            else copy_misses<NT, false, 1>(s, mpos, vlist, rl, r, layer, c_begin, c_end);
+        }
+        // arrival (every read of the old metadata is long done: its values were
+        // used before the barriers above); the last workgroup goes on
+        if (tid == 0) misc[X_LAST] = atomicAdd(&s.arrive[rl], 1u) == static_cast<unsigned>(G - 1) ? 1 : 0;
+        __syncthreads();
+        if (!misc[X_LAST]) {
+            HB_PHASE(10);
+            HB_PHASE_FLUSH();
+            return;
+        }
+        if (tid == 0) s.arrive[rl] = 0u;  // ready for the next launch
+        // the unit's new metadata: evicted positions back to host only (no
+        // write-back, the host copy is authoritative), the stamp run with the
+        // hits at 2t+2 and the victims at 2t+1, then per miss the plan entry,
+        // the page table and the slot map
+        int32_t* pt = s.page_table + rl * s.L_ctx;
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+            if (((vbits >> q) & 1u) && spos[q] >= 0) pt[spos[q]] = -1;
+        if (vbits | hitbits) {
+            uint32_t tsn[PER];
+#pragma unroll
+            for (int q = 0; q < PER; ++q)
+                tsn[q] = ((vbits >> q) & 1u) ? ts_miss : (((hitbits >> q) & 1u) ? ts_hit : tsv[q]);
+            store_run_masked<PER, VEC, uint32_t>(ts_g, s0, B, tsn, vbits | hitbits);
+        }
+        int4* plan = s.plan + rl * B;
+        int i = i0;
+#pragma unroll
+        for (int q = 0; q < SPL; ++q) {
+            if ((mf >> q) & 1u) {
+                const int j = j0 + q, p = selv[q];
+                const int v = vlist[i], old = vold[i];
+                plan[i] = make_int4(j, v, old, p);
+                pt[p] = v;
+                spos_g[v] = p;
+                ++i;
+            }
+        }
+        if (tid == 0) finish_unit(s, clock_u, mc_u, rl, t, k, m);
+        HB_PHASE(10);
+        HB_PHASE_FLUSH();
     }
-    HB_PHASE(10);
-    HB_PHASE_FLUSH();
 }
 
-template <int NT, int SPL, int PER, bool VEC, bool WIDE>
+template <int NT, int SPL, int PER, bool VEC, bool WIDE, bool SPLIT>
 hipError_t launch_b(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
     static LdsGrants granted;  // per instantiation
-    const void* fn = reinterpret_cast<const void*>(&bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE>);
+    const void* fn = reinterpret_cast<const void*>(&bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE, SPLIT>);
     const hipError_t e = ensure_lds_limit(fn, lds, granted);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE>), dim3(s.R, lb.n), dim3(NT), lds, st, s, lb);
+    const unsigned gx = SPLIT ? static_cast<unsigned>(s.R) * static_cast<unsigned>(lb.wgs) : static_cast<unsigned>(s.R);
+    hipLaunchKernelGGL((bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE, SPLIT>), dim3(gx, lb.n), dim3(NT), lds, st, s,
+                       lb);
     return hipGetLastError();
 }
 
 template <int NT, int SPL, int PER, bool WIDE>
 hipError_t launch_v(const StateBase& s, const LayerBatch& lb, size_t lds, bool vec, hipStream_t st) {
-    return vec ? launch_b<NT, SPL, PER, true, WIDE>(s, lb, lds, st) : launch_b<NT, SPL, PER, false, WIDE>(s, lb, lds, st);
+    if (lb.wgs > 0) {
+        // split units: 1024 lanes, vector runs (plan_wgs checks both)
+        if constexpr (NT == 1024 && !WIDE) {
+            if (vec) return launch_b<NT, SPL, PER, true, false, true>(s, lb, lds, st);
+        }
+        return hipErrorInvalidValue;
+    }
+    return vec ? launch_b<NT, SPL, PER, true, WIDE, false>(s, lb, lds, st)
+               : launch_b<NT, SPL, PER, false, WIDE, false>(s, lb, lds, st);
 }
 
 template <int NT, int SPL, bool WIDE>
@@ -803,7 +911,7 @@ size_t bitmap_lds_bytes(int k, int64_t L_ctx, bool wide) {
 }
 
 int bitmap_lanes(int B, int k, bool wide, int asked) {
-    // 512 lanes let three units share a CU in wide launches; a few units per
+    // 512 lanes let four units share a CU in wide launches; a few units per
     // launch take 1024 lanes unless asked otherwise
     const bool can512 = B <= 8 * 512 && k <= 4 * 512;
     if (asked == 512) return can512 ? 512 : 1024;

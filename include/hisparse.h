@@ -232,6 +232,21 @@ int hisparse_reset(hisparse_t h);
 #define HS_OPT_META_LANES 8     /* lanes a (request, layer) of the bitmap metadata kernel: 512 or */
                                 /* 1024, or 0 to choose by launch size (default); 512 applies     */
                                 /* only up to B = 4096 and k = 2048                               */
+#define HS_OPT_META_WGS 9       /* workgroups per (request, layer) of a metadata launch over few  */
+                                /* units (at most 256 request-layers), which all plan the unit    */
+                                /* alike and copy its misses between them in the same launch, so  */
+                                /* no fetch launch follows: G in 1..HS_MAX_META_WGS, 0 for one    */
+                                /* workgroup and a separate fetch launch, -1 to choose by launch  */
+                                /* size (default: split when the launch's misses cannot exceed    */
+                                /* 64 MB, into about 256 workgroups; larger launches keep the     */
+                                /* fetch launch, which balances the copy over all requests; so do */
+                                /* layers that have been prefetch anchors, whose plan the shared  */
+                                /* layers' replay then gets before the anchor's own copy).        */
+                                /* Applies to the bitmap kernel at 1024 lanes                     */
+                                /* with vector runs (k, B multiples of 4, 16-byte aligned arrays) */
+                                /* and records up to 1 MB; other launches keep the fetch launch.  */
+                                /* Same results either way.                                       */
+#define HS_MAX_META_WGS 64
 int hisparse_set_option(hisparse_t h, int key, int64_t value);
 
 /* Per-kernel times of launches issued while HS_OPT_TIMING was on, measured

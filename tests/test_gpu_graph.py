@@ -151,6 +151,7 @@ def test_timing_skips_captured_launches(hs):
     sel_buf = torch.empty((w.num_layers, w.num_req, w.k), dtype=torch.int32, device=dev)
     out_buf = torch.empty_like(sel_buf)
     cur = torch.cuda.current_stream()
+    res.set_option(hs.HS_OPT_META_WGS, 0)  # a metadata and a fetch launch per layer
     res.set_option(hs.HS_OPT_TIMING, 1)
     res.timing(clear=True)
     for l in range(w.num_layers):  # one eager step: timed

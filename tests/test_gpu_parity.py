@@ -69,6 +69,31 @@ def test_tiny_workload_full(hs):
     run_parity(hs, tg.TINY)
 
 
+@pytest.mark.parametrize("wgs", [0, 1, 3, 32, -1], ids=["fetch_launch", "g1", "g3", "g32", "auto"])
+def test_units_split_over_workgroups(hs, wgs):
+    """Several workgroups per (request, layer) that plan the unit alike and
+    copy its misses between them (no fetch launch; the last one to finish
+    writes the metadata), one workgroup with a separate fetch launch (0), and
+    the choice by launch size (-1): all equal the oracle bit for bit, cached
+    bytes, page tables and stamps included, over steps with and without
+    misses."""
+    w = wl("split_wgs", num_req=4, k=512, B=1024, L_ctx=9000, W_KV=136, steps=10, p_keep=0.9)
+    run_parity(hs, w, options={hs.HS_OPT_META_WGS: wgs})
+    run_parity(hs, tg.hit_only(w).replace(name="split_wgs_hits"), steps=4, options={hs.HS_OPT_META_WGS: wgs})
+
+
+def test_split_option_range(hs):
+    w = wl("split_opt", steps=1)
+    pool = make_pool(hs, w)
+    res = make_resolver(hs, w, pool)
+    for bad in (-2, hs.HS_MAX_META_WGS + 1):
+        with pytest.raises(hs.HisparseError):
+            res.set_option(hs.HS_OPT_META_WGS, bad)
+    res.set_option(hs.HS_OPT_META_WGS, hs.HS_MAX_META_WGS)
+    res.close()
+    pool.free()
+
+
 def wl(name, **kw):
     base = dict(name=name, num_req=3, num_layers=2, L_ctx=6000, W_KV=72, elem_bytes=2, k=700, B=1500, steps=12,
                 p_keep=0.8, seed_index=31)
@@ -239,7 +264,7 @@ def test_synchronous_argument_errors(hs):
     # page table of L_ctx entries, four 32-bit words, the 64-bit region row and four 64-bit
     # counters; the error word
     nrl = 2 * 2
-    assert hs.hisparse_meta_bytes(res.h) == (nrl * 32 * (4 + 4 + 16 + 1) + nrl * w.L_ctx * 4 + nrl * (4 * 4 + 8)
+    assert hs.hisparse_meta_bytes(res.h) == (nrl * 32 * (4 + 4 + 16 + 1) + nrl * w.L_ctx * 4 + nrl * (5 * 4 + 8)
                                              + nrl * 4 * 8 + 16)
     res.close()
     pool.free()
@@ -417,10 +442,12 @@ def test_wide_launch_copies_multi_piece_rows(hs, w):
     pool.free()
 
 
-def test_instrumentation_changes_nothing(hs):
+@pytest.mark.parametrize("wgs", [0, -1], ids=["fetch_launch", "split_units"])
+def test_instrumentation_changes_nothing(hs, wgs):
     """Per-launch timing and phase stamps on: results still equal the oracle
-    bit for bit, every launch is counted, and each request-layer's stamps
-    (taken by its first wave in program order) never go backwards."""
+    bit for bit, every launch is counted (no fetch launch when units copy
+    their own misses), and each request-layer's stamps (taken by the first
+    wave of its lead workgroup, in program order) never go backwards."""
     from oracle import Oracle
     w = wl("instrumented", num_req=4, num_layers=2, B=1024, k=512, L_ctx=20000, W_KV=8, steps=6)
     tr = tg.trace(w)
@@ -429,6 +456,7 @@ def test_instrumentation_changes_nothing(hs):
     res = make_resolver(hs, w, pool)
     res.set_option(hs.HS_OPT_TIMING, 1)
     res.set_option(hs.HS_OPT_PHASE_TRACE, 1)
+    res.set_option(hs.HS_OPT_META_WGS, wgs)
     o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes)
     dev = torch.device("cuda:0")
     sel = torch.from_numpy(tr).to(dev)
@@ -446,8 +474,9 @@ def test_instrumentation_changes_nothing(hs):
                 assert stamps[r, 0] != 0 and stamps[r, 10] != 0
                 assert seq == sorted(seq), f"stamps out of order, step {t} layer {l} request {r}"
     tim = res.timing(clear=True)
-    assert tim.plan_launches == w.steps * w.num_layers == tim.fetch_launches
-    assert tim.dropped == 0 and tim.plan_ms > 0 and tim.fetch_ms > 0
+    assert tim.plan_launches == w.steps * w.num_layers
+    assert tim.fetch_launches == (w.steps * w.num_layers if wgs == 0 else 0)
+    assert tim.dropped == 0 and tim.plan_ms > 0 and (tim.fetch_ms > 0) == (wgs == 0)
     st = res.state(w.num_layers - 1)
     assert np.array_equal(st["slot_pos"], o.slot_pos[w.num_layers - 1])
     assert res.error()[0] == 0
