@@ -813,13 +813,24 @@ def node_cpus(node):
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family, model and
+    stepping numbers (a virtualised host may give only a short name)."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                key, val = (x.strip() for x in line.split(":", 1))
+                if key in ("model name", "cpu family", "model", "stepping") and key not in fields:
+                    fields[key] = val
+            elif fields:
+                break
     except OSError:
-        pass
-    return None
+        return None
+    name = fields.get("model name")
+    if name is None:
+        return None
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def cpu_baseline(tg, w, tr, pool, warm_steps, seconds):
