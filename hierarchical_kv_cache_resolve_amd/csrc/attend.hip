@@ -35,8 +35,11 @@
 // exactly as the score registers hold them.  A lane of the score phase owns
 // one head: running maximum and sum are per lane (log2 units) and reduce over
 // the 4 lanes holding the same head (and, at 32 heads, over the two waves
-// sharing the head, through LDS).  A second kernel combines the chunks of
-// each (request, head).
+// sharing the head, through LDS).  A chunk's output goes out normalised by
+// its own sum, in fp16 (its values are weighted means of bf16 records, well
+// inside fp16's range; rounding adds at most 2^-11 of sum_j p_j |v_j| to the
+// error, next to 2^-9 from the bf16 probabilities), with its maximum and sum
+// in fp32; a second kernel combines the chunks of each (request, head).
 #include "hs_internal.h"
 
 namespace hs {
@@ -46,6 +49,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -125,7 +129,7 @@ __device__ __forceinline__ void issue_records(uint8_t* buf, const uint8_t* const
 template <int HT, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W / 4)))
 void mla_partial_kernel(StateBase s, int layer, const uint16_t* q, int H, const int32_t* slot_idx, int k, int chunk,
-                        int nchunk, float scale_log2, float* part_o, float* part_ml) {
+                        int nchunk, float scale_log2, _Float16* part_o, float* part_ml) {
     constexpr int HPW = 16 * HT;         // heads per workgroup
     constexpr int RS = W / HT;           // waves sharing a head tile in the score phase
     constexpr int TPW = 4 / RS;          // score tiles (of 16 records) per wave
@@ -376,38 +380,47 @@ void mla_partial_kernel(StateBase s, int layer, const uint16_t* q, int H, const 
         // issues loads into this buffer or rewrites P) orders it
     }
 
-    // partials: unnormalised O, running maximum and sum (log2 units); lane
-    // (grp, n) holds dims kDimsPerWave·w + 16dt + 4grp + i of head 16ht + n, and the
-    // score-phase statistics of head h0 + n
-    const int64_t hbase = (static_cast<int64_t>(r) * nchunk + c) * H + g * HPW;
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        float* orow = part_o + (hbase + ht * 16 + n) * kDv + wave * kDimsPerWave + 4 * grp;
-#pragma unroll
-        for (int dt = 0; dt < kWaveDTiles; ++dt) *reinterpret_cast<f32x4*>(orow + 16 * dt) = acc_o[dt][ht];
-    }
-    // the running sum of each head is split over its record shares
+    // partials: O normalised by the chunk's sum (fp16), running maximum and
+    // sum (log2 units, fp32).  The running sum of each head is split over its
+    // record shares: the shares add first (this barrier also orders every
+    // wave's last reads of the rescale factors before they are overwritten).
     float l_tot = l_run;
     if constexpr (RS > 1) {
         if (grp == 0 && rh > 0) xchg[(rh - 1) * HPW + hts * 16 + n] = l_run;
         __syncthreads();
 #pragma unroll
         for (int o = 1; o < RS; ++o) l_tot += xchg[(o - 1) * HPW + hts * 16 + n];
+    } else {
+        __syncthreads();
     }
+    const int64_t hbase = (static_cast<int64_t>(r) * nchunk + c) * H + g * HPW;
     if (grp == 0 && rh == 0) {
         part_ml[(hbase + hts * 16 + n) * 2 + 0] = m_run;
         part_ml[(hbase + hts * 16 + n) * 2 + 1] = l_tot;
+        alpha_lds[hts * 16 + n] = l_tot;
+    }
+    __syncthreads();
+    // lane (grp, n) holds dims kDimsPerWave·w + 16dt + 4grp + i of head 16ht + n
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const float l = alpha_lds[ht * 16 + n];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        _Float16* orow = part_o + (hbase + ht * 16 + n) * kDv + wave * kDimsPerWave + 4 * grp;
+#pragma unroll
+        for (int dt = 0; dt < kWaveDTiles; ++dt)
+            *reinterpret_cast<f16x4*>(orow + 16 * dt) = __builtin_convertvector(acc_o[dt][ht] * inv, f16x4);
     }
 }
 
-// Combine the chunks of each (request, head): out = sum_c w_c O_c / sum_c w_c l_c
-// with w_c = 2^(m_c - max_c m_c); lse in natural-log units.  128 lanes, four
-// dimensions each; the partial loads of up to kCombineBatch chunks are all
-// issued before any is used.
+// Combine the chunks of each (request, head): out = sum_c w_c l_c o_c /
+// sum_c w_c l_c with w_c = 2^(m_c - max_c m_c) and o_c the chunk's normalised
+// output; lse in natural-log units.  128 lanes, four dimensions each; the
+// partial loads of up to kCombineBatch chunks are all issued before any is
+// used.
 constexpr int kCombineThreads = kDv / 4;
 constexpr int kCombineBatch = 8;
 
-__global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const float* part_o, const float* part_ml,
+__global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const _Float16* part_o, const float* part_ml,
                                                                       int H, int nchunk, float* out, float* lse) {
     const int h = blockIdx.x, r = blockIdx.y;
     const int64_t first = static_cast<int64_t>(r) * nchunk * H + h;   // chunk c at first + c * H
@@ -416,20 +429,20 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const floa
     float denom = 0.f;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < nchunk; c0 += kCombineBatch) {
-        f32x4 o[kCombineBatch];
+        f16x4 o[kCombineBatch];
         float wgt[kCombineBatch];
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u) {
             const int c = min(c0 + u, nchunk - 1);
             const int64_t idx = first + static_cast<int64_t>(c) * H;
-            o[u] = *reinterpret_cast<const f32x4*>(part_o + idx * kDv + 4 * threadIdx.x);
+            o[u] = *reinterpret_cast<const f16x4*>(part_o + idx * kDv + 4 * threadIdx.x);
             const float m = part_ml[idx * 2];
-            wgt[u] = (c0 + u < nchunk && m != -INFINITY) ? exp2f(m - M) : 0.f;
-            denom += wgt[u] * part_ml[idx * 2 + 1];
+            wgt[u] = (c0 + u < nchunk && m != -INFINITY) ? exp2f(m - M) * part_ml[idx * 2 + 1] : 0.f;
+            denom += wgt[u];
         }
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u)
-            if (wgt[u] != 0.f) acc += wgt[u] * o[u];
+            if (wgt[u] != 0.f) acc += wgt[u] * __builtin_convertvector(o[u], f32x4);
     }
     const float inv = denom > 0.f ? 1.f / denom : 0.f;
     *reinterpret_cast<f32x4*>(out + (static_cast<int64_t>(r) * H + h) * kDv + 4 * threadIdx.x) = acc * inv;
@@ -440,7 +453,8 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const floa
 }  // namespace
 
 size_t attend_workspace_floats(int R, int H, int nchunk) {
-    return static_cast<size_t>(R) * nchunk * H * (kDv + 2);
+    // fp16 outputs (kDv halves) and fp32 maximum and sum per (request, chunk, head)
+    return static_cast<size_t>(R) * nchunk * H * (kDv / 2 + 2);
 }
 
 int attend_chunk(int R, int H, int k, int ht) {
@@ -466,8 +480,8 @@ hipError_t launch_attend_mla(const StateBase& s, int layer, const uint16_t* q, i
                              hipStream_t st) {
     if (ht != 2 && ht != 4) return hipErrorInvalidValue;
     const int nchunk = (k + chunk - 1) / chunk;
-    float* part_o = workspace;
-    float* part_ml = workspace + static_cast<size_t>(s.R) * nchunk * H * kDv;
+    _Float16* part_o = reinterpret_cast<_Float16*>(workspace);
+    float* part_ml = workspace + static_cast<size_t>(s.R) * nchunk * H * (kDv / 2);
     const void* fn = ht == 2 ? reinterpret_cast<const void*>(&mla_partial_kernel<2, 4>)
                              : reinterpret_cast<const void*>(&mla_partial_kernel<4, 8>);
     static LdsGrants granted[2];  // one per kernel instance

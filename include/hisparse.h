@@ -301,12 +301,13 @@ int hisparse_attend_mla(hisparse_t h, int layer, const void* d_q, int num_heads,
 /* hisparse_attend_mla without any allocation, for callers that cannot
  * allocate device memory (code under HIP graph capture, serving loops that
  * must not call hipMalloc, harnesses that forbid it).  Same arguments, same
- * kernels and the same results as hisparse_attend_mla; its fp32 split-k
- * partials go to a fixed device area of HS_SCRATCH_BYTES that the library
- * holds on each GPU until the process ends, instead of the handle's
- * workspace.  A call whose partials, num_req * num_heads * chunks * 514
- * floats, exceed that area is refused with HS_E_SCRATCH (at most 64 MiB:
- * e.g. 32 requests x 128 heads x k = 2048).  The handle's device must be
+ * kernels and the same results as hisparse_attend_mla; its split-k partials
+ * (fp16 outputs, fp32 maxima and sums) go to a fixed device area of
+ * HS_SCRATCH_BYTES that the library holds on each GPU until the process ends,
+ * instead of the handle's workspace.  A call whose partials, num_req *
+ * num_heads * chunks * 258 floats' worth, exceed that area is refused with
+ * HS_E_SCRATCH (at k = 2048: above 256 requests at 128 heads, above 63
+ * requests at 1024 heads).  The handle's device must be
  * current (else HS_E_INVAL).  All calls on one GPU share the area: calls that
  * overlap on one GPU (on different streams, or from different handles) race
  * and must be ordered by the caller.  Nothing in the area needs clearing

@@ -47,12 +47,15 @@ def mla_decode(q_bits: np.ndarray, rec_bits: np.ndarray, scale: float):
 
 def error_bound(q_bits: np.ndarray, rec_bits: np.ndarray, scale: float) -> np.ndarray:
     """Per-element bound for a kernel that forms scores in float32 from bf16
-    inputs, keeps softmax in float32 and rounds the probabilities to bf16
-    before the value product (relative error at most 2^-9 each):
+    inputs, keeps softmax in float32, rounds the probabilities to bf16
+    before the value product (relative error at most 2^-9 each) and may
+    round partial outputs over subsets of the records, each normalised by
+    its own sum, to fp16 (relative 2^-11, of a value bounded by that subset's
+    sum_j p_j |rec_j[d]| / sum_j p_j):
         |err[h, d]| <= 2^-8 * sum_j p[h, j] * |rec_j[d]| + 1e-6
-    (a factor 2 over the rounding term covers the float32 score, exponent
-    and normalisation errors: for scores of a few units they are near 1e-5
-    relative, far below the 2^-9 margin)."""
+    (2^-9 + 2^-11 of the same sum leave a quarter of the 2^-8 for the float32
+    score, exponent and normalisation errors, which for scores of a few units
+    are near 1e-5 relative; the 1e-6 covers fp16 subnormal spacing)."""
     q = bf16_to_f64(q_bits)
     rec = bf16_to_f64(rec_bits)
     s = np.matmul(q, np.swapaxes(rec, 1, 2)) * scale

@@ -68,8 +68,8 @@ def test_noalloc_equals_allocating_entry_point(hs):
 
 
 def test_noalloc_refuses_partials_beyond_its_area(hs):
-    """64 requests x 1024 heads x k = 2048 needs 64 * 1024 * 514 floats of
-    partials (one chunk), more than the 64 MiB area: HS_E_SCRATCH, nothing
+    """64 requests x 1024 heads x k = 2048 needs 64 * 1024 * 258 floats' worth
+    of partials (one chunk), more than the 64 MiB area: HS_E_SCRATCH, nothing
     launched, and the allocating entry point still takes the same call."""
     w = tg.MLA.replace(name="noalloc_big", num_req=64, num_layers=1, L_ctx=4096, B=2048, k=2048, steps=1)
     tr = tg.trace(w)
@@ -82,7 +82,7 @@ def test_noalloc_refuses_partials_beyond_its_area(hs):
     q = torch.zeros((w.num_req, heads, 576), dtype=torch.int16, device=dev)
     out = torch.empty((w.num_req, heads, 512), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
-    assert w.num_req * heads * 514 * 4 > hs.HS_SCRATCH_BYTES
+    assert w.num_req * heads * 258 * 4 > hs.HS_SCRATCH_BYTES
     rc = hs.hisparse_attend_mla_noalloc(res.h, 0, q.data_ptr(), heads, slots.data_ptr(), w.k, 1.0,
                                         out.data_ptr(), 0, stream)
     assert rc == hs.HS_E_SCRATCH
