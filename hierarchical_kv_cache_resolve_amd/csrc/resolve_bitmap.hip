@@ -342,9 +342,10 @@ __device__ inline void copy_misses(const StateBase& s, const int* mpos, const in
 // and it copies its own misses); SPLIT: each unit takes lb.wgs workgroups,
 // which all plan it alike (the plan is deterministic) and copy its misses
 // between them, so no fetch launch follows.  A split unit's workgroups read
-// the old slot map, stamps and clock; only the last one to finish (a counter
-// per unit, no workgroup ever waits for another) writes the new metadata, so
-// none is overwritten while another workgroup may still read it.  A unit
+// the old slot map, stamps and clock; only the last one to be done reading
+// them (a counter per unit, bumped before the copy and looked at after it; no
+// workgroup ever waits for another) writes the new metadata, after its copy,
+// so none is overwritten while another workgroup may still read it.  A unit
 // without misses is the exception: the lead workgroup ends it at once, as
 // what it writes (hit stamps, clock) changes nothing the others need when
 // every selection hits.
@@ -790,6 +791,12 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         }
         __syncthreads();  // every miss's position is listed
         HB_PHASE(9);
+        // arrival, before the copy (which reads no metadata): every read of
+        // the old metadata is long done, its values used before the barriers
+        // above.  The counter's answer is only looked at after the copy, so
+        // its round trip overlaps the copy instead of following it.
+        unsigned arrived_before = 0;
+        if (tid == 0) arrived_before = atomicAdd(&s.arrive[rl], 1u);
         {
             // this workgroup's share of the flat (row, piece) space of the misses
             const int total = m * static_cast<int>(s.row_bytes >> 4);
@@ -802,9 +809,8 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
             if (lb.nt) copy_misses<NT, true, 1>(s, mpos, vlist, rl, r, layer, c_begin, c_end);
             else copy_misses<NT, false, 1>(s, mpos, vlist, rl, r, layer, c_begin, c_end);
         }
-        // arrival (every read of the old metadata is long done: its values were
-        // used before the barriers above); the last workgroup goes on
-        if (tid == 0) misc[X_LAST] = atomicAdd(&s.arrive[rl], 1u) == static_cast<unsigned>(G - 1) ? 1 : 0;
+        // the last workgroup to arrive writes the new metadata
+        if (tid == 0) misc[X_LAST] = arrived_before == static_cast<unsigned>(G - 1) ? 1 : 0;
         __syncthreads();
         if (!misc[X_LAST]) {
             HB_PHASE(10);

@@ -24,7 +24,8 @@ def hs():
     return m
 
 
-def test_append_then_select(hs):
+@pytest.mark.parametrize("wgs", [0, -1], ids=["fetch_launch", "split_units"])
+def test_append_then_select(hs, wgs):
     from oracle import Oracle
     L0 = 5000
     w = tg.Workload("append", 4, 2, 6000, 64, 2, 300, 600, 40, tg.LOCALITY, 0.8, seed_index=51)
@@ -34,6 +35,7 @@ def test_append_then_select(hs):
     pool_copy = pinned.copy()                     # the oracle's own host pool
     rr = w.region_rows()
     res = make_resolver(hs, w, pool)
+    res.set_option(hs.HS_OPT_META_WGS, wgs)
     o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes)
     lengths = np.full((w.num_req, w.num_layers), L0, np.int64)
     res.set_lengths(lengths)
@@ -93,7 +95,8 @@ def test_append_then_select(hs):
     pool.free()
 
 
-def test_shrink_drops_cached_tail_then_refetches(hs):
+@pytest.mark.parametrize("wgs", [0, -1], ids=["fetch_launch", "split_units"])
+def test_shrink_drops_cached_tail_then_refetches(hs, wgs):
     """Lowering the lengths after records are cached: the positions cut off
     leave the cache on the GPU exactly as in the oracle (slot empty, stamp 0,
     page-table entry -1); records appended again at those positions are
@@ -107,6 +110,7 @@ def test_shrink_drops_cached_tail_then_refetches(hs):
     pool_copy = pinned.copy()
     rr = w.region_rows()
     res = make_resolver(hs, w, pool)
+    res.set_option(hs.HS_OPT_META_WGS, wgs)
     o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes)
     lengths = np.full((w.num_req, w.num_layers), L0, np.int64)
     res.set_lengths(lengths)

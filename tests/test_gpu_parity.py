@@ -174,13 +174,15 @@ def test_gather_checksum_matches_pool_rows(hs):
     pool.free()
 
 
-def test_rejected_requests_and_sticky_error(hs):
+@pytest.mark.parametrize("wgs", [0, -1], ids=["fetch_launch", "split_units"])
+def test_rejected_requests_and_sticky_error(hs, wgs):
     from oracle import Oracle
     w = wl("errors", num_req=4, num_layers=1, B=64, k=16, L_ctx=200, W_KV=8, steps=3)
     tr = tg.trace(w)
     pool = make_pool(hs, w)
     pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
     res = make_resolver(hs, w, pool)
+    res.set_option(hs.HS_OPT_META_WGS, wgs)
     o = Oracle(w.num_req, 1, w.B, w.L_ctx, w.row_bytes)
     dev = torch.device("cuda:0")
     out = torch.empty((w.num_req, w.k), dtype=torch.int32, device=dev)
@@ -298,7 +300,8 @@ def test_reset_refills_exactly(hs):
     pool.free()
 
 
-def test_victims_older_than_histogram_range(hs):
+@pytest.mark.parametrize("wgs", [0, -1], ids=["fetch_launch", "split_units"])
+def test_victims_older_than_histogram_range(hs, wgs):
     """Victims whose stamps are more than 1023 apart from 2t (slots filled early
     and never touched again) take the kernel's general radix-select path; a
     hand-built trace forces it, the oracle decides."""
@@ -317,6 +320,7 @@ def test_victims_older_than_histogram_range(hs):
     pool = make_pool(hs, w)
     pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
     res = make_resolver(hs, w, pool)
+    res.set_option(hs.HS_OPT_META_WGS, wgs)
     scan = make_resolver(hs, w, pool)
     scan.set_option(hs.HS_OPT_PROBE, hs.HS_PROBE_PAGE_TABLE)
     hscan = make_resolver(hs, w, pool)
