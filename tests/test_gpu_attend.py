@@ -215,6 +215,40 @@ def test_attend_full_size(hs, heads_per_wg):
     check(hs, q_np, records(w, pool_np, 0, sel), 1.0 / 24.0, out, lse)
 
 
+@pytest.mark.parametrize("heads_per_wg", [0, 32])
+def test_attend_full_size_with_holes(hs, heads_per_wg):
+    """The decode shape with slots left out: whole leading sub-chunks of every
+    chunk empty (the running maximum stays -inf across them), a single record,
+    no record, random holes; a large scale so that the lazily moved reference
+    of the softmax moves often."""
+    w = tg.Workload("attend_full_holes", 16, 1, 32768, 576, 2, 2048, 4096, 2, tg.LOCALITY, 0.87, seed_index=69)
+    sel_all = tg.trace(w)
+    pool = keep(make_pool(hs, w))
+    pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
+    res = keep(make_resolver(hs, w, pool))
+    res.set_option(hs.HS_OPT_ATTN_HEADS, heads_per_wg)
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(12)
+    slot_idx = torch.empty((w.num_req, w.k), dtype=torch.int32, device=dev)
+    for t in range(w.steps):
+        sel = np.ascontiguousarray(sel_all[t, 0])
+        res.resolve(0, torch.from_numpy(sel).to(dev), slot_idx)
+        res.check_error()
+    valid = rng.random((w.num_req, w.k)) < 0.9
+    valid[0, :] = True
+    valid[1, :] = (np.arange(w.k) % 256) >= 200     # the first 200 of every 256 left out
+    valid[2, :] = False
+    valid[2, w.k - 1] = True
+    valid[3, :] = False
+    s = slot_idx.cpu().numpy()
+    s[~valid] = -1
+    slot_idx = torch.from_numpy(s).to(dev)
+    q_np = rand_bits(rng, (w.num_req, 128, D_QK))
+    print(f"attend full size with holes, heads/wg={heads_per_wg}", flush=True)
+    out, lse = run_attend(hs, res, 0, q_np, slot_idx, 0.5, dev)
+    check(hs, q_np, records(w, pool_np, 0, sel), 0.5, out, lse, valid=valid)
+
+
 def test_attend_in_a_captured_graph(hs):
     """RESOLVE + attention captured together and replayed over several steps,
     with eager work between replays: every replay equals the eager run."""
