@@ -266,7 +266,8 @@ __device__ inline void radix_select(int* hist, int* misc, const uint32_t (&tsv)[
 // them out at the end.  Slots in program order: 0 start, 1 reads issued and
 // LDS cleared, 2 selection inserted, 3 ranks and hit test, 4 threshold, 5 slot
 // by rank and victim counts, 7 selection side looked up, 8 hits published,
-// 6 victim lists, 9 metadata written, 10 end.
+// 6 victim lists, 9 metadata written, 10 end; split units take 7 and 8
+// (and their host loads) before 4 and 5.
 #define HB_PHASE(i)                                                                      \
     do {                                                                                 \
         if (lb.trace && tid == 0 && lead)                                                \
@@ -357,7 +358,10 @@ __device__ inline void copy_misses(const StateBase& s, const int* mpos, const in
 // counts; (m > 0 only) hits published and miss counts, then -- wide launches:
 // after one more barrier, as the lists overlay the bitmap -- victims listed
 // by rank, B5.  After B5 each missing selection takes the victim of its own
-// rank.
+// rank.  A split unit with misses takes B4 for the slot by rank alone, looks
+// its selections up, lists each miss's position by rank (two barriers),
+// issues its first host loads, and only then finds the threshold and victim
+// counts (one barrier) before the victim lists and B5.
 template <int NT, int SPL, int PER, bool VEC, bool WIDE, bool SPLIT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WIDE ? (NT == 512 ? 8 : 6) : 1)))
 void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
@@ -557,11 +561,13 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     // threshold stamp T and how many candidates stamped exactly T go (lowest
     // slots first; every other victim is older than T), then the victim
     // counts in slot order, strict and tied packed into one scan (strict in
-    // the low 16 bits, tied in the high; both at most B <= 16384)
+    // the low 16 bits, tied in the high; both at most B <= 16384).  A split
+    // unit finds it later, after its selections are looked up and its host
+    // loads issued, so that they are in flight meanwhile.
     uint32_t T = 0;
     int need_eq = 0, packed = 0, vincl = 0;
     unsigned strict_bits = 0, tie_bits = 0;
-    if (m > 0) {
+    auto find_threshold = [&]() {
         if (!spec) {
 #pragma unroll
             for (int q = 0; q < PER; ++q) {
@@ -608,9 +614,10 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         vincl = wave_incl_scan(packed);
         if (lane == 63) misc[X_VICT + wave] = vincl;
         HB_PHASE(4);
-    }
+    };
+    if (!SPLIT && m > 0) find_threshold();
     __syncthreads();
-    HB_PHASE(5);
+    if constexpr (!SPLIT) HB_PHASE(5);
 
     // 5. selection side: the slot recorded at each selection's rank is its
     // hit, published now, or nothing (a miss)
@@ -701,6 +708,53 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     const int mincl = wave_incl_scan(mc);
     if (lane == 63) misc[X_MISS + wave] = mincl;
     if constexpr (WIDE) __syncthreads();  // the victim lists overwrite the bitmap
+    // a split unit: the position of each miss is listed by rank (over the slot
+    // by rank, read by nobody any more) and this workgroup's first pieces of
+    // the unit's flat (row, piece) space of misses are loaded from the host
+    // into registers now; the victim slots they go to are found meanwhile
+    // (one piece a lane, as in the copy: with every workgroup of a launch
+    // loading, that is already megabytes in flight, and two measured slower)
+    constexpr int kEarly = 1;
+    int i0 = 0, c_begin = 0, c_end = 0;
+    u32x4 ev[kEarly];
+    int ei[kEarly], eoff[kEarly];
+    if constexpr (SPLIT) {
+        __syncthreads();  // miss counts visible; every read of the slot by rank done
+        i0 = mincl - mc + sum_before(misc + X_MISS, wave);
+        int* const mpos = byrank;
+        {
+            int i = i0;
+#pragma unroll
+            for (int q = 0; q < SPL; ++q) {
+                if ((mf >> q) & 1u) {
+                    mpos[i] = selv[q];
+                    ++i;
+                }
+            }
+        }
+        __syncthreads();  // every miss's position is listed
+        const int row16 = static_cast<int>(s.row_bytes >> 4);
+        const int total = m * row16;
+        c_begin = static_cast<int>(static_cast<int64_t>(total) * g / G);
+        c_end = static_cast<int>(static_cast<int64_t>(total) * (g + 1) / G);
+        const uint8_t* src_base = s.pool + s.region_row[static_cast<int64_t>(r) * s.NL + layer] * s.row_bytes;
+#pragma unroll
+        for (int x = 0; x < kEarly; ++x) {
+            const int c = c_begin + tid + x * NT;
+            ei[x] = -1;
+            eoff[x] = 0;
+            if (c < c_end) {
+                const int i = c / row16, off = c - i * row16;
+                const u32x4* src = reinterpret_cast<const u32x4*>(src_base + static_cast<int64_t>(mpos[i]) * s.row_bytes) + off;
+                ei[x] = i;
+                eoff[x] = off;
+                ev[x] = lb.nt ? ld16<true>(src) : ld16<false>(src);
+            }
+        }
+        find_threshold();
+        __syncthreads();  // victim counts visible
+        HB_PHASE(5);
+    }
     unsigned vbits = 0;
     {
         const int vpre = vincl - packed + sum_before(misc + X_VICT, wave);
@@ -741,7 +795,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
 
     // 6. the i-th miss (ascending selection index) takes the victim of rank i
     // (ascending slot): plan entry, page table, slot map and publication
-    const int i0 = mincl - mc + sum_before(misc + X_MISS, wave);  // this lane's first miss
+    if constexpr (!SPLIT) i0 = mincl - mc + sum_before(misc + X_MISS, wave);  // this lane's first miss
     if constexpr (!SPLIT) {
         int32_t* pt = s.page_table + rl * s.L_ctx;
         int4* plan = s.plan + rl * B;
@@ -775,21 +829,17 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         HB_PHASE(10);
         HB_PHASE_FLUSH();
     } else {
-        // every workgroup lists each miss's position (the slot by rank is no
-        // longer read) for the copy; the lead publishes the misses' slots
-        int* const mpos = byrank;
-        {
+        // the lead publishes the misses' slots
+        if (lead) {
             int i = i0;
 #pragma unroll
             for (int q = 0; q < SPL; ++q) {
                 if ((mf >> q) & 1u) {
-                    mpos[i] = selv[q];
-                    if (lead) out[j0 + q] = vlist[i];
+                    out[j0 + q] = vlist[i];
                     ++i;
                 }
             }
         }
-        __syncthreads();  // every miss's position is listed
         HB_PHASE(9);
         // arrival, before the copy (which reads no metadata): every read of
         // the old metadata is long done, its values used before the barriers
@@ -798,16 +848,23 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         unsigned arrived_before = 0;
         if (tid == 0) arrived_before = atomicAdd(&s.arrive[rl], 1u);
         {
-            // this workgroup's share of the flat (row, piece) space of the misses
-            const int total = m * static_cast<int>(s.row_bytes >> 4);
-            const int c_begin = static_cast<int>(static_cast<int64_t>(total) * g / G);
-            const int c_end = static_cast<int>(static_cast<int64_t>(total) * (g + 1) / G);
-            // (one host load a lane in flight, as in the fetch kernel, where each
-            // piece's address waits for a global load: with every workgroup
-            // of the launch copying, that is megabytes in flight, and more
-            // per lane measured slower over the host link)
-            if (lb.nt) copy_misses<NT, true, 1>(s, mpos, vlist, rl, r, layer, c_begin, c_end);
-            else copy_misses<NT, false, 1>(s, mpos, vlist, rl, r, layer, c_begin, c_end);
+            // the pieces loaded early go to their victim slots, then the rest
+            // of this workgroup's share (one host load a lane in flight, as in
+            // the fetch kernel: with every workgroup of the launch copying,
+            // that is megabytes in flight, and more per lane measured slower
+            // over the host link)
+            uint8_t* dst_base = s.cache + rl * s.B * s.row_bytes;
+#pragma unroll
+            for (int x = 0; x < kEarly; ++x) {
+                if (ei[x] >= 0) {
+                    u32x4* dst = reinterpret_cast<u32x4*>(dst_base + static_cast<int64_t>(vlist[ei[x]]) * s.row_bytes) + eoff[x];
+                    if (lb.nt) st16<true>(dst, ev[x]);
+                    else st16<false>(dst, ev[x]);
+                }
+            }
+            const int c_rest = min(c_end, c_begin + kEarly * NT);
+            if (lb.nt) copy_misses<NT, true, 1>(s, byrank, vlist, rl, r, layer, c_rest, c_end);
+            else copy_misses<NT, false, 1>(s, byrank, vlist, rl, r, layer, c_rest, c_end);
         }
         // the last workgroup to arrive writes the new metadata
         if (tid == 0) misc[X_LAST] = arrived_before == static_cast<unsigned>(G - 1) ? 1 : 0;
