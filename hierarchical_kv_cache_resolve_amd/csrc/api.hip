@@ -793,6 +793,8 @@ static int attend_shape(hisparse_t h, int layer, const void* d_q, int num_heads,
     if (layer < 0 || layer >= h->NL) return HS_E_LAYER;
     if (!d_q || !d_slot_idx || !d_out || num_heads < 64 || num_heads % 64 != 0 || num_heads > HS_MAX_HEADS)
         return HS_E_INVAL;
+    // queries are read and outputs written 16 bytes a lane
+    if ((reinterpret_cast<uintptr_t>(d_q) | reinterpret_cast<uintptr_t>(d_out)) & 15u) return HS_E_INVAL;
     if (h->dtype != HS_BF16 || h->W_KV != 576) return HS_E_INVAL;
     if (k < 1 || k > h->B) return HS_E_K;
     *ht = h->attn_heads ? h->attn_heads / 16 : hs::attend_head_tiles(h->R, num_heads, k);

@@ -292,7 +292,8 @@ int hisparse_gather_checksum(hisparse_t h, int layer, const int32_t* d_slot_idx,
  *   d_lse   fp32 [num_req][num_heads] log-sum-exp of the scaled scores, or NULL
  * A record whose slot is -1 (a rejected request) is left out; a request
  * with none gives zeros and lse = -inf.  num_heads must be a multiple of
- * 64, at most HS_MAX_HEADS.  The first call for a larger shape allocates the handle's workspace
+ * 64, at most HS_MAX_HEADS; d_q and d_out must be 16-byte aligned (both are
+ * moved 16 bytes a lane).  The first call for a larger shape allocates the handle's workspace
  * (make that call before capturing a graph).
  * Errors: HS_E_HANDLE, HS_E_LAYER, HS_E_INVAL, HS_E_K, HS_E_NOMEM, HS_E_HIP. */
 int hisparse_attend_mla(hisparse_t h, int layer, const void* d_q, int num_heads, const int32_t* d_slot_idx, int k,

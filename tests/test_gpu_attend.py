@@ -190,6 +190,18 @@ def test_attend_rejects_bad_arguments(hs):
         res2.attend_mla(0, q_many, idx, 0.1, out_many)  # more heads than HS_MAX_HEADS
     with pytest.raises(hs.HisparseError):
         res2.set_option(hs.HS_OPT_ATTN_HEADS, 48)       # 32 or 64 heads a workgroup, or 0
+    # queries and outputs move 16 bytes a lane: views 2 and 4 bytes off alignment are refused
+    qbuf = torch.zeros(64 * D_QK + 8, dtype=torch.int16, device=dev)
+    obuf = torch.zeros(64 * D_V + 4, dtype=torch.float32, device=dev)
+    q_off = qbuf[1:1 + 64 * D_QK].view(1, 64, D_QK)
+    out_off = obuf[1:1 + 64 * D_V].view(1, 64, D_V)
+    assert q_off.data_ptr() % 16 == 2 and out_off.data_ptr() % 16 == 4
+    with pytest.raises(hs.HisparseError):
+        res2.attend_mla(0, q_off, idx, 0.1, out)
+    with pytest.raises(hs.HisparseError):
+        res2.attend_mla(0, q, idx, 0.1, out_off)
+    assert hs.hisparse_attend_mla_noalloc(res2.h, 0, q_off.data_ptr(), 64, idx.data_ptr(), 16, 0.1, out.data_ptr(),
+                                          0, 0) == hs.HS_E_INVAL
 
 
 @pytest.mark.parametrize("heads_per_wg", [0, 32])
