@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hit-only", action="store_true")
     ap.add_argument("--no-probes", action="store_true")
+    ap.add_argument("--markers", action="store_true",
+                    help="roctx range around every library call that enqueues work (rocprofv3 --marker-trace)")
     ap.add_argument("--probe", default="default", choices=["default", "page_table", "slot_scan", "slot_scan_hash"],
                     help="how the metadata kernel finds hits (default: the library's)")
     ap.add_argument("--meta-lanes", type=int, default=0, choices=[0, 512, 1024],
@@ -147,6 +149,8 @@ def main():
         res.set_option(hs.HS_OPT_META_LANES, args.meta_lanes)
     if args.meta_wgs is not None:
         res.set_option(hs.HS_OPT_META_WGS, args.meta_wgs)
+    if args.markers:
+        res.set_option(hs.HS_OPT_MARKERS, 1)
     if args.unroll:
         res.set_option(hs.HS_OPT_FETCH_UNROLL, args.unroll)
     sel = torch.from_numpy(tr).to(dev)

@@ -7,6 +7,8 @@
 // the metadata kernel (resolve.hip) and the fetch kernel (fetch.hip) -- and
 // nothing else: no allocation, no synchronisation, no host read of device
 // memory, so a decode step that calls it can be captured in a HIP graph.
+#include <dlfcn.h>
+
 #include <algorithm>
 #include <climits>
 #include <cstdint>
@@ -34,6 +36,7 @@ struct hisparse_ctx {
     int attn_heads = 0;  // heads per attention workgroup: 0 = by shape, 32 or 64
     int meta_lanes = 0;  // lanes a unit of the bitmap metadata kernel: 0 = by launch size, 512 or 1024
     int meta_wgs = -1;   // workgroups a unit that copies its own misses: -1 = by launch size, 0 = never, G
+    bool markers = false;  // roctx range around each enqueueing entry point
     float* attn_ws = nullptr;       // consumer workspace (partials per chunk)
     size_t attn_ws_floats = 0;
     // ordering of resolve / prefetch (host-side bookkeeping only)
@@ -54,6 +57,52 @@ struct hisparse_ctx {
     double acc_ms[4] = {0, 0, 0, 0};
     int64_t acc_n[4] = {0, 0, 0, 0};
 };
+
+// roctx ranges (HS_OPT_MARKERS): the profiler's marker library is opened on
+// first use, so the library has no link-time dependency on it; with no tool
+// attached its calls do nothing.
+namespace {
+struct RoctxApi {
+    int (*push)(const char*) = nullptr;
+    int (*pop)() = nullptr;
+};
+const RoctxApi* roctx_api() {
+    static RoctxApi api;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        void* lib = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+        if (!lib) lib = dlopen("librocprofiler-sdk-roctx.so", RTLD_NOW | RTLD_LOCAL);
+        if (!lib) return;
+        auto push = reinterpret_cast<int (*)(const char*)>(dlsym(lib, "roctxRangePushA"));
+        auto pop = reinterpret_cast<int (*)()>(dlsym(lib, "roctxRangePop"));
+        if (push && pop) {
+            api.push = push;
+            api.pop = pop;
+        }
+    });
+    return api.push ? &api : nullptr;
+}
+// a range named after the entry point and its layer for the lifetime of the guard
+class MarkRange {
+   public:
+    MarkRange(const hisparse_ctx* h, const char* what, int layer) {
+        if (!h || !h->markers) return;
+        api_ = roctx_api();
+        if (!api_) return;
+        char name[64];
+        std::snprintf(name, sizeof name, "%s layer %d", what, layer);
+        api_->push(name);
+    }
+    ~MarkRange() {
+        if (api_) api_->pop();
+    }
+    MarkRange(const MarkRange&) = delete;
+    MarkRange& operator=(const MarkRange&) = delete;
+
+   private:
+    const RoctxApi* api_ = nullptr;
+};
+}  // namespace
 
 // Scratch area of the no-allocation attention entry point: the fp32 split-k
 // partials of hisparse_attend_mla_noalloc live here instead of in a workspace
@@ -434,6 +483,7 @@ static int resolve_plan_path(hisparse_t h, int n, const int* layers, const int32
 
 int hisparse_resolve(hisparse_t h, int layer, const int32_t* d_sel, int k, int32_t* d_slot_idx, void* stream) {
     if (!valid(h)) return HS_E_HANDLE;
+    MarkRange mark(h, "hisparse_resolve", layer);
     if (layer < 0 || layer >= h->NL) return HS_E_LAYER;
     if (!d_sel || !d_slot_idx) return HS_E_INVAL;
     int rc = check_k(h, k);
@@ -468,6 +518,7 @@ int hisparse_resolve_layers(hisparse_t h, int n, const int* layers, const int32_
                             int32_t* const* d_slot_idx_ptrs, void* stream) {
     if (!valid(h)) return HS_E_HANDLE;
     if (n < 1 || n > hs::kMaxBatch || !layers || !d_sel_ptrs || !d_slot_idx_ptrs) return HS_E_INVAL;
+    MarkRange mark(h, "hisparse_resolve_layers", layers[0]);
     if (static_cast<int64_t>(n) * h->R > 8192) return HS_E_INVAL;
     int rc = check_k(h, k);
     if (rc != HS_OK) return rc;
@@ -483,6 +534,7 @@ int hisparse_resolve_layers(hisparse_t h, int n, const int* layers, const int32_
 
 int hisparse_prefetch(hisparse_t h, int anchor, const int* shared, int n, void* side_stream) {
     if (!valid(h)) return HS_E_HANDLE;
+    MarkRange mark(h, "hisparse_prefetch", anchor);
     if (anchor < 0 || anchor >= h->NL) return HS_E_LAYER;
     if (n < 1 || n > hs::kMaxBatch || !shared) return HS_E_INVAL;
     if (static_cast<int64_t>(n) * h->R > 8192) return HS_E_INVAL;
@@ -524,6 +576,7 @@ int hisparse_prefetch(hisparse_t h, int anchor, const int* shared, int n, void* 
 
 int hisparse_append(hisparse_t h, int layer, const void* d_rows, void* stream) {
     if (!valid(h)) return HS_E_HANDLE;
+    MarkRange mark(h, "hisparse_append", layer);
     if (layer < 0 || layer >= h->NL) return HS_E_LAYER;
     if (!d_rows) return HS_E_INVAL;
     return hs::launch_append(h->s, layer, static_cast<const uint8_t*>(d_rows), static_cast<hipStream_t>(stream)) ==
@@ -692,6 +745,10 @@ int hisparse_set_option(hisparse_t h, int key, int64_t value) {
                 h->s.phase = nullptr;
             }
             return HS_OK;
+        case HS_OPT_MARKERS:
+            if (value && !roctx_api()) return HS_E_INVAL;  // the marker library is not there
+            h->markers = value != 0;
+            return HS_OK;
         case HS_OPT_TIMING:
             if (value && h->ring.empty()) {
                 h->ring.resize(kRingPairs);
@@ -810,6 +867,7 @@ int hisparse_attend_mla(hisparse_t h, int layer, const void* d_q, int num_heads,
     size_t need = 0;
     const int rc = attend_shape(h, layer, d_q, num_heads, d_slot_idx, k, d_out, &ht, &chunk, &need);
     if (rc != HS_OK) return rc;
+    MarkRange mark(h, "hisparse_attend_mla", layer);
     if (need > h->attn_ws_floats) {
         HS_TRY(hipDeviceSynchronize());
         if (h->attn_ws) (void)hipFree(h->attn_ws);
@@ -833,6 +891,7 @@ int hisparse_attend_mla_noalloc(hisparse_t h, int layer, const void* d_q, int nu
     const int rc = attend_shape(h, layer, d_q, num_heads, d_slot_idx, k, d_out, &ht, &chunk, &need);
     if (rc != HS_OK) return rc;
     if (need > kScratchFloats) return HS_E_SCRATCH;
+    MarkRange mark(h, "hisparse_attend_mla_noalloc", layer);
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev != h->device) {
         (void)hipGetLastError();

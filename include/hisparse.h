@@ -247,6 +247,12 @@ int hisparse_reset(hisparse_t h);
                                 /* and records up to 1 MB; other launches keep the fetch launch.  */
                                 /* Same results either way.                                       */
 #define HS_MAX_META_WGS 64
+#define HS_OPT_MARKERS 10       /* 1: a roctx range ("hisparse_resolve layer 3", ...) around each */
+                                /* call that enqueues work (resolve, resolve_layers, prefetch,    */
+                                /* append, attend_mla and its no-allocation form), for host-side  */
+                                /* traces (rocprofv3 --marker-trace); the ranges mark when a call */
+                                /* enqueues, not when its kernels run.  HS_E_INVAL if the marker  */
+                                /* library (librocprofiler-sdk-roctx) cannot be opened.           */
 int hisparse_set_option(hisparse_t h, int key, int64_t value);
 
 /* Per-kernel times of launches issued while HS_OPT_TIMING was on, measured

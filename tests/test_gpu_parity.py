@@ -448,10 +448,11 @@ def test_wide_launch_copies_multi_piece_rows(hs, w):
 
 @pytest.mark.parametrize("wgs", [0, -1], ids=["fetch_launch", "split_units"])
 def test_instrumentation_changes_nothing(hs, wgs):
-    """Per-launch timing and phase stamps on: results still equal the oracle
-    bit for bit, every launch is counted (no fetch launch when units copy
-    their own misses), and each request-layer's stamps (taken by the first
-    wave of its lead workgroup, in program order) never go backwards."""
+    """Per-launch timing, phase stamps and roctx ranges on: results still
+    equal the oracle bit for bit, every launch is counted (no fetch launch
+    when units copy their own misses), and each request-layer's stamps (taken
+    by the first wave of its lead workgroup, in program order) never go
+    backwards."""
     from oracle import Oracle
     w = wl("instrumented", num_req=4, num_layers=2, B=1024, k=512, L_ctx=20000, W_KV=8, steps=6)
     tr = tg.trace(w)
@@ -460,6 +461,7 @@ def test_instrumentation_changes_nothing(hs, wgs):
     res = make_resolver(hs, w, pool)
     res.set_option(hs.HS_OPT_TIMING, 1)
     res.set_option(hs.HS_OPT_PHASE_TRACE, 1)
+    res.set_option(hs.HS_OPT_MARKERS, 1)   # the image ships the profiler's marker library
     res.set_option(hs.HS_OPT_META_WGS, wgs)
     o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes)
     dev = torch.device("cuda:0")
@@ -488,6 +490,7 @@ def test_instrumentation_changes_nothing(hs, wgs):
     assert res.error()[0] == 0
     res.set_option(hs.HS_OPT_PHASE_TRACE, 0)
     res.set_option(hs.HS_OPT_TIMING, 0)
+    res.set_option(hs.HS_OPT_MARKERS, 0)
     res.close()
     pool.free()
 
