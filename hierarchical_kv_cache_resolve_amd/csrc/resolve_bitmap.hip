@@ -24,6 +24,8 @@
 // Determinism: victims are the m candidate slots with the smallest
 // (stamp, slot) keys, assigned in ascending slot order to the misses in
 // ascending selection order, whatever the order in which waves run.
+#include <type_traits>
+
 #include "hs_device.h"
 
 namespace hs {
@@ -329,6 +331,60 @@ __device__ inline void copy_misses(const StateBase& s, const int* mpos, const in
     }
 }
 
+// The victim threshold of a unit with misses (the kernel's step 4, in the
+// kernel's own variables): the age histogram unless built speculatively, its
+// crossing bin or the radix select, the strict and tied victim bits and
+// their packed scan.
+#define HB_FIND_THRESHOLD()                                                                   \
+    do {                                                                                      \
+        if (!spec) {                                                                          \
+        _Pragma("unroll")                                                                     \
+            for (int q = 0; q < PER; ++q) {                                                   \
+                int bin = -1;                                                                 \
+                if ((candbits >> q) & 1u) {                                                   \
+                    const uint32_t age = 2u * t - tsv[q];                                     \
+                    bin = age < kHistBins - 1 ? static_cast<int>(age) : kHistBins - 1;        \
+                }                                                                             \
+                hist_add(hist, bin);                                                          \
+            }                                                                                 \
+            __syncthreads();                                                                  \
+        }                                                                                     \
+        const int ncand = B - h;                                                              \
+        if (m == ncand) {                                                                     \
+            T = 0xFFFFFFFFu; /* every candidate is a victim (stamps never reach this value) */\
+        } else {                                                                              \
+            int bin, below;                                                                   \
+            crossing_from_top(hist, m, bin, below);                                           \
+            if (bin < kHistBins - 1) {                                                        \
+                T = 2u * t - static_cast<uint32_t>(bin);                                      \
+                need_eq = m - below;                                                          \
+            } else {                                                                          \
+                /* All m victims are at least 1023 ages old: select among those               \
+                   with a radix select on their stamps (hist must start at zero). */          \
+                __syncthreads();                                                              \
+                for (int i = tid; i < kHistBins; i += NT) hist[i] = 0;                        \
+                unsigned old_bits = 0;                                                        \
+        _Pragma("unroll")                                                                     \
+                for (int q = 0; q < PER; ++q)                                                 \
+                    if (((candbits >> q) & 1u) &&                                             \
+                        2u * t - tsv[q] >= static_cast<uint32_t>(kHistBins - 1))              \
+                        old_bits |= 1u << q;                                                  \
+                __syncthreads();                                                              \
+                radix_select<NT, PER>(hist, misc, tsv, old_bits, m, T, need_eq);              \
+            }                                                                                 \
+        }                                                                                     \
+        _Pragma("unroll")                                                                     \
+        for (int q = 0; q < PER; ++q) {                                                       \
+            const bool cand = (candbits >> q) & 1u;                                           \
+            strict_bits |= static_cast<unsigned>(cand && tsv[q] < T) << q;                    \
+            tie_bits |= static_cast<unsigned>(cand && tsv[q] == T) << q;                      \
+        }                                                                                     \
+        packed = __popc(strict_bits) | (__popc(tie_bits) << 16);                              \
+        vincl = wave_incl_scan(packed);                                                       \
+        if (lane == 63) misc[X_VICT + wave] = vincl;                                          \
+        HB_PHASE(4);                                                                          \
+    } while (0)
+
 // LDS layout (ints): region 1 -- bitmap [4*NG words as NG 16-byte groups],
 // 16-bit rank of each word [4*NG halves], slot by rank [k] with a spare word
 // per lane [64], then victim slot by victim rank [k] and evicted position by
@@ -362,6 +418,16 @@ __device__ inline void copy_misses(const StateBase& s, const int* mpos, const in
 // its selections up, lists each miss's position by rank (two barriers),
 // issues its first host loads, and only then finds the threshold and victim
 // counts (one barrier) before the victim lists and B5.
+// a split unit's first host piece of each lane, loaded before its victims are
+// found, and its share of the flat (row, piece) space of the unit's misses
+struct SplitEarly {
+    u32x4 v;
+    int i, off;  // miss row (by rank; -1: none) and piece of the loaded piece
+    int i0;      // this lane's first miss (by rank)
+    int c_begin, c_end;
+};
+struct NoSplitEarly {};
+
 template <int NT, int SPL, int PER, bool VEC, bool WIDE, bool SPLIT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WIDE ? (NT == 512 ? 8 : 6) : 1)))
 void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
@@ -567,55 +633,9 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     uint32_t T = 0;
     int need_eq = 0, packed = 0, vincl = 0;
     unsigned strict_bits = 0, tie_bits = 0;
-    auto find_threshold = [&]() {
-        if (!spec) {
-#pragma unroll
-            for (int q = 0; q < PER; ++q) {
-                int bin = -1;
-                if ((candbits >> q) & 1u) {
-                    const uint32_t age = 2u * t - tsv[q];
-                    bin = age < kHistBins - 1 ? static_cast<int>(age) : kHistBins - 1;
-                }
-                hist_add(hist, bin);
-            }
-            __syncthreads();
-        }
-        const int ncand = B - h;
-        if (m == ncand) {
-            T = 0xFFFFFFFFu;  // every candidate is a victim (stamps never reach this value)
-        } else {
-            int bin, below;
-            crossing_from_top(hist, m, bin, below);
-            if (bin < kHistBins - 1) {
-                T = 2u * t - static_cast<uint32_t>(bin);
-                need_eq = m - below;
-            } else {
-                // All m victims are at least 1023 ages old: select among those
-                // with a radix select on their stamps (hist must start at zero).
-                __syncthreads();
-                for (int i = tid; i < kHistBins; i += NT) hist[i] = 0;
-                unsigned old_bits = 0;
-#pragma unroll
-                for (int q = 0; q < PER; ++q)
-                    if (((candbits >> q) & 1u) &&
-                        2u * t - tsv[q] >= static_cast<uint32_t>(kHistBins - 1))
-                        old_bits |= 1u << q;
-                __syncthreads();
-                radix_select<NT, PER>(hist, misc, tsv, old_bits, m, T, need_eq);
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            const bool cand = (candbits >> q) & 1u;
-            strict_bits |= static_cast<unsigned>(cand && tsv[q] < T) << q;
-            tie_bits |= static_cast<unsigned>(cand && tsv[q] == T) << q;
-        }
-        packed = __popc(strict_bits) | (__popc(tie_bits) << 16);
-        vincl = wave_incl_scan(packed);
-        if (lane == 63) misc[X_VICT + wave] = vincl;
-        HB_PHASE(4);
-    };
-    if (!SPLIT && m > 0) find_threshold();
+    if constexpr (!SPLIT) {
+        if (m > 0) HB_FIND_THRESHOLD();
+    }
     __syncthreads();
     if constexpr (!SPLIT) HB_PHASE(5);
 
@@ -713,14 +733,14 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     // the unit's flat (row, piece) space of misses are loaded from the host
     // into registers now; the victim slots they go to are found meanwhile
     // (one piece a lane, as in the copy: with every workgroup of a launch
-    // loading, that is already megabytes in flight, and two measured slower)
-    constexpr int kEarly = 1;
-    int i0 = 0, c_begin = 0, c_end = 0;
-    u32x4 ev[kEarly];
-    int ei[kEarly], eoff[kEarly];
+    // loading, that is already megabytes in flight, and two measured slower;
+    // the state exists in split builds only, so the others keep their
+    // registers)
+    std::conditional_t<SPLIT, SplitEarly, NoSplitEarly> early;
     if constexpr (SPLIT) {
         __syncthreads();  // miss counts visible; every read of the slot by rank done
-        i0 = mincl - mc + sum_before(misc + X_MISS, wave);
+        const int i0 = mincl - mc + sum_before(misc + X_MISS, wave);
+        early.i0 = i0;
         int* const mpos = byrank;
         {
             int i = i0;
@@ -735,23 +755,20 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         __syncthreads();  // every miss's position is listed
         const int row16 = static_cast<int>(s.row_bytes >> 4);
         const int total = m * row16;
-        c_begin = static_cast<int>(static_cast<int64_t>(total) * g / G);
-        c_end = static_cast<int>(static_cast<int64_t>(total) * (g + 1) / G);
+        early.c_begin = static_cast<int>(static_cast<int64_t>(total) * g / G);
+        early.c_end = static_cast<int>(static_cast<int64_t>(total) * (g + 1) / G);
         const uint8_t* src_base = s.pool + s.region_row[static_cast<int64_t>(r) * s.NL + layer] * s.row_bytes;
-#pragma unroll
-        for (int x = 0; x < kEarly; ++x) {
-            const int c = c_begin + tid + x * NT;
-            ei[x] = -1;
-            eoff[x] = 0;
-            if (c < c_end) {
-                const int i = c / row16, off = c - i * row16;
-                const u32x4* src = reinterpret_cast<const u32x4*>(src_base + static_cast<int64_t>(mpos[i]) * s.row_bytes) + off;
-                ei[x] = i;
-                eoff[x] = off;
-                ev[x] = lb.nt ? ld16<true>(src) : ld16<false>(src);
-            }
+        const int c = early.c_begin + tid;
+        early.i = -1;
+        early.off = 0;
+        if (c < early.c_end) {
+            const int i = c / row16, off = c - i * row16;
+            const u32x4* src = reinterpret_cast<const u32x4*>(src_base + static_cast<int64_t>(mpos[i]) * s.row_bytes) + off;
+            early.i = i;
+            early.off = off;
+            early.v = lb.nt ? ld16<true>(src) : ld16<false>(src);
         }
-        find_threshold();
+        HB_FIND_THRESHOLD();
         __syncthreads();  // victim counts visible
         HB_PHASE(5);
     }
@@ -795,8 +812,8 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
 
     // 6. the i-th miss (ascending selection index) takes the victim of rank i
     // (ascending slot): plan entry, page table, slot map and publication
-    if constexpr (!SPLIT) i0 = mincl - mc + sum_before(misc + X_MISS, wave);  // this lane's first miss
     if constexpr (!SPLIT) {
+        const int i0 = mincl - mc + sum_before(misc + X_MISS, wave);  // this lane's first miss
         int32_t* pt = s.page_table + rl * s.L_ctx;
         int4* plan = s.plan + rl * B;
         int i = i0;
@@ -829,6 +846,7 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         HB_PHASE(10);
         HB_PHASE_FLUSH();
     } else {
+        const int i0 = early.i0;  // this lane's first miss
         // the lead publishes the misses' slots
         if (lead) {
             int i = i0;
@@ -854,17 +872,14 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
             // that is megabytes in flight, and more per lane measured slower
             // over the host link)
             uint8_t* dst_base = s.cache + rl * s.B * s.row_bytes;
-#pragma unroll
-            for (int x = 0; x < kEarly; ++x) {
-                if (ei[x] >= 0) {
-                    u32x4* dst = reinterpret_cast<u32x4*>(dst_base + static_cast<int64_t>(vlist[ei[x]]) * s.row_bytes) + eoff[x];
-                    if (lb.nt) st16<true>(dst, ev[x]);
-                    else st16<false>(dst, ev[x]);
-                }
+            if (early.i >= 0) {
+                u32x4* dst = reinterpret_cast<u32x4*>(dst_base + static_cast<int64_t>(vlist[early.i]) * s.row_bytes) + early.off;
+                if (lb.nt) st16<true>(dst, early.v);
+                else st16<false>(dst, early.v);
             }
-            const int c_rest = min(c_end, c_begin + kEarly * NT);
-            if (lb.nt) copy_misses<NT, true, 1>(s, byrank, vlist, rl, r, layer, c_rest, c_end);
-            else copy_misses<NT, false, 1>(s, byrank, vlist, rl, r, layer, c_rest, c_end);
+            const int c_rest = min(early.c_end, early.c_begin + NT);
+            if (lb.nt) copy_misses<NT, true, 1>(s, byrank, vlist, rl, r, layer, c_rest, early.c_end);
+            else copy_misses<NT, false, 1>(s, byrank, vlist, rl, r, layer, c_rest, early.c_end);
         }
         // the last workgroup to arrive writes the new metadata
         if (tid == 0) misc[X_LAST] = arrived_before == static_cast<unsigned>(G - 1) ? 1 : 0;
