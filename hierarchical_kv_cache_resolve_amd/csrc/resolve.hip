@@ -902,14 +902,17 @@ int plan_wgs(const StateBase& s, const LayerBatch& lb, int asked) {
     // by launch size.  A split unit copies only its own misses, so the units
     // with the most misses set the end of the launch, where the fetch kernel
     // spreads all of a launch's misses evenly over the chip: measured, the
-    // split launch saves about 2 us a layer where a layer's misses are a few
-    // MB (16 requests of 1152-byte records: 0.796 against 0.810 ms a step of
-    // 8 layers) and loses 2 % where they are tens of MB (64 requests of 4 KB
-    // records).  Split only launches whose misses cannot exceed 64 MB, into
-    // about 256 workgroups so the copy spreads over the chip.
+    // split launch saves time where a layer's misses are a few MB (16
+    // requests of 1152-byte records) and loses 2 % where they are tens of MB
+    // (64 requests of 4 KB records).  Split only launches whose misses cannot
+    // exceed 64 MB, into about 64 workgroups: fewer, longer copiers than one
+    // per CU kept the host link busier (workgroups per unit measured at
+    // 16 requests x 8 layers of 1152-byte records: 0.753 ms a step at 2-4,
+    // 0.782 at 16, 0.812 at 32; 18 KB records 0.715 at 3-4 against 0.749 at
+    // 16; 8 requests 0.420 at 4-8 against 0.456 at 32).
     const int units = s.R * lb.n;
     if (static_cast<int64_t>(units) * lb.k * s.row_bytes > (static_cast<int64_t>(64) << 20)) return 0;
-    return std::min(32, (256 + units - 1) / units);
+    return std::max(1, std::min(32, (64 + units - 1) / units));
 }
 
 bool plan_copies_misses(const StateBase& s, const LayerBatch& lb) {

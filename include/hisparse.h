@@ -238,7 +238,7 @@ int hisparse_reset(hisparse_t h);
                                 /* no fetch launch follows: G in 1..HS_MAX_META_WGS, 0 for one    */
                                 /* workgroup and a separate fetch launch, -1 to choose by launch  */
                                 /* size (default: split when the launch's misses cannot exceed    */
-                                /* 64 MB, into about 256 workgroups; larger launches keep the     */
+                                /* 64 MB, into about 64 workgroups; larger launches keep the      */
                                 /* fetch launch, which balances the copy over all requests; so do */
                                 /* layers that have been prefetch anchors, whose plan the shared  */
                                 /* layers' replay then gets before the anchor's own copy).        */
