@@ -72,7 +72,8 @@ def parse():
     ap.add_argument("--no-hit-only", action="store_true")
     ap.add_argument("--no-probes", action="store_true")
     ap.add_argument("--markers", action="store_true",
-                    help="roctx range around every library call that enqueues work (rocprofv3 --marker-trace)")
+                    help="roctx ranges around each timed step (eager steps with --graph 0, else the graph) and "
+                         "every library call that enqueues work (rocprofv3 --marker-trace)")
     ap.add_argument("--probe", default="default", choices=["default", "page_table", "slot_scan", "slot_scan_hash"],
                     help="how the metadata kernel finds hits (default: the library's)")
     ap.add_argument("--meta-lanes", type=int, default=0, choices=[0, 512, 1024],
@@ -174,16 +175,20 @@ def main():
 
     step = make_step(res, w, sel, out, consume, side, use_prefetch)
 
+    mark = roctx_ranges(args.markers)
+
     def timed_run(prefetch):
         """Run steps W..W+K-1 (as one captured graph unless --graph 0); returns seconds."""
         if args.graph:
             # the timed steps as one HIP graph: every input already resident,
             # every pointer fixed, the step clock on the device
-            return graph_time(torch, step, W, W + K, prefetch)
+            with mark(f"timed steps {W}..{W + K - 1} (one graph)"):
+                return graph_time(torch, step, W, W + K, prefetch)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for t in range(W, W + K):
-            step(t, sptr, prefetch=prefetch)
+            with mark(f"step {t}"):
+                step(t, sptr, prefetch=prefetch)
         torch.cuda.synchronize()
         return time.perf_counter() - t0
 
@@ -375,6 +380,36 @@ def main():
                 if "prefetch" in row:
                     result["prefetch"] = row["prefetch"]
     print(json.dumps(result), flush=True)
+
+
+def roctx_ranges(on):
+    """A context manager factory: with `on`, each `with mark(name)` is one roctx
+    range (the profiler's marker library, recorded by rocprofv3
+    --marker-trace); otherwise it does nothing."""
+    import contextlib
+    import ctypes
+    lib = None
+    if on:
+        for name in ("librocprofiler-sdk-roctx.so.1", "librocprofiler-sdk-roctx.so"):
+            try:
+                lib = ctypes.CDLL(name)
+                break
+            except OSError:
+                pass
+        if lib is None:
+            raise SystemExit("--markers: the roctx library (librocprofiler-sdk-roctx) cannot be loaded")
+        lib.roctxRangePushA.argtypes = [ctypes.c_char_p]
+
+    @contextlib.contextmanager
+    def mark(name):
+        if lib is not None:
+            lib.roctxRangePushA(name.encode())
+        try:
+            yield
+        finally:
+            if lib is not None:
+                lib.roctxRangePop()
+    return mark
 
 
 def make_step(res, w, sel, out, consume, side, default_prefetch):
