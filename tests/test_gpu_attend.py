@@ -96,10 +96,11 @@ def run_attend(hs, res, layer, q_np, slot_idx, scale, dev):
 
 @pytest.mark.parametrize("heads_per_wg", [0, 32, 64])
 def test_attend_after_resolve_ragged(hs, heads_per_wg):
-    """k from 1 to 1000 (ragged sub-chunks and chunks), 64 and 128 heads, two
-    scales, with the head grouping chosen by shape and forced to 32 and to 64
-    heads a workgroup."""
-    w = tg.Workload("attend", 3, 2, 8192, 576, 2, 1000, 1024, 8, tg.LOCALITY, 0.8, seed_index=61)
+    """k from 1 to 1000 (ragged sub-chunks and chunks), 64 to 1024 heads (192
+    and 320: three and five groups of 64, grids that do not divide into the
+    eight XCDs), two scales, with the head grouping chosen by shape and forced
+    to 32 and to 64 heads a workgroup."""
+    w = tg.Workload("attend", 3, 2, 8192, 576, 2, 1000, 1024, 11, tg.LOCALITY, 0.8, seed_index=61)
     sel_all = tg.trace(w)
     pool = keep(make_pool(hs, w))
     pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
@@ -108,7 +109,8 @@ def test_attend_after_resolve_ragged(hs, heads_per_wg):
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(7)
     cases = [(1, 64, 0.0417), (37, 128, 0.25), (64, 64, 0.0417), (65, 128, 0.0417), (200, 64, 0.25),
-             (513, 64, 0.25), (777, 128, 0.0417), (1000, 128, 0.0417)]
+             (513, 64, 0.25), (777, 128, 0.0417), (1000, 128, 0.0417), (150, 192, 0.0417), (333, 320, 0.25),
+             (97, 1024, 0.0417)]
     for t, (k, H, scale) in enumerate(cases):
         for l in range(w.num_layers):
             sel = np.ascontiguousarray(sel_all[t, l, :, :k])
