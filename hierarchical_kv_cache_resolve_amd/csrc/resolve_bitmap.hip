@@ -736,10 +736,8 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
     // by rank, read by nobody any more) and this workgroup's first pieces of
     // the unit's flat (row, piece) space of misses are loaded from the host
     // into registers now; the victim slots they go to are found meanwhile
-    // (one piece a lane, as in the copy: with every workgroup of a launch
-    // loading, that is already megabytes in flight, and two measured slower;
-    // the state exists in split builds only, so the others keep their
-    // registers)
+    // (kSplitEarly pieces a lane, as in the copy; the state exists in split
+    // builds only, so the others keep their registers)
     std::conditional_t<SPLIT, SplitEarly, NoSplitEarly> early;
     if constexpr (SPLIT) {
         __syncthreads();  // miss counts visible; every read of the slot by rank done
@@ -874,10 +872,9 @@ void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
         if (tid == 0) arrived_before = atomicAdd(&s.arrive[rl], 1u);
         {
             // the pieces loaded early go to their victim slots, then the rest
-            // of this workgroup's share (one host load a lane in flight, as in
-            // the fetch kernel: with every workgroup of the launch copying,
-            // that is megabytes in flight, and more per lane measured slower
-            // over the host link)
+            // of this workgroup's share, one host load a lane in flight as in
+            // the fetch kernel (about a megabyte over the launch's ~64
+            // workgroups; more per lane measured slower over the host link)
             uint8_t* dst_base = s.cache + rl * s.B * s.row_bytes;
 #pragma unroll
             for (int x = 0; x < kSplitEarly; ++x) {
