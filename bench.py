@@ -38,11 +38,24 @@ def fetch_traffic(workload="mla_latent"):
     """Scaled FETCH_SIZE + WRITE_SIZE bytes per fetch_kernel launch of a
     workload from its committed counter summary, or None if there is none or
     the kernel source changed since it was taken."""
+    return counter_traffic(os.path.join("profiles", f"fetch_kernel_traffic_{workload}.md"), "fetch.hip")
+
+
+def attention_traffic():
+    """Scaled FETCH_SIZE + WRITE_SIZE bytes of one MLA attention call (partial
+    and combine kernels) at 16 requests x 128 heads x k = 2048, from the
+    committed counter summary, or None if the kernels' source changed since."""
+    return counter_traffic(os.path.join("profiles", "mla_attention_mla_latent.md"), "attend.hip")
+
+
+def counter_traffic(rel, source):
+    """The `| read (scaled FETCH_SIZE) | N |` and `| written (scaled
+    WRITE_SIZE) | N |` rows of a counter summary, if the summary names the
+    current sha256 prefix of the measured source file."""
     import hashlib
     import re
-    rel = os.path.join("profiles", f"fetch_kernel_traffic_{workload}.md")
     prof = os.path.join(ROOT, rel)
-    src = os.path.join(ROOT, "hierarchical_kv_cache_resolve_amd", "csrc", "fetch.hip")
+    src = os.path.join(ROOT, "hierarchical_kv_cache_resolve_amd", "csrc", source)
     try:
         text = open(prof).read()
         digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
@@ -500,13 +513,18 @@ def attention_leg(hs, torch, res, w, out, heads, dev, hbm_peak, iters=20, heads_
     tflops = flops / (us * 1e-6) / 1e12
     gbps = io_bytes / (us * 1e-6) / 1e9
     log(f"attention: {us:.1f} us per layer ({tflops:.0f} TFLOP/s, {gbps:.0f} GB/s of records+q+out)")
+    # counter traffic is summarised for the benchmark's own shape only
+    tr = (attention_traffic() if (w.num_req, heads, w.k, w.row_bytes, heads_per_wg) == (16, 128, 2048, 1152, 0)
+          else None)
+    if tr:
+        tr["over_algorithmic"] = tr["total_bytes"] / io_bytes
     return {"kernels": "mla_partial_kernel + mla_combine_kernel", "heads": heads, "k": w.k,
             "heads_per_workgroup": heads_per_wg or "by shape",
             "requests": w.num_req, "us_per_layer": us, "TFLOPs": tflops,
             "mfma_frac": tflops / MFMA_BF16_TFLOPS, "algorithmic_GBps": gbps,
             "hbm_frac_published": gbps / HBM_PEAK_GBPS,
             "hbm_frac_measured_copy": gbps / hbm_peak if hbm_peak else None,
-            "algorithmic_bytes": io_bytes, "flops": flops}
+            "algorithmic_bytes": io_bytes, "flops": flops, "traffic": tr}
 
 
 def hit_only_leg(hs, tg, torch, w, dev, sptr, hbm_peak, steps=64, meta_lanes=0, meta_wgs=None):

@@ -76,3 +76,30 @@ def test_traffic_summary_of_each_workload_parses():
             assert t["source"] == f"profiles/fetch_kernel_traffic_{name}.md"
             assert t["read_bytes"] > 0 and t["write_bytes"] > 0
     assert bench.fetch_traffic("no_such_workload") is None
+
+
+def test_attention_traffic_is_tied_to_the_consumer_source(tmp_path, monkeypatch):
+    """The consumer's counter traffic comes from its summary's table while
+    the summary names the current consumer source, and is dropped otherwise."""
+    import hashlib
+    import re
+    sys.path.insert(0, ROOT)
+    import bench
+    prof = open(os.path.join(ROOT, "profiles", "mla_attention_mla_latent.md")).read()
+    src = open(os.path.join(ROOT, "hierarchical_kv_cache_resolve_amd", "csrc", "attend.hip"), "rb").read()
+    for sha in (hashlib.sha256(src).hexdigest()[:16], "0" * 16):
+        tree = tmp_path / sha
+        (tree / "profiles").mkdir(parents=True)
+        (tree / "profiles" / "mla_attention_mla_latent.md").write_text(
+            re.sub(r"sha256 prefix [0-9a-f]{16}", f"sha256 prefix {sha}", prof))
+        (tree / "hierarchical_kv_cache_resolve_amd" / "csrc").mkdir(parents=True)
+        (tree / "hierarchical_kv_cache_resolve_amd" / "csrc" / "attend.hip").write_bytes(src)
+        monkeypatch.setattr(bench, "ROOT", str(tree))
+        t = bench.attention_traffic()
+        if sha == "0" * 16:
+            assert t is None
+        else:
+            rd = int(re.search(r"\| read \(scaled FETCH_SIZE\) \| (\d+) \|", prof).group(1))
+            wr = int(re.search(r"\| written \(scaled WRITE_SIZE\) \| (\d+) \|", prof).group(1))
+            assert t == {"read_bytes": rd, "write_bytes": wr, "total_bytes": rd + wr,
+                         "source": "profiles/mla_attention_mla_latent.md"}
