@@ -95,6 +95,8 @@ def parse():
                     help="workgroups per (request, layer) that plan alike and copy their misses (0: a separate "
                          "fetch launch, -1: by launch size; default: the library's)")
     ap.add_argument("--fetch-blocks", type=int, default=0)
+    ap.add_argument("--prefetch-blocks", type=int, default=None,
+                    help="workgroups of the prefetch's side-stream copy launch (default: the library's)")
     ap.add_argument("--unroll", type=int, default=0)
     ap.add_argument("--coherent", action="store_true")
     ap.add_argument("--timing", type=int, default=1, help="replay the timed steps with HIP events on every launch")
@@ -159,6 +161,8 @@ def main():
         res.set_option(hs.HS_OPT_ATTN_HEADS, args.attn_heads_per_wg)
     if args.fetch_blocks:
         res.set_option(hs.HS_OPT_FETCH_BLOCKS, args.fetch_blocks)
+    if args.prefetch_blocks is not None:
+        res.set_option(hs.HS_OPT_PREFETCH_BLOCKS, args.prefetch_blocks)
     if args.meta_lanes:
         res.set_option(hs.HS_OPT_META_LANES, args.meta_lanes)
     if args.meta_wgs is not None:

@@ -30,6 +30,7 @@ HS_OPT_ATTN_HEADS = 7
 HS_OPT_META_LANES = 8
 HS_OPT_META_WGS, HS_MAX_META_WGS = 9, 64
 HS_OPT_MARKERS = 10
+HS_OPT_PREFETCH_BLOCKS = 11
 HS_PROBE_PAGE_TABLE, HS_PROBE_SLOT_SCAN, HS_PROBE_SLOT_SCAN_HASH = 0, 1, 2
 
 _ERR_NAMES = {v: k for k, v in dict(HS_E_INVAL=-1, HS_E_HANDLE=-2, HS_E_LAYER=-3, HS_E_K=-4, HS_E_ALIGN=-5,

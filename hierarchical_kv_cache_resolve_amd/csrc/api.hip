@@ -29,6 +29,7 @@ struct hisparse_ctx {
     int64_t* d_region_row = nullptr;
     // tuning
     int fetch_blocks = 1024;
+    int prefetch_blocks = 0;  // workgroups of the prefetch's copy launch: 0 = fetch_blocks
     int unroll = 4;
     bool nt = true;
     bool timing = false;
@@ -563,7 +564,8 @@ int hisparse_prefetch(hisparse_t h, int anchor, const int* shared, int n, void* 
     int rc = timed(h, K_REPLAY, side, [&] {
         hipError_t e = hs::launch_replay_meta(h->s, rb, side);
         if (e != hipSuccess) return e;
-        return hs::launch_fetch(h->s, fb, h->fetch_blocks, h->unroll, h->nt, side);
+        return hs::launch_fetch(h->s, fb, h->prefetch_blocks ? h->prefetch_blocks : h->fetch_blocks, h->unroll,
+                                h->nt, side);
     });
     if (rc != HS_OK) return rc;
     HS_TRY(hipEventRecord(h->ev_join[anchor], side));
@@ -705,6 +707,10 @@ int hisparse_set_option(hisparse_t h, int key, int64_t value) {
         case HS_OPT_FETCH_BLOCKS:
             if (value < 1 || value > 65536) return HS_E_INVAL;
             h->fetch_blocks = static_cast<int>(value);
+            return HS_OK;
+        case HS_OPT_PREFETCH_BLOCKS:
+            if (value < 0 || value > 65536) return HS_E_INVAL;
+            h->prefetch_blocks = static_cast<int>(value);
             return HS_OK;
         case HS_OPT_FETCH_UNROLL:
             if (value != 1 && value != 2 && value != 4 && value != 8) return HS_E_INVAL;

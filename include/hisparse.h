@@ -253,6 +253,9 @@ int hisparse_reset(hisparse_t h);
                                 /* traces (rocprofv3 --marker-trace); the ranges mark when a call */
                                 /* enqueues, not when its kernels run.  HS_E_INVAL if the marker  */
                                 /* library (librocprofiler-sdk-roctx) cannot be opened.           */
+#define HS_OPT_PREFETCH_BLOCKS 11 /* workgroups of hisparse_prefetch's copy launch, which runs on  */
+                                /* the side stream beside the main stream's work: 1..65536, or 0  */
+                                /* (default) for the fetch kernel's HS_OPT_FETCH_BLOCKS.          */
 int hisparse_set_option(hisparse_t h, int key, int64_t value);
 
 /* Per-kernel times of launches issued while HS_OPT_TIMING was on, measured

@@ -37,17 +37,23 @@ def run_step_prefetch(res, w, sel_t, out, main, side):
             res.resolve(l, sel_t[l], out[l], main)
 
 
-@pytest.mark.parametrize("w", [
-    tg.PREFETCH.replace(name="prefetch_small", num_req=3, L_ctx=20000, k=512, B=1024, steps=12),
-    tg.PREFETCH.replace(name="prefetch_mid", num_req=8, L_ctx=120000, k=2048, B=4096, steps=8, W_KV=64),
-], ids=lambda w: w.name)
-def test_prefetch_equals_no_prefetch_equals_oracle(hs, w):
+SMALL = tg.PREFETCH.replace(name="prefetch_small", num_req=3, L_ctx=20000, k=512, B=1024, steps=12)
+MID = tg.PREFETCH.replace(name="prefetch_mid", num_req=8, L_ctx=120000, k=2048, B=4096, steps=8, W_KV=64)
+
+
+@pytest.mark.parametrize("w,copy_wgs", [(SMALL, 0), (MID, 0), (SMALL, 3)],
+                         ids=["prefetch_small", "prefetch_mid", "prefetch_small_3_copy_wgs"])
+def test_prefetch_equals_no_prefetch_equals_oracle(hs, w, copy_wgs):
+    """copy_wgs: workgroups of the replay's copy launch (0: the default grid;
+    3 makes every copying workgroup loop over many rounds of misses)."""
     from oracle import Oracle
-    print(f"[prefetch] {w.name} R={w.num_req} layers={w.num_layers} group={w.group} k={w.k} B={w.B}", flush=True)
+    print(f"[prefetch] {w.name} R={w.num_req} layers={w.num_layers} group={w.group} k={w.k} B={w.B} "
+          f"copy_wgs={copy_wgs}", flush=True)
     tr = tg.trace(w)
     pool = make_pool(hs, w)
     pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
     on = make_resolver(hs, w, pool)
+    on.set_option(hs.HS_OPT_PREFETCH_BLOCKS, copy_wgs)
     off = make_resolver(hs, w, pool)
     o = Oracle(w.num_req, w.num_layers, w.B, w.L_ctx, w.row_bytes, model_bytes=True)
     dev = torch.device("cuda:0")
