@@ -23,7 +23,7 @@
 // piece 8L + (j ^ swz(rec)).  One global_load_lds moves whole lines of 8
 // records (8 lanes a line, so every access is a full coalesced line), a lane
 // loads the same record(s) for the whole sub-chunk, and the XOR swizzle
-// spreads both operand reads below over the LDS banks:
+// keeps both operand reads below free of bank conflicts:
 //   scores  wave w: S^T = K Q^T for one tile of 16 heads over 32 of the
 //           sub-chunk's 64 records (two waves share a tile)
 //           (v_mfma_f32_16x16x32_bf16, K from
@@ -87,16 +87,16 @@ constexpr int kVDepth = 3;                     // value tiles read ahead
 __device__ __align__(16) uint4 g_zero_record[kRecPieces];
 
 // slot of piece p%8 inside line p/8 of LDS record rec is (p%8) ^ swz(rec).
-// swz takes record bits 1..3: records 2i and 2i+1 share an XOR and lie in
-// the two 128-byte halves of a 256-byte row of LDS banks, so 16 consecutive
-// records read at one piece fall on 16 distinct 16-byte bank groups; it
-// depends only on the record's place in its tile of 16, which the
-// precomputed read offsets below rely on.  Of the swizzles measured it gave
-// the fastest kernel (partial kernel at 16 requests x 128 heads: 20.2 us,
-// against 20.4 with bits 0..2, 21.9 with bits {1,2,3} onto slot bits
-// {1,2,0}, 25.4 with none); the bank-conflict counter still reads about 15 %
-// of the kernel's LDS-active cycles.
-__device__ __forceinline__ int swz(int rec) { return (rec >> 1) & 7; }
+// swz takes record bits 0..2, so it depends only on the record's place in
+// its tile of 16, which the precomputed read offsets below rely on.  Both
+// operand reads are then free of bank conflicts (bank-conflict counter of a
+// probe replaying their lane addresses: a 16-byte score read takes 4 LDS
+// cycles a wave, a transposing 8-byte value read 2; with record bits 1..3 the
+// value read took 4, with bits {1,2,3} onto slot bits {1,2,0} the score read
+// took 8).  Partial kernel at 16 requests x 128 heads, five interleaved runs
+// on one box: 20.1 us against 20.5 with bits 1..3 (and 21.9 with bits
+// {1,2,3} onto slot bits {1,2,0}, 25.4 with none, in an earlier comparison).
+__device__ __forceinline__ int swz(int rec) { return rec & 7; }
 
 // This wave's share of line L of one sub-chunk, HBM -> LDS: NR groups of 8
 // records (records 8NR·w .. 8NR·w + 8NR - 1; NR = 2 with 4 waves, 1 with 8),
