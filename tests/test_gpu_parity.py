@@ -90,6 +90,12 @@ def test_split_option_range(hs):
         with pytest.raises(hs.HisparseError):
             res.set_option(hs.HS_OPT_META_WGS, bad)
     res.set_option(hs.HS_OPT_META_WGS, hs.HS_MAX_META_WGS)
+    # the prefetch copy grid: 0 (the fetch grid) .. 65536 workgroups
+    for bad in (-1, 65537):
+        with pytest.raises(hs.HisparseError):
+            res.set_option(hs.HS_OPT_PREFETCH_BLOCKS, bad)
+    for ok in (0, 1, 65536):
+        res.set_option(hs.HS_OPT_PREFETCH_BLOCKS, ok)
     res.close()
     pool.free()
 
