@@ -105,9 +105,9 @@ class MarkRange {
 };
 }  // namespace
 
-// Scratch area of the no-allocation attention entry point: the fp32 split-k
-// partials of hisparse_attend_mla_noalloc live here instead of in a workspace
-// the handle allocates.  Each GPU the library runs on holds its own copy
+// Scratch area of the no-allocation attention entry point: the split-k
+// partials of hisparse_attend_mla_noalloc (fp16 outputs, fp32 maxima and sums)
+// live here instead of in a workspace the handle allocates.  Each GPU the library runs on holds its own copy
 // until the process ends.  In host code `scratch` names a host-side stand-in,
 // not the device copy: kernels and copies use the address that
 // hipGetSymbolAddress returns for the current device (scratch_ptr below).
