@@ -44,6 +44,8 @@ enum : int {
     X_BIN = 3,      // radix select: crossing bin of the current pass
     X_BELOW = 4,    // radix select: candidates below it
     X_LAST = 5,     // split unit: this workgroup arrived last
+    X_TBIN = 6,     // victim threshold: crossing bin found by wave 0
+    X_TBELOW = 7,   // victim threshold: candidates in the bins above it
     X_MISS = 16,    // [16] per-wave inclusive miss counts
     X_VICT = 32,    // [16] per-wave packed (strict | tie << 16) victim counts
     X_HIST = 48,    // [16] radix-scan partials
@@ -153,13 +155,12 @@ __device__ inline void bitmap_ranks(const unsigned* bits, const uint16_t* wrank,
 }
 
 // The age bin where the count taken from the oldest bin downwards first
-// reaches `need`, and the count of the bins above it.  Every wave computes it
-// on its own from the finished histogram (no barrier, no broadcast): lane i
-// sums the 16 bins [1008 - 16i, 1023 - 16i], one wave scan orders the lanes
-// from the top and a ballot finds the lane L where the count crosses `need`;
-// then lanes 0..15 take L's bins from the top down, one each, and a scan over
-// that row of 16 lanes finds the bin.  Requires 0 < need <= the histogram's
-// total.
+// reaches `need`, and the count of the bins above it, found by one wave from
+// the finished histogram: lane i sums the 16 bins [1008 - 16i, 1023 - 16i],
+// one wave scan orders the lanes from the top and a ballot finds the lane L
+// where the count crosses `need`; then lanes 0..15 take L's bins from the top
+// down, one each, and a scan over that row of 16 lanes finds the bin.
+// Requires 0 < need <= the histogram's total.
 __device__ inline void crossing_from_top(const int* hist, int need, int& bin, int& below) {
     const int lane = threadIdx.x & 63;
     const int lo = kHistBins - kHistQ * (lane + 1);
@@ -334,7 +335,10 @@ __device__ inline void copy_misses(const StateBase& s, const int* mpos, const in
 // The victim threshold of a unit with misses (the kernel's step 4, in the
 // kernel's own variables): the age histogram unless built speculatively, its
 // crossing bin or the radix select, the strict and tied victim bits and
-// their packed scan.
+// their packed scan.  Wave 0 alone finds the crossing bin and hands it to
+// the others through LDS (one more barrier): every wave finding it on its own
+// cost more issue slots than the barrier (per-layer launch of 64 request-
+// layers of 4 KB records: 11.9 against 12.3 us by events).
 #define HB_FIND_THRESHOLD()                                                                   \
     do {                                                                                      \
         if (!spec) {                                                                          \
@@ -354,7 +358,16 @@ __device__ inline void copy_misses(const StateBase& s, const int* mpos, const in
             T = 0xFFFFFFFFu; /* every candidate is a victim (stamps never reach this value) */\
         } else {                                                                              \
             int bin, below;                                                                   \
-            crossing_from_top(hist, m, bin, below);                                           \
+            if (wave == 0) {                                                                  \
+                crossing_from_top(hist, m, bin, below);                                       \
+                if (lane == 0) {                                                              \
+                    misc[X_TBIN] = bin;                                                       \
+                    misc[X_TBELOW] = below;                                                   \
+                }                                                                             \
+            }                                                                                 \
+            __syncthreads();                                                                  \
+            bin = misc[X_TBIN];                                                               \
+            below = misc[X_TBELOW];                                                           \
             if (bin < kHistBins - 1) {                                                        \
                 T = 2u * t - static_cast<uint32_t>(bin);                                      \
                 need_eq = m - below;                                                          \
