@@ -493,14 +493,17 @@ def attention_buffers(torch, w, heads, dev):
             "lse": torch.empty((w.num_req, heads), dtype=torch.float32, device=dev)}
 
 
-def attention_leg(hs, torch, res, w, out, heads, dev, hbm_peak, iters=20, heads_per_wg=0):
+def attention_leg(hs, torch, res, w, out, heads, dev, hbm_peak, iters=20, heads_per_wg=0, warm=20):
     """The consumer alone: sparse MLA decode attention over the slots the last
     timed step published, every layer, timed with HIP events on the stream
-    the kernels run on.  Algorithmic work per (request, layer): k records of
-    1152 B read once, heads x k x (576 + 512) multiply-adds."""
+    the kernels run on, after `warm` untimed passes over the layers (the
+    leg follows link-bound work, and the first few milliseconds of attention
+    after it run slower).  Algorithmic work per (request, layer): k records
+    of 1152 B read once, heads x k x (576 + 512) multiply-adds."""
     a = attention_buffers(torch, w, heads, dev)
-    for l in range(w.num_layers):
-        res.attend_mla(l, a["q"], out[l], a["scale"], a["o"], a["lse"])
+    for _ in range(warm):
+        for l in range(w.num_layers):
+            res.attend_mla(l, a["q"], out[l], a["scale"], a["o"], a["lse"])
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
