@@ -160,7 +160,7 @@ __device__ __forceinline__ float rows_sum(float x) {
 template <int HT, int W, int HPWS>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W / 4)))
 void mla_partial_kernel(StateBase s, int layer, const uint16_t* q, int H, const int32_t* slot_idx, int k, int chunk,
-                        int nchunk, float scale_log2, _Float16* part_o, float* part_ml) {
+                        int nchunk, float scale_log2, _Float16* part_o, float* part_ml, float* out, float* lse) {
     constexpr int HPW = 16 * HT;         // heads per workgroup
     constexpr int HG = HT / HPWS;        // head-tile groups of the score phase
     constexpr int RS = W / HG;           // waves sharing a group in the score phase
@@ -490,6 +490,44 @@ void mla_partial_kernel(StateBase s, int layer, const uint16_t* q, int H, const 
     } else {
         __syncthreads();
     }
+    if (nchunk == 1) {
+        // a single chunk: this workgroup's outputs are final -- fp32 rows
+        // normalised by the sum and the log-sum-exp go straight out, and no
+        // combine follows.  Rows of kDv floats (padded by 16 bytes) staged
+        // through both record buffers, idle now, two 16-byte stores a lane a row.
+        const int64_t obase = static_cast<int64_t>(r) * H + g * HPW;
+        if (grp == 0 && rh == 0) {
+#pragma unroll
+            for (int p = 0; p < HPWS; ++p) {
+                alpha_lds[(t0 + p) * 16 + n] = l_tot[p];
+                if (lse)
+                    lse[obase + (t0 + p) * 16 + n] =
+                        l_tot[p] > 0.f ? (m_run[p] + log2f(l_tot[p])) * 0.69314718055994530942f : -INFINITY;
+            }
+        }
+        __syncthreads();
+        constexpr int kFRow = 4 * kDv + 16;
+        static_assert(HPW * kFRow <= 2 * kBufBytes, "the fp32 outputs fit the two buffers");
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const float l = alpha_lds[ht * 16 + n];
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            uint8_t* orow = attn_lds + (ht * 16 + n) * kFRow + 4 * (wave * kDimsPerWave + 4 * grp);
+#pragma unroll
+            for (int dt = 0; dt < kWaveDTiles; ++dt) *reinterpret_cast<f32x4*>(orow + 64 * dt) = acc_o[dt][ht] * inv;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < HPW / W; ++i) {
+            const int row = wave * (HPW / W) + i;
+            float* orow = out + (obase + row) * kDv;
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+                *reinterpret_cast<uint4*>(orow + 4 * (lane + 64 * half)) =
+                    *reinterpret_cast<const uint4*>(attn_lds + row * kFRow + 16 * (lane + 64 * half));
+        }
+        return;
+    }
     const int64_t hbase = (static_cast<int64_t>(r) * nchunk + c) * H + g * HPW;
     if (grp == 0 && rh == 0) {
 #pragma unroll
@@ -630,10 +668,11 @@ hipError_t launch_attend_mla(const StateBase& s, int layer, const uint16_t* q, i
     const int nwg = nchunk * (H / (16 * ht)) * s.R;
     if (ht == 2)
         hipLaunchKernelGGL((mla_partial_kernel<2, 4, 1>), dim3(nwg), dim3(256), kAttnLds, st, s, layer, q, H, slot_idx,
-                           k, chunk, nchunk, scale_log2, part_o, part_ml);
+                           k, chunk, nchunk, scale_log2, part_o, part_ml, out, lse);
     else
         hipLaunchKernelGGL((mla_partial_kernel<4, 8, 1>), dim3(nwg), dim3(512), kAttnLds, st, s, layer, q, H, slot_idx,
-                           k, chunk, nchunk, scale_log2, part_o, part_ml);
+                           k, chunk, nchunk, scale_log2, part_o, part_ml, out, lse);
+    if (nchunk == 1) return hipGetLastError();  // the partial kernel wrote the final outputs
     hipLaunchKernelGGL(mla_combine_kernel, dim3((H + kCombineHeadsPerWg - 1) / kCombineHeadsPerWg, s.R),
                        dim3(64 * kCombineHeadsPerWg), 0, st, part_o, part_ml, H, nchunk, out,
                        lse);

@@ -230,6 +230,31 @@ def test_attend_full_size(hs, heads_per_wg):
 
 
 @pytest.mark.parametrize("heads_per_wg", [0, 32])
+def test_attend_large_batch_single_chunk(hs, heads_per_wg):
+    """128 requests x 128 heads, k = 640: enough workgroups without splitting
+    the records, so each workgroup's outputs are final and go out in fp32 from
+    the partial kernel with no combine launch (also with 32 heads a
+    workgroup); every request checked against the float64 oracle."""
+    w = tg.Workload("attend_big", 128, 1, 8192, 576, 2, 640, 1024, 2, tg.LOCALITY, 0.87, seed_index=67)
+    sel_all = tg.trace(w)
+    pool = keep(make_pool(hs, w))
+    pool_np = pool.numpy_view().reshape(w.pool_rows, w.row_bytes)
+    res = keep(make_resolver(hs, w, pool))
+    res.set_option(hs.HS_OPT_ATTN_HEADS, heads_per_wg)
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(12)
+    slot_idx = torch.empty((w.num_req, w.k), dtype=torch.int32, device=dev)
+    for t in range(w.steps):
+        sel = np.ascontiguousarray(sel_all[t, 0])
+        res.resolve(0, torch.from_numpy(sel).to(dev), slot_idx)
+        res.check_error()
+    q_np = rand_bits(rng, (w.num_req, 128, D_QK))
+    print(f"attend large batch heads/wg={heads_per_wg}", flush=True)
+    out, lse = run_attend(hs, res, 0, q_np, slot_idx, 1.0 / 24.0, dev)
+    check(hs, q_np, records(w, pool_np, 0, sel), 1.0 / 24.0, out, lse)
+
+
+@pytest.mark.parametrize("heads_per_wg", [0, 32])
 def test_attend_full_size_with_holes(hs, heads_per_wg):
     """The decode shape with slots left out: whole leading sub-chunks of every
     chunk empty (the running maximum stays -inf across them), a single record,
