@@ -17,12 +17,13 @@ HIPCC_FLAGS = [
 ]
 
 
-# Per-source extra flags.  The consumer's kernels take their scalar arguments
-# first and have the first 16 dwords of them preloaded into scalar registers
+# Per-source extra flags.  The consumer's kernels, and the per-layer metadata
+# kernel, take their scalar arguments first and have the first 16 dwords of them preloaded into scalar registers
 # at wave launch (gfx950 kernel-argument preloading; the code object keeps a
 # compatible entry that loads them itself), which saves a round trip to the
 # argument block before the first loads of every workgroup.
-EXTRA_FLAGS = {"csrc/attend.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+EXTRA_FLAGS = {"csrc/attend.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
+               "csrc/resolve_bitmap.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 
 
 def hipcc() -> str:

@@ -273,12 +273,12 @@ __device__ inline void radix_select(int* hist, int* misc, const uint32_t (&tsv)[
 // (and their host loads) before 4 and 5.
 #define HB_PHASE(i)                                                                      \
     do {                                                                                 \
-        if (lb.trace && tid == 0 && lead)                                                \
+        if (HB_ARG(trace) && tid == 0 && lead)                                                \
             reinterpret_cast<unsigned long long*>(misc + X_STAMP)[(i)] = wall_clock64(); \
     } while (0)
 #define HB_PHASE_FLUSH()                                                                                 \
     do {                                                                                                 \
-        if (lb.trace && tid == 0 && lead) {                                                              \
+        if (HB_ARG(trace) && tid == 0 && lead) {                                                              \
             const unsigned long long* st_ = reinterpret_cast<const unsigned long long*>(misc + X_STAMP); \
             for (int i_ = 0; i_ < 11; ++i_) s.phase[rl * kPhaseSlots + i_] = st_[i_];                    \
         }                                                                                                \
@@ -445,515 +445,65 @@ struct SplitEarly {
 };
 struct NoSplitEarly {};
 
+// Where a kernel's first phase takes its scalars from: the argument structs,
+// read at each use (wide and split launches), or separate arguments that the
+// build preloads into scalar registers at wave launch (per-layer launches).
+#define HB_STRUCT_k lb.k
+#define HB_STRUCT_B s.B
+#define HB_STRUCT_R s.R
+#define HB_STRUCT_ngroups lb.ngroups
+#define HB_STRUCT_r1_ints lb.r1_ints
+#define HB_STRUCT_trace lb.trace
+#define HB_STRUCT_clock s.clock
+#define HB_STRUCT_length s.length
+#define HB_STRUCT_miss_count s.miss_count
+#define HB_STRUCT_slot_pos s.slot_pos
+#define HB_STRUCT_ts s.ts
+#define HB_PRELOADED(x) x##_arg
+
+// Wide and split launches: every argument read from the argument block (these
+// builds are short of scalar registers; preloading measured slower there).
 template <int NT, int SPL, int PER, bool VEC, bool WIDE, bool SPLIT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WIDE ? (NT == 512 ? 8 : 6) : 1)))
 void bitmap_resolve_kernel(StateBase s, LayerBatch lb) {
-    constexpr int NW = NT / 64;
-    static_assert(NW <= 16, "per-wave partials fit one row of 16 lanes");
-    static_assert(!(WIDE && SPLIT), "a wide launch has one workgroup a unit");
-    extern __shared__ int lds[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-    const int G = SPLIT ? lb.wgs : 1;
-    const int r = SPLIT ? static_cast<int>(blockIdx.x) / G : static_cast<int>(blockIdx.x);
-    const int g = SPLIT ? static_cast<int>(blockIdx.x) - r * G : 0;
-    const bool lead = g == 0;  // publishes slot_idx and the hit mask, stamps phases
-    const int layer = lb.layer[blockIdx.y];
-    const int k = lb.k, B = s.B, NG = lb.ngroups;
-    const int64_t rl = static_cast<int64_t>(layer) * s.R + r;
-    const int32_t* sel = lb.sel[blockIdx.y] + static_cast<int64_t>(r) * k;
-    int32_t* out = lb.out[blockIdx.y] + static_cast<int64_t>(r) * k;
-    int32_t* spos_g = s.slot_pos + rl * B;
-    uint32_t* ts_g = s.ts + rl * B;
-    uint32_t* clock_u = s.clock + rl;
-    int32_t* mc_u = s.miss_count + rl;
-    uint4* const bits4 = reinterpret_cast<uint4*>(lds);
-    unsigned* const bits = reinterpret_cast<unsigned*>(lds);
-    uint16_t* const wrank = reinterpret_cast<uint16_t*>(lds + 4 * NG);  // [4*NG] rank of each word
-    int* const byrank = lds + 6 * NG;
-    // victim lists: a wide launch lays them over the bitmap, its ranks and
-    // the slot by rank once every wave is done reading those (one more
-    // barrier, only in units with misses), so four units fit a CU's LDS
-    int* const vlist = WIDE ? lds : byrank + k + 64;
-    int* const vold = vlist + k + 64;  // (each list has a spare word per lane)
-    int* const hist = lds + lb.r1_ints;
-    int* const misc = hist + kHistBins;
-    if (lb.trace && tid == 0 && lead) {
-        // the stamp words lie outside the part of the misc block cleared below
-        unsigned long long* st0 = reinterpret_cast<unsigned long long*>(misc + X_STAMP);
-        st0[0] = wall_clock64();
-        for (int i = 1; i < 11; ++i) st0[i] = 0ull;
-    }
+#define HB_ARG(x) HB_STRUCT_##x
+#include "resolve_bitmap_unit.inc"
+#undef HB_ARG
+}
 
-    // 1. every global read up front: clock, history length, last step's miss
-    // count, this lane's runs of the selection, the slot map and the stamps
-    const uint32_t t = *clock_u;
-    const int hist_len = s.length[rl];
-    const bool spec = *mc_u > 0;  // expect misses: build the age histogram early
-    const int j0 = tid * SPL, s0 = tid * PER;
-    const unsigned insel = run_mask<SPL>(k - j0), inslot = run_mask<PER>(B - s0);
-    int selv[SPL];
-    load_run<SPL, VEC, int>(sel, j0, k, selv, kEmpty);
-    int spos[PER];
-    load_run<PER, VEC, int>(spos_g, s0, B, spos, kEmpty);
-    // (the stamp run is read even by a unit that will hit everywhere: its
-    // hit stamps go back as whole 16-byte pieces, which measured faster than
-    // scattered 4-byte stores without the read)
-    uint32_t tsv[PER];
-    load_run<PER, VEC, uint32_t>(ts_g, s0, B, tsv, 0u);
-    for (int g = tid; g < NG; g += NT) bits4[g] = make_uint4(0u, 0u, 0u, 0u);
-    for (int i = tid; i < k; i += NT) byrank[i] = kEmpty;
-    for (int i = tid; i < kHistBins; i += NT) hist[i] = 0;
-    if (tid < X_STAMP) misc[tid] = 0;
-    __syncthreads();
-    HB_PHASE(1);
-
-    // 2. every selected position sets its bit; a bit already set is a
-    // repeated position, a position outside the history rejects the request
-    // (straight-line: a lane without a valid selection ORs nothing into word 0)
-    {
-        int bad = 0, bad_at = 0;
-#pragma unroll
-        for (int q = 0; q < SPL; ++q) {
-            const int j = j0 + q;
-            const int p = selv[q];
-            const bool live = (insel >> q) & 1u;
-            const bool inr = live && static_cast<unsigned>(p) < static_cast<unsigned>(hist_len);
-            const unsigned bit = inr ? 1u << (p & 31) : 0u;
-            const unsigned old = atomicOr(&bits[inr ? p >> 5 : 0], bit);
-            const int bb = ((live && !inr) ? 1 : 0) | ((old & bit) ? 2 : 0);
-            bad |= bb;
-            bad_at = bb ? j + 1 : bad_at;
-        }
-        block_or_into(&misc[X_FLAGS], bad);
-        if (bad) atomicMax(&misc[X_BADAT], bad_at);
-    }
-    __syncthreads();
-    HB_PHASE(2);
-    const int flags = misc[X_FLAGS];
-    if (flags) {
-        // reject: -1 everywhere, state unchanged
-        if (!lead) return;
-        for (int j = tid; j < k; j += NT) {
-            out[j] = -1;
-            s.hit_mask[rl * B + j] = 0;
-        }
-        if (tid == 0) {
-            *mc_u = 0;
-            s.status[rl] = (flags & 1) ? HS_DEV_RANGE : HS_DEV_DUP;
-            record_error(s.err, (flags & 1) ? HS_DEV_RANGE : HS_DEV_DUP, layer, r, misc[X_BADAT] - 1);
-        }
-        return;
-    }
-
-    // 3. group ranks: lane tid owns groups tid, tid + NT, ... (consecutive
-    // lanes, consecutive 16-byte pieces); each wave takes its run of ranks
-    // with one LDS atomic, so ranks map the selected positions one to one
-    // onto [0, k) whatever order the waves' atomics land in
-    {
-        int cnt = 0;
-        for (int g = tid; g < NG; g += NT) {
-            const uint4 v = bits4[g];
-            cnt += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
-        }
-        const int incl = wave_incl_scan(cnt);
-        int wb = 0;
-        if (lane == 63) wb = atomicAdd(&misc[X_RANK], incl);
-        int base = __builtin_amdgcn_readlane(wb, 63) + incl - cnt;
-        for (int g = tid; g < NG; g += NT) {
-            const uint4 v = bits4[g];
-            const unsigned r0 = static_cast<unsigned>(base);
-            const unsigned r1 = r0 + __popc(v.x), r2 = r1 + __popc(v.y), r3 = r2 + __popc(v.z);
-            reinterpret_cast<uint2*>(wrank)[g] = make_uint2(r0 | (r1 << 16), r2 | (r3 << 16));
-            base = static_cast<int>(r3) + __popc(v.w);
-        }
-    }
-    // hit test of this lane's slots (one bit each: a cached position whose
-    // bit is set is selected), the hit stamps 2t+2 written back as whole
-    // pieces of the stamp run, and the hit count
-    const uint32_t ts_hit = 2u * t + 2u, ts_miss = 2u * t + 1u;
-    const int nbits_pos = NG * 128;
-    unsigned hitbits = 0;
-    {
-        unsigned w[PER];
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            // (a slot past the end of the run holds -1, as does an empty one)
-            const int p = spos[q];
-            const bool live = static_cast<unsigned>(p) < static_cast<unsigned>(nbits_pos);
-            w[q] = bits[live ? p >> 5 : 0];
-        }
-        // every word is read whether or not its slot is live (the empty asm
-        // uses each one unconditionally), so no read sits in a branch of its
-        // own that waits for it on the spot
-#pragma unroll
-        for (int q = 0; q < PER; ++q) asm volatile("" : "+v"(w[q]));
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            const int p = spos[q];
-            const bool live = static_cast<unsigned>(p) < static_cast<unsigned>(nbits_pos);
-            hitbits |= static_cast<unsigned>(live && ((w[q] >> (p & 31)) & 1u)) << q;
-        }
-    }
-    const unsigned candbits = inslot & ~hitbits;  // slots that may be evicted
-    if (!SPLIT && hitbits) {
-        uint32_t tsn[PER];
-#pragma unroll
-        for (int q = 0; q < PER; ++q) tsn[q] = ((hitbits >> q) & 1u) ? ts_hit : tsv[q];
-        store_run_masked<PER, VEC, uint32_t>(ts_g, s0, B, tsn, hitbits);
-    }
-    {
-        const int hincl = wave_incl_scan(__popc(hitbits));
-        if (lane == 63) misc[X_HITS + wave] = hincl;
-    }
-    if (spec) {
-        // candidate ages (2t - stamp; no stamp exceeds 2t before step t);
-        // ages of 1023 and more share the top bin
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            int bin = -1;
-            if ((candbits >> q) & 1u) {
-                const uint32_t age = 2u * t - tsv[q];
-                bin = age < kHistBins - 1 ? static_cast<int>(age) : kHistBins - 1;
-            }
-            hist_add(hist, bin);
-        }
-    }
-    __syncthreads();
-    HB_PHASE(3);
-    const int h = sum_before(misc + X_HITS, NW);
-    const int m = k - h;
-
-    // 4. each hit slot records itself at its position's rank (a slot that is
-    // not a hit writes its lane's spare word byrank[k + lane] instead)
-    {
-        constexpr int NB = PER < 4 ? PER : 4;
-#pragma unroll
-        for (int q0 = 0; q0 < PER; q0 += NB) {
-            int pp[NB], rk[NB];
-            unsigned isset;
-#pragma unroll
-            for (int i = 0; i < NB; ++i) pp[i] = ((hitbits >> (q0 + i)) & 1u) ? spos[q0 + i] : 0;
-            bitmap_ranks<NB>(bits, wrank, pp, rk, isset);
-#pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                const bool hit = (hitbits >> (q0 + i)) & 1u;
-                byrank[hit ? rk[i] : k + lane] = s0 + q0 + i;
-            }
-        }
-    }
-    // threshold stamp T and how many candidates stamped exactly T go (lowest
-    // slots first; every other victim is older than T), then the victim
-    // counts in slot order, strict and tied packed into one scan (strict in
-    // the low 16 bits, tied in the high; both at most B <= 16384).  A split
-    // unit finds it later, after its selections are looked up and its host
-    // loads issued, so that they are in flight meanwhile.
-    uint32_t T = 0;
-    int need_eq = 0, packed = 0, vincl = 0;
-    unsigned strict_bits = 0, tie_bits = 0;
-    if constexpr (!SPLIT) {
-        if (m > 0) HB_FIND_THRESHOLD();
-    }
-    __syncthreads();
-    if constexpr (!SPLIT) HB_PHASE(5);
-
-    // 5. selection side: the slot recorded at each selection's rank is its
-    // hit, published now, or nothing (a miss)
-    int slv[SPL];
-    unsigned mf = 0;
-    {
-        // (a lane past the end looks up position 0; its rank stays within
-        // [0, k], so the read stays inside byrank and is discarded)
-        int pp[SPL], rk[SPL];
-        unsigned isset;
-#pragma unroll
-        for (int q = 0; q < SPL; ++q) pp[q] = ((insel >> q) & 1u) ? selv[q] : 0;
-        bitmap_ranks<SPL>(bits, wrank, pp, rk, isset);
-        (void)isset;
-        int v[SPL];
-#pragma unroll
-        for (int q = 0; q < SPL; ++q) v[q] = byrank[rk[q]];
-#pragma unroll
-        for (int q = 0; q < SPL; ++q) asm volatile("" : "+v"(v[q]));
-#pragma unroll
-        for (int q = 0; q < SPL; ++q) {
-            const bool live = (insel >> q) & 1u;
-            slv[q] = live ? v[q] : kEmpty;
-            mf |= static_cast<unsigned>(live && v[q] < 0) << q;
-        }
-    }
-    HB_PHASE(7);
-    if (lead) {
-        constexpr int W = SPL < 4 ? SPL : 4;
-        constexpr unsigned PM = (1u << W) - 1u;
-        uint8_t* hm = s.hit_mask + rl * B;
-        if constexpr (VEC && W >= 2) {
-#pragma unroll
-            for (int q = 0; q < SPL; q += W) {
-                if (j0 + q < k) {
-                    if (((mf >> q) & PM) == 0u) {
-                        if constexpr (W == 4)
-                            *reinterpret_cast<int4*>(out + j0 + q) = make_int4(slv[q], slv[q + 1], slv[q + 2], slv[q + 3]);
-                        else
-                            *reinterpret_cast<int2*>(out + j0 + q) = make_int2(slv[q], slv[q + 1]);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < W; ++e)
-                            if (!((mf >> (q + e)) & 1u)) out[j0 + q + e] = slv[q + e];
-                    }
-                    unsigned hw = 0;
-#pragma unroll
-                    for (int e = 0; e < W; ++e) hw |= static_cast<unsigned>(!((mf >> (q + e)) & 1u)) << (8 * e);
-                    if constexpr (W == 4) *reinterpret_cast<uint32_t*>(hm + j0 + q) = hw;
-                    else *reinterpret_cast<uint16_t*>(hm + j0 + q) = static_cast<uint16_t>(hw);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < SPL; ++q) {
-                const int j = j0 + q;
-                if (j < k) {
-                    if (!((mf >> q) & 1u)) out[j] = slv[q];
-                    hm[j] = ((mf >> q) & 1u) ? 0 : 1;
-                }
-            }
-        }
-    }
-    HB_PHASE(8);
-    if (m == 0) {
-        // every selection hit: the hit stamps are written, nothing else changes
-        if constexpr (SPLIT) {
-            // (the other workgroups of the unit find no miss either: the slot
-            // map does not change, and stamps and clock only matter to misses)
-            if (!lead) return;
-            if (hitbits) {
-                uint32_t tsn[PER];
-#pragma unroll
-                for (int q = 0; q < PER; ++q) tsn[q] = ((hitbits >> q) & 1u) ? ts_hit : tsv[q];
-                store_run_masked<PER, VEC, uint32_t>(ts_g, s0, B, tsn, hitbits);
-            }
-        }
-        if (tid == 0) finish_unit(s, clock_u, mc_u, rl, t, k, 0);
-        HB_PHASE(10);
-        HB_PHASE_FLUSH();
-        return;
-    }
-    // misses per wave (for each miss's rank), and the victims: the slot of
-    // victim rank i goes to vlist[i], its evicted position to vold[i] (and
-    // back to host-only: no write-back, the host copy is authoritative); its
-    // stamp becomes 2t+1 in this lane's run, written back whole
-    const int mc = __popc(mf);
-    const int mincl = wave_incl_scan(mc);
-    if (lane == 63) misc[X_MISS + wave] = mincl;
-    if constexpr (WIDE) __syncthreads();  // the victim lists overwrite the bitmap
-    // a split unit: the position of each miss is listed by rank (over the slot
-    // by rank, read by nobody any more) and this workgroup's first pieces of
-    // the unit's flat (row, piece) space of misses are loaded from the host
-    // into registers now; the victim slots they go to are found meanwhile
-    // (kSplitEarly pieces a lane, as in the copy; the state exists in split
-    // builds only, so the others keep their registers)
-    std::conditional_t<SPLIT, SplitEarly, NoSplitEarly> early;
-    if constexpr (SPLIT) {
-        __syncthreads();  // miss counts visible; every read of the slot by rank done
-        const int i0 = mincl - mc + sum_before(misc + X_MISS, wave);
-        early.i0 = i0;
-        int* const mpos = byrank;
-        {
-            int i = i0;
-#pragma unroll
-            for (int q = 0; q < SPL; ++q) {
-                if ((mf >> q) & 1u) {
-                    mpos[i] = selv[q];
-                    ++i;
-                }
-            }
-        }
-        __syncthreads();  // every miss's position is listed
-        const int row16 = static_cast<int>(s.row_bytes >> 4);
-        const int total = m * row16;
-        early.c_begin = static_cast<int>(static_cast<int64_t>(total) * g / G);
-        early.c_end = static_cast<int>(static_cast<int64_t>(total) * (g + 1) / G);
-        const uint8_t* src_base = s.pool + s.region_row[static_cast<int64_t>(r) * s.NL + layer] * s.row_bytes;
-#pragma unroll
-        for (int x = 0; x < kSplitEarly; ++x) {
-            const int c = early.c_begin + tid + x * NT;
-            early.i[x] = -1;
-            early.off[x] = 0;
-            if (c < early.c_end) {
-                const int i = c / row16, off = c - i * row16;
-                const u32x4* src = reinterpret_cast<const u32x4*>(src_base + static_cast<int64_t>(mpos[i]) * s.row_bytes) + off;
-                early.i[x] = i;
-                early.off[x] = off;
-                early.v[x] = lb.nt ? ld16<true>(src) : ld16<false>(src);
-            }
-        }
-        HB_FIND_THRESHOLD();
-        __syncthreads();  // victim counts visible
-        HB_PHASE(5);
-    }
-    unsigned vbits = 0;
-    {
-        const int vpre = vincl - packed + sum_before(misc + X_VICT, wave);
-        int sb = vpre & 0xFFFF, tb = vpre >> 16;
-        int32_t* pt = s.page_table + rl * s.L_ctx;
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            const bool st = (strict_bits >> q) & 1u, ti = (tie_bits >> q) & 1u;
-            const int rank = st ? sb + min(tb, need_eq) : ((ti && tb < need_eq) ? sb + tb : -1);
-            sb += st ? 1 : 0;
-            tb += ti ? 1 : 0;
-            const bool victim = rank >= 0 && rank < m;
-            // (straight-line: a slot that is not a victim writes its lane's
-            // spare words past the lists instead)
-            const int at = victim ? rank : k + lane;
-            vlist[at] = s0 + q;
-            vold[at] = spos[q];
-            vbits |= static_cast<unsigned>(victim) << q;
-        }
-        if constexpr (!SPLIT) {
-#pragma unroll
-            for (int q = 0; q < PER; ++q) {
-                if (((vbits >> q) & 1u) && spos[q] >= 0) pt[spos[q]] = -1;
-                if constexpr (WIDE)
-                    if ((vbits >> q) & 1u) ts_g[s0 + q] = ts_miss;  // (the stamp run is not kept live this far)
-            }
-        }
-        if (!WIDE && !SPLIT && vbits) {
-            uint32_t tsn[PER];
-#pragma unroll
-            for (int q = 0; q < PER; ++q)
-                tsn[q] = ((vbits >> q) & 1u) ? ts_miss : (((hitbits >> q) & 1u) ? ts_hit : tsv[q]);
-            store_run_masked<PER, VEC, uint32_t>(ts_g, s0, B, tsn, vbits | hitbits);
-        }
-    }
-    __syncthreads();
-    HB_PHASE(6);
-
-    // 6. the i-th miss (ascending selection index) takes the victim of rank i
-    // (ascending slot): plan entry, page table, slot map and publication
-    if constexpr (!SPLIT) {
-        const int i0 = mincl - mc + sum_before(misc + X_MISS, wave);  // this lane's first miss
-        int32_t* pt = s.page_table + rl * s.L_ctx;
-        int4* plan = s.plan + rl * B;
-        int i = i0;
-#pragma unroll
-        for (int q = 0; q < SPL; ++q) {
-            if ((mf >> q) & 1u) {
-                const int j = j0 + q, p = selv[q];
-                const int v = vlist[i], old = vold[i];
-                plan[i] = make_int4(j, v, old, p);
-                pt[p] = v;
-                spos_g[v] = p;
-                out[j] = v;
-                if constexpr (WIDE) vold[i] = p;  // the copy reads positions from here
-                ++i;
-            }
-        }
-        HB_PHASE(9);
-        if (tid == 0) finish_unit(s, clock_u, mc_u, rl, t, k, m);
-        if constexpr (WIDE) {
-            // a wide launch copies its own misses: with hundreds of workgroups
-            // copying at once the link is as busy as under the chip-wide fetch
-            // kernel, and the launch after it is saved
-            if (lb.copy) {
-                __syncthreads();  // every miss's position is in vold
-                const int total = m * static_cast<int>(s.row_bytes >> 4);
-                if (lb.nt) copy_misses<NT, true, 4>(s, vold, vlist, rl, r, layer, 0, total);
-                else copy_misses<NT, false, 4>(s, vold, vlist, rl, r, layer, 0, total);
-            }
-        }
-        HB_PHASE(10);
-        HB_PHASE_FLUSH();
-    } else {
-        const int i0 = early.i0;  // this lane's first miss
-        // the lead publishes the misses' slots
-        if (lead) {
-            int i = i0;
-#pragma unroll
-            for (int q = 0; q < SPL; ++q) {
-                if ((mf >> q) & 1u) {
-                    out[j0 + q] = vlist[i];
-                    ++i;
-                }
-            }
-        }
-        HB_PHASE(9);
-        // arrival, before the copy (which reads no metadata): every read of
-        // the old metadata is long done, its values used before the barriers
-        // above.  The counter's answer is only looked at after the copy, so
-        // its round trip overlaps the copy instead of following it.
-        unsigned arrived_before = 0;
-        if (tid == 0) arrived_before = atomicAdd(&s.arrive[rl], 1u);
-        {
-            // the pieces loaded early go to their victim slots, then the rest
-            // of this workgroup's share, one host load a lane in flight as in
-            // the fetch kernel (about a megabyte over the launch's ~64
-            // workgroups; more per lane measured slower over the host link)
-            uint8_t* dst_base = s.cache + rl * s.B * s.row_bytes;
-#pragma unroll
-            for (int x = 0; x < kSplitEarly; ++x) {
-                if (early.i[x] >= 0) {
-                    u32x4* dst = reinterpret_cast<u32x4*>(dst_base + static_cast<int64_t>(vlist[early.i[x]]) * s.row_bytes) +
-                                 early.off[x];
-                    if (lb.nt) st16<true>(dst, early.v[x]);
-                    else st16<false>(dst, early.v[x]);
-                }
-            }
-            const int c_rest = min(early.c_end, early.c_begin + kSplitEarly * NT);
-            if (lb.nt) copy_misses<NT, true, 1>(s, byrank, vlist, rl, r, layer, c_rest, early.c_end);
-            else copy_misses<NT, false, 1>(s, byrank, vlist, rl, r, layer, c_rest, early.c_end);
-        }
-        // the last workgroup to arrive writes the new metadata
-        if (tid == 0) misc[X_LAST] = arrived_before == static_cast<unsigned>(G - 1) ? 1 : 0;
-        __syncthreads();
-        if (!misc[X_LAST]) {
-            HB_PHASE(10);
-            HB_PHASE_FLUSH();
-            return;
-        }
-        if (tid == 0) s.arrive[rl] = 0u;  // ready for the next launch
-        // the unit's new metadata: evicted positions back to host only (no
-        // write-back, the host copy is authoritative), the stamp run with the
-        // hits at 2t+2 and the victims at 2t+1, then per miss the plan entry,
-        // the page table and the slot map
-        int32_t* pt = s.page_table + rl * s.L_ctx;
-#pragma unroll
-        for (int q = 0; q < PER; ++q)
-            if (((vbits >> q) & 1u) && spos[q] >= 0) pt[spos[q]] = -1;
-        if (vbits | hitbits) {
-            uint32_t tsn[PER];
-#pragma unroll
-            for (int q = 0; q < PER; ++q)
-                tsn[q] = ((vbits >> q) & 1u) ? ts_miss : (((hitbits >> q) & 1u) ? ts_hit : tsv[q]);
-            store_run_masked<PER, VEC, uint32_t>(ts_g, s0, B, tsn, vbits | hitbits);
-        }
-        int4* plan = s.plan + rl * B;
-        int i = i0;
-#pragma unroll
-        for (int q = 0; q < SPL; ++q) {
-            if ((mf >> q) & 1u) {
-                const int j = j0 + q, p = selv[q];
-                const int v = vlist[i], old = vold[i];
-                plan[i] = make_int4(j, v, old, p);
-                pt[p] = v;
-                spos_g[v] = p;
-                ++i;
-            }
-        }
-        if (tid == 0) finish_unit(s, clock_u, mc_u, rl, t, k, m);
-        HB_PHASE(10);
-        HB_PHASE_FLUSH();
-    }
+// Per-layer launches, one workgroup a unit: the first phase's values lead the
+// arguments, and the build preloads them into scalar registers at wave launch
+// (the per-layer launch at 64 request-layers of 4 KB records: 11.4 against
+// 11.8 us by events over three interleaved runs).
+template <int NT, int SPL, int PER, bool VEC, bool WIDE = false, bool SPLIT = false>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1)))
+void bitmap_resolve_layer_kernel(int k_arg, int B_arg, int R_arg, int ngroups_arg, int r1_ints_arg, int trace_arg,
+                                 uint32_t* clock_arg, int32_t* length_arg, int32_t* miss_count_arg,
+                                 int32_t* slot_pos_arg, uint32_t* ts_arg, StateBase s, LayerBatch lb) {
+    static_assert(!WIDE && !SPLIT, "one workgroup a unit, one unit a workgroup");
+#define HB_ARG(x) HB_PRELOADED(x)
+#include "resolve_bitmap_unit.inc"
+#undef HB_ARG
 }
 
 template <int NT, int SPL, int PER, bool VEC, bool WIDE, bool SPLIT>
 hipError_t launch_b(const StateBase& s, const LayerBatch& lb, size_t lds, hipStream_t st) {
     static LdsGrants granted;  // per instantiation
-    const void* fn = reinterpret_cast<const void*>(&bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE, SPLIT>);
-    const hipError_t e = ensure_lds_limit(fn, lds, granted);
-    if (e != hipSuccess) return e;
     const unsigned gx = SPLIT ? static_cast<unsigned>(s.R) * static_cast<unsigned>(lb.wgs) : static_cast<unsigned>(s.R);
-    hipLaunchKernelGGL((bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE, SPLIT>), dim3(gx, lb.n), dim3(NT), lds, st, s,
-                       lb);
+    if constexpr (!WIDE && !SPLIT) {
+        const void* fn = reinterpret_cast<const void*>(&bitmap_resolve_layer_kernel<NT, SPL, PER, VEC>);
+        const hipError_t e = ensure_lds_limit(fn, lds, granted);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((bitmap_resolve_layer_kernel<NT, SPL, PER, VEC>), dim3(gx, lb.n), dim3(NT), lds, st, lb.k,
+                           s.B, s.R, lb.ngroups, lb.r1_ints, lb.trace, s.clock, s.length, s.miss_count, s.slot_pos,
+                           s.ts, s, lb);
+    } else {
+        const void* fn = reinterpret_cast<const void*>(&bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE, SPLIT>);
+        const hipError_t e = ensure_lds_limit(fn, lds, granted);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((bitmap_resolve_kernel<NT, SPL, PER, VEC, WIDE, SPLIT>), dim3(gx, lb.n), dim3(NT), lds, st,
+                           s, lb);
+    }
     return hipGetLastError();
 }
 
